@@ -1,0 +1,61 @@
+"""Seeded synthetic rank buffers.
+
+This module only draws random numbers; it holds none of the collectives'
+arithmetic.  Both the HIP path's tests and the CPU oracle consume what it
+returns.
+
+Rank r of a workload draws from ``numpy.random.default_rng([seed, cfg, N, r])``
+so every rank's buffer is reproducible on its own.  Distributions:
+
+``uniform``     fp32 uniform on [-1, 1)
+``normal``      N(0, 1)
+``normal_1e-3`` N(0, sigma = 1e-3)   (gradient buckets)
+``int20``       int32 uniform on [-2**20, 2**20]
+``ones``        every element 1
+
+A bf16 buffer holds the fp32 draws truncated to their top 16 bits (which are
+exact bf16 values); it is returned as the uint16 bit patterns.
+"""
+
+import numpy as np
+
+DISTS = ("uniform", "normal", "normal_1e-3", "int20", "ones")
+_STORAGE = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32}
+
+
+def rank_rng(seed: int, cfg: int, nranks: int, rank: int) -> np.random.Generator:
+    return np.random.default_rng([seed, cfg, nranks, rank])
+
+
+def _draw(rng, size, dt, dist):
+    if dist == "ones":
+        if dt == "bf16":
+            return np.full(size, 0x3F80, dtype=np.uint16)
+        return np.ones(size, dtype=_STORAGE[dt])
+    if dist == "int20":
+        v = rng.integers(-(2 ** 20), 2 ** 20, size=size, endpoint=True)
+        if dt == "i32":
+            return v.astype(np.int32)
+        f = v.astype(np.float32)
+    elif dist == "uniform":
+        f = rng.uniform(-1.0, 1.0, size=size).astype(np.float32)
+    elif dist == "normal":
+        f = rng.standard_normal(size=size, dtype=np.float32)
+    elif dist == "normal_1e-3":
+        f = (rng.standard_normal(size=size, dtype=np.float32) * np.float32(1e-3)).astype(np.float32)
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    if dt == "f32":
+        return f
+    if dt == "bf16":
+        return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    if dt == "i32":
+        return np.rint(f * 1024).astype(np.int32)
+    raise ValueError(f"unknown payload type {dt!r}")
+
+
+def rank_inputs(nranks: int, count: int, dt: str, dist: str, seed: int = 0, cfg: int = 0):
+    """N host arrays of `count` elements each (uint16 bit patterns for bf16)."""
+    if dt not in _STORAGE:
+        raise ValueError(f"unknown payload type {dt!r}")
+    return [_draw(rank_rng(seed, cfg, nranks, r), count, dt, dist) for r in range(nranks)]

@@ -1,0 +1,272 @@
+"""Pins of the oracle's collectives against what the pages and arithmetic fix.
+
+None of these re-types the oracle's own code: each checks it against an
+independent fact -- a closed form, Python's exact integer / rational
+arithmetic, a worked value chosen so that the association order shows in the
+result, or an identity the pages state.
+"""
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from all_reduce_reduction_rank_amd import inputs
+from oracle import bf16, collectives as C, geometry
+
+ALGOS = ("oneshot", "twoshot", "ring")
+DTYPES = ("f32", "bf16", "i32")
+
+
+def _as_float(x, dt):
+    if dt == "bf16":
+        return bf16.widen(x).astype(np.float64)
+    return x.astype(np.float64)
+
+
+# ---------------------------------------------------------------- all ones
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("count", [0, 1, 7, 64, 131])
+def test_all_ones_sum_to_n(algo, dt, n, count):
+    # "NCCL collectives..." section "Code": an all-reduce of ones must sum to
+    # the world size on every rank.
+    x = inputs.rank_inputs(n, count, dt, "ones")
+    for out in C.allreduce(x, dt, algo, chunk_bytes=64):
+        assert np.all(_as_float(out, dt) == n)
+
+
+def test_page_sanity_case_128_ones():
+    # The page's sanity script: torch.ones(128), all_reduce SUM, mean == N.
+    for n in (2, 8):
+        out = C.allreduce(inputs.rank_inputs(n, 128, "f32", "ones"), "f32", "ring")
+        assert all(o.mean() == n for o in out)
+
+
+# ------------------------------------------------------------- int32 exact
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+def test_int32_equals_python_integer_sum(algo, n):
+    count = 1000 + 3 * n
+    x = inputs.rank_inputs(n, count, "i32", "int20", seed=5)
+    exact = [sum(int(x[i][k]) for i in range(n)) for k in range(count)]
+    for out in C.allreduce(x, "i32", algo, chunk_bytes=256):
+        assert [int(v) for v in out] == exact
+
+
+def test_int32_wraps_twos_complement():
+    big = np.full(4, 2 ** 31 - 1, dtype=np.int32)
+    x = [big, big, np.full(4, 5, dtype=np.int32)]
+    v = 2 * (2 ** 31 - 1) + 5
+    want = (v + 2 ** 31) % 2 ** 32 - 2 ** 31  # two's-complement wrap of v
+    assert want == 3
+    for algo in ALGOS:
+        for out in C.allreduce(x, "i32", algo):
+            assert np.all(out.astype(np.int64) == want)
+
+
+# ----------------------------------------------- fp32 bound vs exact sum
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_f32_within_bound_of_exact_sum(algo, n):
+    count = 777
+    x = inputs.rank_inputs(n, count, "f32", "normal", seed=11)
+    xs = np.stack([v.astype(np.float64) for v in x])
+    bound = n * 2.0 ** -23 * np.abs(xs).sum(axis=0)
+    exact = np.array([math.fsum(xs[:, k]) for k in range(count)])
+    for out in C.allreduce(x, "f32", algo, chunk_bytes=128):
+        assert np.all(np.abs(out.astype(np.float64) - exact) <= bound)
+
+
+def test_f32_exact_with_fractions_on_wide_exponents():
+    # Terms spanning ~100 binary orders: compare with exact rationals.
+    rng = np.random.default_rng(3)
+    n, count = 5, 64
+    x = [(rng.standard_normal(count) * 2.0 ** rng.integers(-50, 50, count)).astype(np.float32)
+         for _ in range(n)]
+    for algo in ALGOS:
+        for out in C.allreduce(x, "f32", algo, chunk_bytes=32):
+            for k in range(count):
+                exact = sum(Fraction(float(x[i][k])) for i in range(n))
+                bound = n * Fraction(1, 2 ** 23) * sum(abs(Fraction(float(x[i][k]))) for i in range(n))
+                assert abs(Fraction(float(out[k])) - exact) <= bound
+
+
+def test_f32_subnormals_are_not_flushed():
+    tiny = np.float32(1e-45)  # the smallest binary32 subnormal
+    x = [np.full(8, tiny, dtype=np.float32), np.zeros(8, dtype=np.float32)]
+    for algo in ALGOS:
+        for out in C.allreduce(x, "f32", algo):
+            assert np.all(out == tiny) and out[0] != 0
+
+
+# ------------------------------------------- association order, closed form
+def _order_probe(n, per_block, dt="f32"):
+    """Block j: rank j+1 holds 2**24, rank j holds -2**24, everyone else 1.
+
+    In binary32, 2**24 + 1 is a tie that rounds back to 2**24, so the ones
+    vanish if and only if 2**24 is added before them, and the result is 0
+    exactly when -2**24 comes last."""
+    a = geometry.vec_elems(dt)
+    count = n * per_block * a
+    blocks = geometry.ar_blocks(count, n, dt)
+    x = [np.ones(count, dtype=np.float32) for _ in range(n)]
+    for j, (lo, hi) in enumerate(blocks):
+        x[(j + 1) % n][lo:hi] = 2.0 ** 24
+        x[j][lo:hi] = -(2.0 ** 24)
+    return x, blocks
+
+
+@pytest.mark.parametrize("n", [3, 4, 5, 8])
+def test_ring_sum_starts_after_owner_and_ends_at_owner(n):
+    # Ring: reduce steps pass block j from rank j+1 around to rank j, which
+    # keeps it ("each keeps only its slice of the sum").  With the probe the
+    # sum is 2**24 (+1 lost) ... (+1 lost) - 2**24 = 0 exactly.
+    x, blocks = _order_probe(n, 3)
+    for out in C.allreduce_ring(x, "f32", chunk_bytes=16):
+        assert np.all(out == 0.0)
+
+
+@pytest.mark.parametrize("n", [3, 4, 5, 8])
+def test_oneshot_twoshot_sum_in_ascending_rank_order(n):
+    # Ascending order 0..N-1: for j < N-1 the -2**24 comes right before the
+    # +2**24, the ones survive, result N-2; for j = N-1 the +2**24 comes first
+    # (rank 0), eats the ones, and -2**24 closes: result 0.
+    x, blocks = _order_probe(n, 2)
+    for algo in ("oneshot", "twoshot"):
+        for out in C.allreduce(x, "f32", algo):
+            for j, (lo, hi) in enumerate(blocks):
+                want = 0.0 if j == n - 1 else float(n - 2)
+                assert np.all(out[lo:hi] == want), (algo, j)
+
+
+def test_bf16_ring_rounds_every_hop():
+    # bf16 keeps 8 significant bits: 256 + 1 is a tie that rounds to 256.
+    # Ring with N=3, block 0: rank 1 holds 256, rank 2 holds 1, rank 0 holds 1.
+    # Per-hop rounding: bf16(256 + 1) = 256, then bf16(256 + 1) = 256.
+    # A single rounding of the fp32 sum would give bf16(258) = 258.
+    n, a = 3, geometry.vec_elems("bf16")
+    count = n * a
+    one, b256 = 0x3F80, 0x4380  # bf16 encodings of 1.0 and 256.0
+    x = [np.full(count, one, dtype=np.uint16) for _ in range(n)]
+    x[1][:a] = b256
+    ring = C.allreduce_ring(x, "bf16")
+    assert np.all(bf16.widen(ring[0][:a]) == 256.0)
+    one_shot = C.allreduce_oneshot(x, "bf16")
+    assert np.all(bf16.widen(one_shot[0][:a]) == 258.0)
+
+
+# ------------------------------------------------------------- identities
+@pytest.mark.parametrize("dt", DTYPES)
+def test_two_ranks_all_algorithms_bitwise_equal(dt):
+    # With two terms there is one association and IEEE add commutes.
+    x = inputs.rank_inputs(2, 999, dt, "normal" if dt != "i32" else "int20", seed=2)
+    outs = [C.allreduce(x, dt, a, chunk_bytes=64) for a in ALGOS]
+    for o in outs[1:]:
+        for r in range(2):
+            assert np.array_equal(o[r], outs[0][r])
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("dt", DTYPES)
+def test_every_rank_gets_the_same_result(algo, dt):
+    n = 5
+    x = inputs.rank_inputs(n, 301, dt, "normal" if dt != "i32" else "int20", seed=4)
+    out = C.allreduce(x, dt, algo, chunk_bytes=48)
+    for r in range(1, n):
+        assert np.array_equal(out[r], out[0])
+
+
+def test_oneshot_equals_twoshot_bitwise():
+    for dt in DTYPES:
+        x = inputs.rank_inputs(7, 1234, dt, "normal" if dt != "i32" else "int20", seed=9)
+        a = C.allreduce_oneshot(x, dt)
+        b = C.allreduce_twoshot(x, dt)
+        assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+def test_ring_independent_of_chunk_size(dt):
+    x = inputs.rank_inputs(4, 1000, dt, "normal" if dt != "i32" else "int20", seed=6)
+    ref = C.allreduce_ring(x, dt, chunk_bytes=1 << 22)
+    for cb in (16, 48, 4096, 512 * 1024):
+        got = C.allreduce_ring(x, dt, chunk_bytes=cb)
+        assert all(np.array_equal(u, v) for u, v in zip(ref, got))
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+def test_reduce_scatter_then_all_gather_is_all_reduce(dt, n):
+    # "ring all-reduce = reduce-scatter + all-gather" ("NCCL collectives...",
+    # sections "Direct answer" and "Interviewer follow-ups").  With recvcount a
+    # whole number of 16-byte vectors the all-reduce blocks equal the slices.
+    rc = 5 * geometry.vec_elems(dt)
+    x = inputs.rank_inputs(n, n * rc, dt, "normal" if dt != "i32" else "int20", seed=8)
+    for rs_algo, ar_algo in (("twoshot", "twoshot"), ("ring", "ring")):
+        shards = C.reduce_scatter(x, dt, rs_algo, chunk_bytes=32)
+        again = C.allgather(shards, dt, rs_algo, chunk_bytes=32)
+        ar = C.allreduce(x, dt, ar_algo, chunk_bytes=32)
+        for r in range(n):
+            assert np.array_equal(again[r], ar[r]), (rs_algo, r)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_all_gather_is_concatenation(algo):
+    n, sc = 4, 37
+    x = inputs.rank_inputs(n, sc, "f32", "uniform", seed=1)
+    for out in C.allgather(x, "f32", algo, chunk_bytes=16):
+        for j in range(n):
+            assert np.array_equal(out[j * sc:(j + 1) * sc], x[j])
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_reduce_scatter_int_slices(algo):
+    n, rc = 4, 50
+    x = inputs.rank_inputs(n, n * rc, "i32", "int20", seed=12)
+    out = C.reduce_scatter(x, "i32", algo, chunk_bytes=16)
+    for r in range(n):
+        want = [sum(int(x[i][r * rc + k]) for i in range(n)) for k in range(rc)]
+        assert [int(v) for v in out[r]] == want
+
+
+# --------------------------------------------------------------- bf16 bounds
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_bf16_oneshot_within_one_ulp_of_rounded_exact_sum(n):
+    x = inputs.rank_inputs(n, 2000, "bf16", "normal", seed=13)
+    exact = np.sum(np.stack([bf16.widen(v).astype(np.float64) for v in x]), axis=0)
+    # RNE of the exact (double) sum: go through float32 only when exact there.
+    ref = bf16.narrow_rne(exact.astype(np.float32))
+    for algo in ("oneshot", "twoshot"):
+        out = C.allreduce(x, "bf16", algo)[0]
+        assert int(bf16.ulp_distance(out, ref).max()) <= 1
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_bf16_ring_error_bound(n):
+    # N-1 roundings to 8 significant bits, each at most 2**-8 relative to a
+    # partial sum whose magnitude is at most sum |x|.
+    x = inputs.rank_inputs(n, 2000, "bf16", "normal", seed=14)
+    xs = np.stack([bf16.widen(v).astype(np.float64) for v in x])
+    exact, mag = xs.sum(axis=0), np.abs(xs).sum(axis=0)
+    out = bf16.widen(C.allreduce_ring(x, "bf16", chunk_bytes=64)[0]).astype(np.float64)
+    assert np.all(np.abs(out - exact) <= (n * 2.0 ** -8 + n * 2.0 ** -23) * mag)
+
+
+# ------------------------------------------------------------ edge cases
+def test_empty_and_single_rank():
+    for algo in ALGOS:
+        assert [len(o) for o in C.allreduce(inputs.rank_inputs(3, 0, "f32", "ones"), "f32", algo)] == [0] * 3
+        x = inputs.rank_inputs(1, 10, "f32", "uniform")
+        assert np.array_equal(C.allreduce(x, "f32", algo)[0], x[0])
+
+
+def test_more_ranks_than_vectors_leaves_empty_blocks():
+    # 8 B per rank at N=8 (two fp32): one 16-byte vector, blocks 1..7 empty.
+    x = inputs.rank_inputs(8, 2, "f32", "uniform", seed=3)
+    ref = C.allreduce_oneshot(x, "f32")[0]
+    for algo in ("twoshot", "ring"):
+        for out in C.allreduce(x, "f32", algo):
+            assert np.allclose(out, ref, rtol=0, atol=8 * 2.0 ** -23 * 8)
+    assert geometry.ar_blocks(2, 8, "f32")[1] == (2, 2)
