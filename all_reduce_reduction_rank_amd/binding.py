@@ -1,0 +1,196 @@
+"""Python binding of libar.so: argument marshalling only.
+
+Every step of a collective runs in the library's HIP kernels; PyTorch only
+supplies device memory (tensors) and the stream.  The entry points keep the
+C names (``include/ar.h``):
+
+    comm = Comm(nranks, max_bytes_per_rank, max_line_bytes_per_rank)
+    comm.allreduce(send, recv, algo="ring", proto="simple", chunk_bytes=0)
+    comm.reduce_scatter(send, recv, ...)
+    comm.allgather(send, recv, ...)
+    plan_bytes(nranks, op, count, dtype, algo, proto, ...)
+
+``send`` / ``recv`` are lists of N contiguous CUDA (HIP) tensors on the
+communicator's device.  If the library is missing it is built once with hipcc;
+if that fails every call raises -- there is no CPU fallback.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libar.so")
+
+OPS = {"allreduce": 0, "reduce_scatter": 1, "allgather": 2}
+ALGOS = {"oneshot": 0, "twoshot": 1, "ring": 2}
+PROTOS = {"simple": 0, "ll": 1, "ll128": 2}
+DTYPES = {"f32": 0, "bf16": 1, "i32": 2}
+ESIZE = {"f32": 4, "bf16": 2, "i32": 4}
+
+STATUS = {
+    0: "AR_OK", 1: "AR_ERR_INVALID", 2: "AR_ERR_UNSUPPORTED", 3: "AR_ERR_NOMEM",
+    4: "AR_ERR_TOO_LARGE", 5: "AR_ERR_HIP", 6: "AR_ERR_TIMEOUT", 7: "AR_ERR_BROKEN",
+}
+
+# Every symbol include/ar.h declares.
+SYMBOLS = (
+    "ar_comm_create", "ar_comm_destroy", "ar_comm_check", "ar_comm_reset",
+    "ar_comm_workspace_bytes", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
+    "ar_plan_bytes", "ar_debug_inject", "ar_status_string",
+)
+
+
+class ARError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_lib().ar_status_string(status).decode()})")
+
+
+_LIB = None
+
+
+def _declare(lib):
+    P, S, I, U64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint64
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    lib.ar_comm_create.argtypes = [I, S, S, ctypes.POINTER(P)]
+    lib.ar_comm_destroy.argtypes = [P]
+    lib.ar_comm_check.argtypes = [P, P, ctypes.POINTER(I), ctypes.POINTER(I)]
+    lib.ar_comm_reset.argtypes = [P, P]
+    lib.ar_comm_workspace_bytes.argtypes = [P]
+    lib.ar_comm_workspace_bytes.restype = S
+    for name in ("ar_allreduce", "ar_reduce_scatter", "ar_allgather"):
+        getattr(lib, name).argtypes = [P, PP, PP, S, I, I, I, S, P]
+    lib.ar_plan_bytes.argtypes = [I, I, S, I, I, I, S, I, ctypes.POINTER(U64), ctypes.POINTER(U64),
+                                  ctypes.POINTER(U64), ctypes.POINTER(U64)]
+    lib.ar_debug_inject.argtypes = [P, I, I, U64]
+    lib.ar_status_string.argtypes = [I]
+    lib.ar_status_string.restype = ctypes.c_char_p
+    for name in SYMBOLS:
+        if name not in ("ar_comm_workspace_bytes", "ar_status_string"):
+            getattr(lib, name).restype = I
+    return lib
+
+
+def _lib():
+    """Load libar.so (building it first if it is not there)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            from .build import build
+            build()
+        _LIB = _declare(ctypes.CDLL(LIB_PATH))
+    return _LIB
+
+
+def library():
+    return _lib()
+
+
+def _check(status, what):
+    if status != 0:
+        raise ARError(status, what)
+
+
+def _dtype_name(t):
+    import torch
+
+    names = {torch.float32: "f32", torch.bfloat16: "bf16", torch.int32: "i32"}
+    if t.dtype not in names:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return names[t.dtype]
+
+
+def _ptrs(tensors, nranks, device):
+    if len(tensors) != nranks:
+        raise ValueError(f"need {nranks} rank buffers, got {len(tensors)}")
+    for t in tensors:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("rank buffers must be contiguous device tensors")
+        if t.device.index != device:
+            raise ValueError("rank buffers must live on the communicator's device")
+    return (ctypes.c_void_p * nranks)(*[t.data_ptr() for t in tensors])
+
+
+def _stream_handle(stream):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Comm:
+    """N simulated ranks on the current device with a workspace allocated once."""
+
+    def __init__(self, nranks: int, max_bytes_per_rank: int, max_line_bytes_per_rank: int = 0):
+        import torch
+
+        self.nranks = nranks
+        self.device = torch.cuda.current_device()
+        self._h = ctypes.c_void_p()
+        _check(_lib().ar_comm_create(nranks, max_bytes_per_rank, max_line_bytes_per_rank,
+                                     ctypes.byref(self._h)), "ar_comm_create")
+
+    def close(self):
+        if self._h:
+            _check(_lib().ar_comm_destroy(self._h), "ar_comm_destroy")
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            if self._h:
+                _lib().ar_comm_destroy(self._h)
+        except Exception:
+            pass
+
+    @property
+    def workspace_bytes(self) -> int:
+        return _lib().ar_comm_workspace_bytes(self._h)
+
+    def _call(self, name, send, recv, count, algo, proto, chunk_bytes, stream):
+        dt = _dtype_name(send[0])
+        for t in list(send) + list(recv):
+            if _dtype_name(t) != dt:
+                raise TypeError("all rank buffers must share one dtype")
+        s, r = _ptrs(send, self.nranks, self.device), _ptrs(recv, self.nranks, self.device)
+        status = getattr(_lib(), name)(self._h, s, r, count, DTYPES[dt], ALGOS[algo], PROTOS[proto],
+                                       chunk_bytes, _stream_handle(stream))
+        _check(status, name)
+
+    def allreduce(self, send, recv=None, algo="ring", proto="simple", chunk_bytes=0, stream=None):
+        """recv[r] = sum of send[0..N-1]; recv=None runs in place."""
+        recv = send if recv is None else recv
+        self._call("ar_allreduce", send, recv, send[0].numel(), algo, proto, chunk_bytes, stream)
+        return recv
+
+    def reduce_scatter(self, send, recv, algo="ring", proto="simple", chunk_bytes=0, stream=None):
+        """send[i] holds N*recvcount elements; recv[r] receives slice r of the sum."""
+        self._call("ar_reduce_scatter", send, recv, recv[0].numel(), algo, proto, chunk_bytes, stream)
+        return recv
+
+    def allgather(self, send, recv, algo="ring", proto="simple", chunk_bytes=0, stream=None):
+        """recv[r] = send[0] | send[1] | ... | send[N-1]."""
+        self._call("ar_allgather", send, recv, send[0].numel(), algo, proto, chunk_bytes, stream)
+        return recv
+
+    def check(self, stream=None):
+        """Synchronize and return (status name, rank, step) of a latched error."""
+        rank, step = ctypes.c_int(-1), ctypes.c_int(-1)
+        st = _lib().ar_comm_check(self._h, _stream_handle(stream), ctypes.byref(rank), ctypes.byref(step))
+        return STATUS.get(st, st), rank.value, step.value
+
+    def reset(self, stream=None):
+        _check(_lib().ar_comm_reset(self._h, _stream_handle(stream)), "ar_comm_reset")
+
+    def inject(self, rank: int, step: int, timeout_us: int = 0):
+        _check(_lib().ar_debug_inject(self._h, rank, step, timeout_us), "ar_debug_inject")
+
+
+def plan_bytes(nranks, op, count, dtype, algo, proto, chunk_bytes=0, in_place=False):
+    """Host-side byte accounting of one call (no GPU needed)."""
+    rd, wr, nt = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+    link = (ctypes.c_uint64 * nranks)()
+    _check(_lib().ar_plan_bytes(nranks, OPS[op], count, DTYPES[dtype], ALGOS[algo], PROTOS[proto],
+                                chunk_bytes, int(in_place), ctypes.byref(rd), ctypes.byref(wr), link,
+                                ctypes.byref(nt)), "ar_plan_bytes")
+    return {"read": rd.value, "write": wr.value, "hbm": rd.value + wr.value,
+            "link": list(link), "ntasks": nt.value}

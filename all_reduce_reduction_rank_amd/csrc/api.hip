@@ -1,0 +1,259 @@
+// api.hip -- the C ABI declared in include/ar.h.
+//
+// A communicator ("Add nccl support for tensor parrallel", overview: a
+// communicator is set up once, then collective calls are made on it) owns one
+// device workspace allocated at creation, as a custom all-reduce's
+// pre-registered buffer is ("Collective communication: NCCL's algorithms and
+// protocols, and custom all-reduce", exercise 3): calls allocate nothing, so
+// they can be captured in HIP graphs, and the workspace caps the message size.
+//
+// Workspace layout (one hipMalloc, 256-byte aligned regions):
+//   [Ctl][flags: u64 x nflags][LL/LL128 lines][ring reduce-scatter partials]
+// Ctl, flags and lines are zeroed at creation; flags and lines are tagged
+// with the device call counter, so they are never cleared again.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "../../include/ar.h"
+#include "device.hpp"
+#include "plan.hpp"
+
+namespace ar {
+hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream);
+hipError_t launch_reset(Ctl* c, hipStream_t stream);
+}  // namespace ar
+
+using namespace ar;
+
+struct ar_comm {
+  int nranks = 0;
+  int device = 0;
+  size_t max_bytes = 0, max_line_bytes = 0;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  Ctl* ctl = nullptr;
+  uint64_t* flags = nullptr;
+  uint64_t nflags = 0;
+  char* lines = nullptr;
+  uint64_t lines_bytes = 0;
+  char* stage = nullptr;
+  uint64_t stage_stride = 0;
+  uint64_t ticks_per_us = 100;
+  uint64_t timeout_ticks = 0;
+  int inj_rank = -1, inj_step = -1;
+  bool broken = false;
+};
+
+static uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }
+
+// Largest staging any LL / LL128 call on payloads of up to `line_bytes` per
+// rank can need (the ring all-reduce dominates; checked again per call).
+static uint64_t line_capacity(int n, uint64_t line_bytes) {
+  if (!line_bytes) return 0;
+  uint64_t best = 0;
+  for (int op = 0; op < 3; ++op)
+    for (int algo = 0; algo < 3; ++algo)
+      for (int proto = PROTO_LL; proto <= PROTO_LL128; ++proto)
+        for (int dt = 0; dt < 3; dt += 1) {
+          const uint64_t es = (uint64_t)esize_of(dt);
+          const uint64_t cnt = op == OP_ALLREDUCE ? line_bytes / es : line_bytes / es / n;
+          Geometry g;
+          if (make_geometry(op, algo, proto, dt, n, cnt, 0, 0, &g)) best = umax(best, staging_bytes(g));
+        }
+  return best + best / 8 + (1u << 20);
+}
+
+extern "C" {
+
+const char* ar_status_string(ar_status s) {
+  switch (s) {
+    case AR_OK: return "ok";
+    case AR_ERR_INVALID: return "invalid argument";
+    case AR_ERR_UNSUPPORTED: return "unsupported combination";
+    case AR_ERR_NOMEM: return "out of device memory";
+    case AR_ERR_TOO_LARGE: return "message exceeds the communicator's capacity";
+    case AR_ERR_HIP: return "HIP runtime error";
+    case AR_ERR_TIMEOUT: return "a rank program timed out waiting for a peer";
+    case AR_ERR_BROKEN: return "communicator holds a latched device error";
+  }
+  return "unknown status";
+}
+
+ar_status ar_comm_create(int nranks, size_t max_bytes_per_rank, size_t max_line_bytes_per_rank,
+                         ar_comm_t* out) {
+  if (!out || nranks < 1 || nranks > MAX_RANKS) return AR_ERR_INVALID;
+  *out = nullptr;
+  ar_comm* c = new ar_comm();
+  c->nranks = nranks;
+  c->max_bytes = max_bytes_per_rank;
+  c->max_line_bytes = max_line_bytes_per_rank;
+  if (hipGetDevice(&c->device) != hipSuccess) { delete c; return AR_ERR_HIP; }
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, c->device) == hipSuccess && khz > 0)
+    c->ticks_per_us = (uint64_t)khz / 1000 ? (uint64_t)khz / 1000 : 1;
+  c->timeout_ticks = 5ull * 1000 * 1000 * c->ticks_per_us;  // 5 s
+
+  const uint64_t n = (uint64_t)nranks;
+  c->nflags = umax(65536, 2 * n * (max_bytes_per_rank / 4096 + 8));
+  c->lines_bytes = line_capacity(nranks, max_line_bytes_per_rank);
+  c->stage_stride = align256(max_bytes_per_rank);
+  const uint64_t off_flags = align256(sizeof(Ctl));
+  const uint64_t off_lines = off_flags + align256(c->nflags * 8);
+  const uint64_t off_stage = off_lines + align256(c->lines_bytes);
+  c->ws_bytes = off_stage + (nranks > 1 ? n * c->stage_stride : 0);
+  if (hipMalloc((void**)&c->ws, c->ws_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    delete c;
+    return AR_ERR_NOMEM;
+  }
+  c->ctl = (Ctl*)c->ws;
+  c->flags = (uint64_t*)(c->ws + off_flags);
+  c->lines = c->ws + off_lines;
+  c->stage = c->ws + off_stage;
+  Ctl init = {};
+  init.err_key = 0xffffffffu;
+  if (hipMemset(c->ws, 0, off_stage) != hipSuccess ||
+      hipMemcpy(c->ctl, &init, sizeof(Ctl), hipMemcpyHostToDevice) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(c->ws);
+    delete c;
+    return AR_ERR_HIP;
+  }
+  *out = c;
+  return AR_OK;
+}
+
+ar_status ar_comm_destroy(ar_comm_t c) {
+  if (!c) return AR_ERR_INVALID;
+  const hipError_t e = hipFree(c->ws);
+  delete c;
+  return e == hipSuccess ? AR_OK : AR_ERR_HIP;
+}
+
+size_t ar_comm_workspace_bytes(ar_comm_t c) { return c ? c->ws_bytes : 0; }
+
+ar_status ar_comm_check(ar_comm_t c, ar_stream_t stream, int* err_rank, int* err_step) {
+  if (!c) return AR_ERR_INVALID;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return AR_ERR_HIP;
+  Ctl h;
+  if (hipMemcpy(&h, c->ctl, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return AR_ERR_HIP;
+  if (!h.err_code) return AR_OK;
+  c->broken = true;
+  if (err_rank) *err_rank = h.err_key == 0xffffffffu ? -1 : (int)(h.err_key & 0xff);
+  if (err_step) *err_step = h.err_key == 0xffffffffu ? -1 : (int)(h.err_key >> 8);
+  return (ar_status)h.err_code;
+}
+
+ar_status ar_comm_reset(ar_comm_t c, ar_stream_t stream) {
+  if (!c) return AR_ERR_INVALID;
+  if (ar::launch_reset(c->ctl, (hipStream_t)stream) != hipSuccess) return AR_ERR_HIP;
+  c->broken = false;
+  return AR_OK;
+}
+
+ar_status ar_debug_inject(ar_comm_t c, int rank, int step, uint64_t timeout_us) {
+  if (!c || rank >= c->nranks || rank < -1) return AR_ERR_INVALID;
+  c->inj_rank = rank;
+  c->inj_step = rank < 0 ? -1 : step;
+  c->timeout_ticks = (timeout_us ? timeout_us : 5ull * 1000 * 1000) * c->ticks_per_us;
+  return AR_OK;
+}
+
+ar_status ar_plan_bytes(int nranks, ar_op op, size_t count, ar_dtype dtype, ar_algo algo, ar_proto proto,
+                        size_t chunk_bytes, int in_place, uint64_t* hbm_read, uint64_t* hbm_write,
+                        uint64_t* link_bytes, uint64_t* ntasks) {
+  Geometry g;
+  if (!make_geometry((int)op, (int)algo, (int)proto, (int)dtype, nranks, count, chunk_bytes, in_place, &g))
+    return AR_ERR_INVALID;
+  const Bytes b = account(g);
+  if (hbm_read) *hbm_read = b.rd;
+  if (hbm_write) *hbm_write = b.wr;
+  if (link_bytes)
+    for (int r = 0; r < nranks; ++r) link_bytes[r] = b.link[r];
+  if (ntasks) *ntasks = g.ntasks;
+  return AR_OK;
+}
+
+}  // extern "C"
+
+// Do [a, a+na) and [b, b+nb) overlap?
+static bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+static ar_status run(ar_comm_t c, int op, const void* const* send, void* const* recv, uint64_t count,
+                     int dtype, int algo, int proto, uint64_t chunk_bytes, ar_stream_t stream) {
+  if (!c || !send || !recv) return AR_ERR_INVALID;
+  if (c->broken) return AR_ERR_BROKEN;
+  if (dtype < 0 || dtype > 2 || algo < 0 || algo > 2 || proto < 0 || proto > 2) return AR_ERR_INVALID;
+  if (count == 0) return AR_OK;  // nothing to move; buffers may be null
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != c->device) return AR_ERR_INVALID;
+  const int n = c->nranks;
+  const uint64_t es = (uint64_t)esize_of(dtype);
+  const uint64_t in_bytes = (op == OP_REDUCE_SCATTER ? (uint64_t)n * count : count) * es;
+  const uint64_t out_bytes = (op == OP_ALLGATHER ? (uint64_t)n * count : count) * es;
+  if (count > (1ull << 40)) return AR_ERR_TOO_LARGE;
+  if (umax(in_bytes, out_bytes) > c->max_bytes) return AR_ERR_TOO_LARGE;
+  if (proto != PROTO_SIMPLE && n > 1 && umax(in_bytes, out_bytes) > c->max_line_bytes) return AR_ERR_TOO_LARGE;
+
+  int in_place = 0, same = 0;
+  for (int r = 0; r < n; ++r) {
+    if (!send[r] || !recv[r]) return AR_ERR_INVALID;
+    if (((uintptr_t)send[r] & 15) || ((uintptr_t)recv[r] & 15)) return AR_ERR_INVALID;
+    same += (send[r] == (const void*)recv[r]);
+  }
+  if (same == n && op == OP_ALLREDUCE) in_place = 1;
+  else if (same) return AR_ERR_INVALID;  // partial in-place, or in-place RS / AG
+  // Outputs must not overlap each other, nor (out of place) any input.
+  for (int r = 0; r < n; ++r) {
+    for (int q = 0; q < n; ++q) {
+      if (q != r && overlap(recv[r], out_bytes, recv[q], out_bytes)) return AR_ERR_INVALID;
+      if (!in_place && overlap(recv[r], out_bytes, send[q], in_bytes)) return AR_ERR_INVALID;
+    }
+  }
+
+  Geometry g;
+  if (!make_geometry(op, algo, proto, dtype, n, count, chunk_bytes, in_place, &g)) return AR_ERR_INVALID;
+  if (g.ntasks == 0) return AR_OK;
+  if (g.ntasks >= (1ull << 31)) return AR_ERR_TOO_LARGE;
+  if (g.nflags > c->nflags || staging_bytes(g) > c->lines_bytes) return AR_ERR_TOO_LARGE;
+
+  KArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int r = 0; r < n; ++r) {
+    a.in[r] = (const char*)send[r];
+    a.out[r] = (char*)recv[r];
+  }
+  a.g = g;
+  a.ctl = c->ctl;
+  a.flags = c->flags;
+  a.lines = c->lines;
+  a.stage = c->stage;
+  a.stage_stride = c->stage_stride;
+  a.timeout = c->timeout_ticks;
+  a.inj_rank = c->inj_rank;
+  a.inj_step = c->inj_step;
+  return ar::launch_collective(a, c->device, (hipStream_t)stream) == hipSuccess ? AR_OK : AR_ERR_HIP;
+}
+
+extern "C" {
+
+ar_status ar_allreduce(ar_comm_t c, const void* const* send, void* const* recv, size_t count, ar_dtype dtype,
+                       ar_algo algo, ar_proto proto, size_t chunk_bytes, ar_stream_t stream) {
+  return run(c, OP_ALLREDUCE, send, recv, count, dtype, algo, proto, chunk_bytes, stream);
+}
+
+ar_status ar_reduce_scatter(ar_comm_t c, const void* const* send, void* const* recv, size_t recvcount,
+                            ar_dtype dtype, ar_algo algo, ar_proto proto, size_t chunk_bytes,
+                            ar_stream_t stream) {
+  return run(c, OP_REDUCE_SCATTER, send, recv, recvcount, dtype, algo, proto, chunk_bytes, stream);
+}
+
+ar_status ar_allgather(ar_comm_t c, const void* const* send, void* const* recv, size_t sendcount,
+                       ar_dtype dtype, ar_algo algo, ar_proto proto, size_t chunk_bytes, ar_stream_t stream) {
+  return run(c, OP_ALLGATHER, send, recv, sendcount, dtype, algo, proto, chunk_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,198 @@
+// device.hpp -- payload arithmetic, memory access and rank-to-rank signalling
+// for the gfx950 kernels.
+//
+// Arithmetic ("NCCL collectives, ring all-reduce & launching TP/PP", section
+// "Direct answer": all-reduce sums): fp32 is one IEEE add per term (the build
+// keeps denormals and has no contraction to apply, since there are only adds);
+// int32 adds wrap; bf16 is widened exactly to fp32, added in fp32 and rounded
+// to nearest even when stored or put on the wire.
+//
+// Signalling ("Collective communication: NCCL's algorithms and protocols, and
+// custom all-reduce", section "Protocols"):
+//   Simple  the producer stores its block, makes it visible device-wide with
+//           an agent-scope release fence, then stores a flag; the consumer
+//           polls the flag with agent-scope atomic loads, then an acquire
+//           fence, then reads.  The eight XCDs of an MI355X have private L2
+//           caches, so agent scope (not workgroup scope) is what makes the
+//           data cross XCDs.
+//   LL      each 8-byte line = 4 payload bytes + a 4-byte flag, written and
+//           read as ONE 64-bit agent-scope atomic: a reader that sees the
+//           flag sees the payload, no fence needed.
+//   LL128   each 128-byte line = 120 payload bytes + an 8-byte flag.  gfx950
+//           gives no 128-byte single-copy atomicity, so the writer stores the
+//           payload, issues an agent-scope release fence, then stores the
+//           flag word; the reader polls the flag, issues an acquire fence,
+//           then reads the payload.  The byte layout (and so the 120/128
+//           efficiency) is the page's; the ordering is made explicit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "schedule.hpp"
+
+namespace ar {
+
+// ----------------------------------------------------------------- numerics
+__device__ __forceinline__ uint32_t bf16_round(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;  // quiet NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;                                // nearest even
+}
+
+// Accumulator for the elements of one 4-byte payload word.
+template <int DT> struct Word;
+
+template <> struct Word<DT_F32> {
+  float a;
+  __device__ __forceinline__ static Word widen(uint32_t w) { return {__uint_as_float(w)}; }
+  __device__ __forceinline__ void add(const Word& o) { a = a + o.a; }
+  __device__ __forceinline__ uint32_t narrow() const { return __float_as_uint(a); }
+};
+
+template <> struct Word<DT_I32> {
+  uint32_t a;
+  __device__ __forceinline__ static Word widen(uint32_t w) { return {w}; }
+  __device__ __forceinline__ void add(const Word& o) { a = a + o.a; }  // wraps
+  __device__ __forceinline__ uint32_t narrow() const { return a; }
+};
+
+template <> struct Word<DT_BF16> {
+  float lo, hi;  // element 0 in the low half-word, element 1 in the high one
+  __device__ __forceinline__ static Word widen(uint32_t w) {
+    return {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+  }
+  __device__ __forceinline__ void add(const Word& o) { lo = lo + o.lo; hi = hi + o.hi; }
+  __device__ __forceinline__ uint32_t narrow() const { return bf16_round(lo) | (bf16_round(hi) << 16); }
+};
+
+// A 16-byte vector of payload as four word accumulators.
+template <int DT> struct Vec {
+  Word<DT> w[4];
+  __device__ __forceinline__ static Vec widen(const uint4& v) {
+    Vec r;
+    r.w[0] = Word<DT>::widen(v.x); r.w[1] = Word<DT>::widen(v.y);
+    r.w[2] = Word<DT>::widen(v.z); r.w[3] = Word<DT>::widen(v.w);
+    return r;
+  }
+  __device__ __forceinline__ void add(const Vec& o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i].add(o.w[i]);
+  }
+  __device__ __forceinline__ uint4 narrow() const {
+    return make_uint4(w[0].narrow(), w[1].narrow(), w[2].narrow(), w[3].narrow());
+  }
+};
+
+// One payload element (tails and unaligned slices), as an accumulator.
+template <int DT> struct Elem {
+  static constexpr int size = (DT == DT_BF16) ? 2 : 4;
+  __device__ __forceinline__ static float ldf(const char* p) {
+    if (DT == DT_BF16) return __uint_as_float((uint32_t)(*(const uint16_t*)p) << 16);
+    return *(const float*)p;
+  }
+  __device__ __forceinline__ static void stf(char* p, float v) {
+    if (DT == DT_BF16) *(uint16_t*)p = (uint16_t)bf16_round(v);
+    else *(float*)p = v;
+  }
+};
+
+// ------------------------------------------------------------ memory access
+__device__ __forceinline__ uint4 ld16(const char* p) { return *(const uint4*)p; }
+__device__ __forceinline__ void st16(char* p, const uint4& v) { *(uint4*)p = v; }
+
+// Load a 16-byte vector of which only `nbytes` (< 16, whole elements) exist;
+// the rest reads as zero.  `esize` = 2 or 4.
+__device__ __forceinline__ uint4 ld_partial(const char* p, uint32_t nbytes, int esize) {
+  uint32_t w[4] = {0, 0, 0, 0};
+  for (uint32_t b = 0; b < nbytes; b += esize) {
+    uint32_t v = (esize == 2) ? (uint32_t)(*(const uint16_t*)(p + b)) : *(const uint32_t*)(p + b);
+    w[b >> 2] |= v << ((b & 3) * 8);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ void st_partial(char* p, const uint4& v, uint32_t nbytes, int esize) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (uint32_t b = 0; b < nbytes; b += esize) {
+    const uint32_t x = w[b >> 2] >> ((b & 3) * 8);
+    if (esize == 2) *(uint16_t*)(p + b) = (uint16_t)x;
+    else *(uint32_t*)(p + b) = x;
+  }
+}
+
+// Load / store `nbytes` (<= 16, whole elements) at a pointer that may be only
+// element-aligned.
+__device__ __forceinline__ uint4 ld_any(const char* p, uint32_t nbytes, int esize) {
+  if (nbytes == 16 && ((uintptr_t)p & 15) == 0) return ld16(p);
+  return ld_partial(p, nbytes, esize);
+}
+__device__ __forceinline__ void st_any(char* p, const uint4& v, uint32_t nbytes, int esize) {
+  if (nbytes == 16 && ((uintptr_t)p & 15) == 0) st16(p, v);
+  else st_partial(p, v, nbytes, esize);
+}
+
+// ------------------------------------------------------- atomics and fences
+__device__ __forceinline__ uint64_t ld_flag(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_flag(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// ---------------------------------------------------------- control block
+// Lives at the start of the communicator's workspace (zeroed at creation).
+struct Ctl {
+  uint32_t ticket;    // next task ticket of the running call
+  uint32_t done;      // workgroups of the running call that have finished
+  uint64_t epoch;     // calls completed on this communicator
+  uint32_t abort;     // a wait timed out: every rank program gives up
+  uint32_t err_code;  // 0 or the ar_status of the latched error
+  uint32_t err_key;   // min over blocked waits of (step << 8 | rank), ~0 if none
+  uint32_t pad;
+};
+
+struct KArgs {
+  const char* in[MAX_RANKS];
+  char* out[MAX_RANKS];
+  Geometry g;
+  Ctl* ctl;
+  uint64_t* flags;
+  char* lines;          // LL / LL128 staging
+  char* stage;          // ring reduce-scatter partials: one full buffer per rank
+  uint64_t stage_stride;
+  uint64_t timeout;     // wall-clock ticks (100 MHz) a wait may last
+  int32_t inj_rank, inj_step;
+};
+
+__device__ __forceinline__ void note_blocked(Ctl* c, int step, int rank) {
+  __hip_atomic_fetch_min(&c->err_key, (uint32_t)((step << 8) | rank), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void raise_timeout(Ctl* c, int step, int rank) {
+  note_blocked(c, step, rank);
+  __hip_atomic_store(&c->err_code, 6u /* AR_ERR_TIMEOUT */, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&c->abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Bounded spin of ONE thread until *f >= target.  Returns false if the call
+// is aborted (by this wait timing out or by another one).
+__device__ __forceinline__ bool wait_ge(const uint64_t* f, uint64_t target, const KArgs& a, int step,
+                                        int rank) {
+  if (ld_flag(f) >= target) return true;
+  const uint64_t t0 = wall_clock64();
+  while (true) {
+    __builtin_amdgcn_s_sleep(1);
+    if (ld_flag(f) >= target) return true;
+    if (ld_u32(&a.ctl->abort)) { note_blocked(a.ctl, step, rank); return false; }
+    if (wall_clock64() - t0 > a.timeout) { raise_timeout(a.ctl, step, rank); return false; }
+  }
+}
+
+}  // namespace ar

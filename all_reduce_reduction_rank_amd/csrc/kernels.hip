@@ -1,0 +1,653 @@
+// kernels.hip -- gfx950 kernels of the all-reduce family.
+//
+// One persistent kernel per call.  Each workgroup (256 threads, 4 wave64s)
+// repeatedly takes a ticket, decodes it into a task (schedule.hpp) and runs
+// it: one rank program's work on one tile.  Payload moves through HBM in
+// 16-byte vectors (global_load/store_dwordx4), several vectors in flight per
+// thread.  This is a streaming reduction (under 0.1 flop per byte): no MFMA,
+// the bound is HBM bandwidth.
+//
+// Which rank reads and writes what at each step follows "Collective
+// communication: NCCL's algorithms and protocols, and custom all-reduce",
+// section "Algorithms" (ring, one-shot, two-shot) and "NCCL collectives, ring
+// all-reduce & launching TP/PP", section "Direct answer" (reduce-scatter,
+// all-gather, ring = reduce-scatter + all-gather); the transfer encodings
+// follow the former page's section "Protocols" (see device.hpp).
+#include "device.hpp"
+
+namespace ar {
+
+constexpr int U_SIMPLE = 4;  // 16-byte vectors in flight per thread per source
+constexpr int U_LL = 4;      // LL words per thread per pass
+constexpr int U_LL128 = 4;   // LL128 line groups (8 lines of a wave) per pass
+
+// =============================================================== Simple path
+// dst = fold(term(0), ..., term(n-1)) over `nbytes` (whole elements); a term
+// is a plain pointer.  One term = raw copy (bit-exact for every type).
+template <int DT, class Term>
+__device__ __forceinline__ void simple_stream(Term term, int nterms, char* dst, uint64_t nbytes) {
+  const int es = Elem<DT>::size;
+  bool aligned = ((uintptr_t)dst & 15) == 0;
+  for (int i = 0; i < nterms; ++i) aligned = aligned && (((uintptr_t)term(i) & 15) == 0);
+  const uint64_t nfull = aligned ? nbytes / 16 : 0;
+  for (uint64_t base = threadIdx.x; base < nfull; base += (uint64_t)U_SIMPLE * WG_THREADS) {
+    uint4 x[U_SIMPLE];
+    Vec<DT> acc[U_SIMPLE];
+#pragma unroll
+    for (int u = 0; u < U_SIMPLE; ++u) {
+      const uint64_t v = base + (uint64_t)u * WG_THREADS;
+      x[u] = (v < nfull) ? ld16(term(0) + v * 16) : make_uint4(0, 0, 0, 0);
+    }
+    if (nterms == 1) {
+#pragma unroll
+      for (int u = 0; u < U_SIMPLE; ++u) {
+        const uint64_t v = base + (uint64_t)u * WG_THREADS;
+        if (v < nfull) st16(dst + v * 16, x[u]);
+      }
+      continue;
+    }
+#pragma unroll
+    for (int u = 0; u < U_SIMPLE; ++u) acc[u] = Vec<DT>::widen(x[u]);
+    for (int i = 1; i < nterms; ++i) {
+      const char* p = term(i);
+#pragma unroll
+      for (int u = 0; u < U_SIMPLE; ++u) {
+        const uint64_t v = base + (uint64_t)u * WG_THREADS;
+        x[u] = (v < nfull) ? ld16(p + v * 16) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U_SIMPLE; ++u) acc[u].add(Vec<DT>::widen(x[u]));
+    }
+#pragma unroll
+    for (int u = 0; u < U_SIMPLE; ++u) {
+      const uint64_t v = base + (uint64_t)u * WG_THREADS;
+      if (v < nfull) st16(dst + v * 16, acc[u].narrow());
+    }
+  }
+  // Remainder (and every vector of a misaligned range): element-exact path.
+  const uint64_t done = nfull * 16;
+  const uint64_t nrest = cdiv(nbytes - done, 16);
+  for (uint64_t v = threadIdx.x; v < nrest; v += WG_THREADS) {
+    const uint64_t off = done + v * 16;
+    const uint32_t nb = (uint32_t)umin(16, nbytes - off);
+    uint4 x = ld_any(term(0) + off, nb, es);
+    if (nterms > 1) {
+      Vec<DT> acc = Vec<DT>::widen(x);
+      for (int i = 1; i < nterms; ++i) acc.add(Vec<DT>::widen(ld_any(term(i) + off, nb, es)));
+      x = acc.narrow();
+    }
+    st_any(dst + off, x, nb, es);
+  }
+}
+
+// Workgroup waits until *f >= target (thread 0 polls); false if aborted.
+__device__ __forceinline__ bool wg_wait(const KArgs& a, const uint64_t* f, uint64_t target, int step,
+                                        int rank) {
+  __shared__ int s_ok;
+  if (threadIdx.x == 0) s_ok = wait_ge(f, target, a, step, rank) ? 1 : 0;
+  __syncthreads();
+  const bool ok = s_ok != 0;
+  fence_acquire();
+  __syncthreads();  // s_ok may be rewritten by the next wait
+  return ok;
+}
+
+// Workgroup publishes everything it stored, then sets *f = v.
+__device__ __forceinline__ void wg_signal(const KArgs& a, uint64_t* f, uint64_t v, int step, int rank) {
+  fence_release();
+  __syncthreads();
+  if (threadIdx.x == 0 && !(rank == a.inj_rank && step == a.inj_step)) st_flag(f, v);
+}
+
+// ============================================================ LL / LL128 path
+// A term of a line-processing pass: a plain buffer or a staging slot.
+struct LTerm {
+  const char* plain;  // payload bytes of the tile, or nullptr
+  const char* lines;  // first line of the tile in staging, or nullptr
+};
+
+__device__ __forceinline__ uint32_t ld_word(const char* p, uint32_t nb, int es) {
+  if (nb == 4 && ((uintptr_t)p & 3) == 0) return *(const uint32_t*)p;
+  uint32_t w = 0;
+  for (uint32_t b = 0; b < nb; b += es)
+    w |= (es == 2 ? (uint32_t)(*(const uint16_t*)(p + b)) : *(const uint32_t*)(p + b)) << (8 * b);
+  return w;
+}
+__device__ __forceinline__ void st_word(char* p, uint32_t w, uint32_t nb, int es) {
+  if (nb == 4 && ((uintptr_t)p & 3) == 0) { *(uint32_t*)p = w; return; }
+  for (uint32_t b = 0; b < nb; b += es) {
+    if (es == 2) *(uint16_t*)(p + b) = (uint16_t)(w >> (8 * b));
+    else *(uint32_t*)(p + b) = w;
+  }
+}
+
+// LL: 8-byte lines {payload word, flag}, written and read as one 64-bit
+// agent-scope atomic.  Thread t handles words t, t+256, ... of the tile, so
+// each wave's line stores and loads are contiguous.
+//
+//   out_plain: store the result word here (may be null)
+//   out_lines: put the result on the wire as lines (may be null)
+template <int DT, class Terms>
+__device__ __forceinline__ void ll_pass(const KArgs& a, Terms terms, int nterms, char* out_plain,
+                                        char* out_lines, uint64_t nbytes, uint32_t flag, int step,
+                                        int rank) {
+  const int es = Elem<DT>::size;
+  const uint64_t nwords = cdiv(nbytes, 4);
+  for (uint64_t base = threadIdx.x; base < nwords; base += (uint64_t)U_LL * WG_THREADS) {
+    uint32_t val[U_LL];
+    Word<DT> acc[U_LL];
+    for (int i = 0; i < nterms; ++i) {
+      const LTerm tm = terms(i);
+      if (tm.plain) {
+#pragma unroll
+        for (int u = 0; u < U_LL; ++u) {
+          const uint64_t w = base + (uint64_t)u * WG_THREADS;
+          val[u] = (w < nwords) ? ld_word(tm.plain + 4 * w, (uint32_t)umin(4, nbytes - 4 * w), es) : 0u;
+        }
+      } else {
+        const uint64_t* ln = (const uint64_t*)tm.lines;
+        uint64_t got[U_LL];
+        bool ready = true;
+#pragma unroll
+        for (int u = 0; u < U_LL; ++u) {
+          const uint64_t w = base + (uint64_t)u * WG_THREADS;
+          got[u] = (w < nwords) ? ld_flag(ln + w) : ((uint64_t)flag << 32);
+          ready = ready && (uint32_t)(got[u] >> 32) == flag;
+        }
+        if (!ready) {
+          const uint64_t t0 = wall_clock64();
+          while (true) {
+            __builtin_amdgcn_s_sleep(1);
+            ready = true;
+#pragma unroll
+            for (int u = 0; u < U_LL; ++u) {
+              const uint64_t w = base + (uint64_t)u * WG_THREADS;
+              if ((uint32_t)(got[u] >> 32) != flag) got[u] = ld_flag(ln + w);
+              ready = ready && (uint32_t)(got[u] >> 32) == flag;
+            }
+            if (ready) break;
+            if (ld_u32(&a.ctl->abort)) { note_blocked(a.ctl, step, rank); break; }
+            if (wall_clock64() - t0 > a.timeout) { raise_timeout(a.ctl, step, rank); break; }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U_LL; ++u) val[u] = (uint32_t)got[u];
+      }
+      if (nterms > 1) {
+#pragma unroll
+        for (int u = 0; u < U_LL; ++u) {
+          const Word<DT> x = Word<DT>::widen(val[u]);
+          if (i == 0) acc[u] = x; else acc[u].add(x);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U_LL; ++u) {
+      const uint64_t w = base + (uint64_t)u * WG_THREADS;
+      if (w >= nwords) continue;
+      const uint32_t r = (nterms > 1) ? acc[u].narrow() : val[u];
+      if (out_plain) st_word(out_plain + 4 * w, r, (uint32_t)umin(4, nbytes - 4 * w), es);
+      if (out_lines) st_flag((uint64_t*)out_lines + w, ((uint64_t)flag << 32) | r);
+    }
+  }
+}
+
+// Bytes [off, off+nb) of a tile, nb <= 16, whole elements, from a pointer
+// that is at least element-aligned; 8-byte aligned 8/16-byte pieces load
+// as dwordx2.
+__device__ __forceinline__ uint4 ld_piece(const char* p, uint32_t nb, int es) {
+  if (((uintptr_t)p & 7) == 0) {
+    if (nb == 16) {
+      const uint2 lo = *(const uint2*)p, hi = *(const uint2*)(p + 8);
+      return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+    if (nb == 8) {
+      const uint2 lo = *(const uint2*)p;
+      return make_uint4(lo.x, lo.y, 0, 0);
+    }
+  }
+  return ld_partial(p, nb, es);
+}
+__device__ __forceinline__ void st_piece(char* p, const uint4& v, uint32_t nb, int es) {
+  if (((uintptr_t)p & 7) == 0) {
+    if (nb == 16) { *(uint2*)p = make_uint2(v.x, v.y); *(uint2*)(p + 8) = make_uint2(v.z, v.w); return; }
+    if (nb == 8) { *(uint2*)p = make_uint2(v.x, v.y); return; }
+  }
+  st_partial(p, v, nb, es);
+}
+
+// LL128: 128-byte lines {120 payload bytes, 8-byte flag}.  Lane q (0..7) of
+// an 8-lane group owns bytes [16q, 16q+16) of its line: lanes 0..6 carry 16
+// payload bytes, lane 7 carries 8 payload bytes and the flag.  Line L of a
+// tile carries payload bytes [120L, 120L+120).  Each wave handles U_LL128
+// groups of 8 consecutive lines per pass (1 KiB per store instruction).
+template <int DT, class Terms>
+__device__ __forceinline__ void ll128_pass(const KArgs& a, Terms terms, int nterms, char* out_plain,
+                                           char* out_lines, uint64_t nbytes, uint64_t flag, int step,
+                                           int rank) {
+  const int es = Elem<DT>::size;
+  const uint64_t nlines = cdiv(nbytes, LL128_DATA);
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int q = lane % 8, grp = lane / 8;
+  const uint32_t lane_cap = (q < 7) ? 16u : 8u;
+  for (uint64_t l0 = (uint64_t)wave * U_LL128 * 8; l0 < nlines; l0 += 4ull * U_LL128 * 8) {
+    uint64_t line[U_LL128];
+    uint32_t nb[U_LL128];  // payload bytes this lane owns in each of its lines
+#pragma unroll
+    for (int u = 0; u < U_LL128; ++u) {
+      line[u] = l0 + (uint64_t)u * 8 + grp;
+      const uint64_t off = line[u] * LL128_DATA + 16ull * q;
+      nb[u] = (line[u] < nlines && off < nbytes) ? (uint32_t)umin(lane_cap, nbytes - off) : 0u;
+    }
+    uint4 val[U_LL128];
+    Vec<DT> acc[U_LL128];
+    for (int i = 0; i < nterms; ++i) {
+      const LTerm tm = terms(i);
+      if (tm.plain) {
+#pragma unroll
+        for (int u = 0; u < U_LL128; ++u)
+          val[u] = nb[u] ? ld_piece(tm.plain + line[u] * LL128_DATA + 16ull * q, nb[u], es)
+                         : make_uint4(0, 0, 0, 0);
+      } else {
+        // Every lane polls its own line's flag word, then acquire, then reads.
+        bool ready = true;
+#pragma unroll
+        for (int u = 0; u < U_LL128; ++u) {
+          if (line[u] < nlines)
+            ready = ready && ld_flag((const uint64_t*)(tm.lines + line[u] * LL128_LINE + LL128_DATA)) == flag;
+        }
+        if (!ready) {
+          const uint64_t t0 = wall_clock64();
+          while (true) {
+            __builtin_amdgcn_s_sleep(1);
+            ready = true;
+#pragma unroll
+            for (int u = 0; u < U_LL128; ++u) {
+              if (line[u] < nlines)
+                ready = ready &&
+                        ld_flag((const uint64_t*)(tm.lines + line[u] * LL128_LINE + LL128_DATA)) == flag;
+            }
+            if (ready) break;
+            if (ld_u32(&a.ctl->abort)) { note_blocked(a.ctl, step, rank); break; }
+            if (wall_clock64() - t0 > a.timeout) { raise_timeout(a.ctl, step, rank); break; }
+          }
+        }
+        fence_acquire();
+#pragma unroll
+        for (int u = 0; u < U_LL128; ++u) {
+          const char* p = tm.lines + line[u] * LL128_LINE + 16ull * q;
+          if (!nb[u]) val[u] = make_uint4(0, 0, 0, 0);
+          else if (q < 7) val[u] = ld16(p);
+          else { const uint2 lo = *(const uint2*)p; val[u] = make_uint4(lo.x, lo.y, 0, 0); }
+        }
+      }
+      if (nterms > 1) {
+#pragma unroll
+        for (int u = 0; u < U_LL128; ++u) {
+          const Vec<DT> x = Vec<DT>::widen(val[u]);
+          if (i == 0) acc[u] = x; else acc[u].add(x);
+        }
+      }
+    }
+    uint4 res[U_LL128];
+#pragma unroll
+    for (int u = 0; u < U_LL128; ++u) res[u] = (nterms > 1) ? acc[u].narrow() : val[u];
+    if (out_plain) {
+#pragma unroll
+      for (int u = 0; u < U_LL128; ++u)
+        if (nb[u]) st_piece(out_plain + line[u] * LL128_DATA + 16ull * q, res[u], nb[u], es);
+    }
+    if (out_lines) {
+      // Payload of every line first (a partial lane stores zero padding) ...
+#pragma unroll
+      for (int u = 0; u < U_LL128; ++u) {
+        if (line[u] >= nlines) continue;
+        char* p = out_lines + line[u] * LL128_LINE + 16ull * q;
+        if (q < 7) st16(p, res[u]);
+        else *(uint2*)p = make_uint2(res[u].x, res[u].y);
+      }
+      // ... made visible device-wide, then the flags.
+      fence_release();
+#pragma unroll
+      for (int u = 0; u < U_LL128; ++u)
+        if (q == 7 && line[u] < nlines)
+          st_flag((uint64_t*)(out_lines + line[u] * LL128_LINE + LL128_DATA), flag);
+    }
+  }
+}
+
+// One line-protocol pass, dispatched on the protocol.
+template <int DT, int PROTO, class Terms>
+__device__ __forceinline__ void line_pass(const KArgs& a, Terms terms, int nterms, char* out_plain,
+                                          char* out_lines, uint64_t nbytes, uint64_t epoch, int step,
+                                          int rank) {
+  if constexpr (PROTO == PROTO_LL) {
+    const uint32_t flag = (uint32_t)(epoch % 0xffffffffull) + 1u;
+    ll_pass<DT>(a, terms, nterms, out_plain, out_lines, nbytes, flag, step, rank);
+  } else {
+    ll128_pass<DT>(a, terms, nterms, out_plain, out_lines, nbytes, epoch + 1, step, rank);
+  }
+}
+
+// Staging address of tile `tile` of slot `slot`.
+__device__ __forceinline__ char* slot_tile(const KArgs& a, uint64_t slot, uint64_t tile) {
+  return a.lines + (slot * a.g.slot_lines + tile * a.g.tile_lines) * a.g.line_bytes;
+}
+
+// =================================================================== tasks
+template <int DT, int PROTO, int KIND>
+__device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t epoch) {
+  const Geometry& g = a.g;
+  const int n = g.nranks;
+  const uint64_t es = (uint64_t)g.esize;
+  const uint64_t nbytes = (k.hi - k.lo) * es;
+  const uint64_t tag = (epoch + 1) << 8;  // Simple flag values of this call
+
+  if constexpr (KIND == K_COPY) {
+    const uint64_t off = k.lo * es;
+    simple_stream<DT>([&](int) { return a.in[0] + off; }, 1, a.out[0] + off, nbytes);
+  }
+
+  if constexpr (KIND == K_ONESHOT) {
+    const uint64_t off = k.lo * es;
+    const int r = k.rank;
+    if constexpr (PROTO == PROTO_SIMPLE) {
+      if (!g.in_place) {
+        simple_stream<DT>([&](int i) { return a.in[i] + off; }, n, a.out[r] + off, nbytes);
+        return;
+      }
+      // In place: every rank program of this tile reads all N inputs into
+      // registers (a tile is at most 16 KiB: 4 vectors per thread), signals
+      // that it has read (step 0), waits for the other N-1, then writes.
+      const int es_i = (int)es;
+      uint4 res[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint64_t o = (threadIdx.x + (uint64_t)u * WG_THREADS) * 16;
+        res[u] = make_uint4(0, 0, 0, 0);
+        if (o < nbytes) {
+          const uint32_t nb = (uint32_t)umin(16, nbytes - o);
+          Vec<DT> acc = Vec<DT>::widen(ld_any(a.in[0] + off + o, nb, es_i));
+          for (int i = 1; i < n; ++i) acc.add(Vec<DT>::widen(ld_any(a.in[i] + off + o, nb, es_i)));
+          res[u] = acc.narrow();
+        }
+      }
+      uint64_t* fl = a.flags + k.tile * n;
+      wg_signal(a, fl + r, tag + 1, 0, r);
+      bool ok = true;
+      for (int i = 0; i < n && ok; ++i) ok = wg_wait(a, fl + i, tag + 1, 1, r);
+      if (!ok) return;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint64_t o = (threadIdx.x + (uint64_t)u * WG_THREADS) * 16;
+        if (o < nbytes) st_any(a.out[r] + off + o, res[u], (uint32_t)umin(16, nbytes - o), es_i);
+      }
+    } else {
+      if (k.phase == PH_SEND) {  // rank r puts its input tile on the wire once
+        line_pass<DT, PROTO>(a, [&](int) { return LTerm{a.in[r] + off, nullptr}; }, 1, nullptr,
+                             slot_tile(a, r, k.tile), nbytes, epoch, 0, r);
+      } else {  // rank r sums all N in rank order: own input, peers' lines
+        line_pass<DT, PROTO>(
+            a,
+            [&](int i) {
+              if (i == r && !g.in_place) return LTerm{a.in[r] + off, nullptr};
+              return LTerm{nullptr, slot_tile(a, i, k.tile)};
+            },
+            n, a.out[r] + off, nullptr, nbytes, epoch, 1, r);
+      }
+    }
+  }
+
+  if constexpr (KIND == K_TWOSHOT) {
+    const uint64_t j = k.block;
+    const uint64_t off = (block_lo(g, j) + k.lo) * es;
+    const int r = k.rank;
+    if constexpr (PROTO == PROTO_SIMPLE) {
+      uint64_t* fl = a.flags + j * g.tiles + k.tile;
+      if (k.phase == PH_FOLD) {  // shot 1: rank j sums block j of every rank
+        simple_stream<DT>([&](int i) { return a.in[i] + off; }, n, a.out[j] + off, nbytes);
+        wg_signal(a, fl, tag + 1, 0, r);
+      } else {  // shot 2: rank r reads block j's sum back
+        if (!wg_wait(a, fl, tag + 1, 1, r)) return;
+        simple_stream<DT>([&](int) { return (const char*)a.out[j] + off; }, 1, a.out[r] + off, nbytes);
+      }
+    } else {
+      const uint64_t nn = (uint64_t)n * n;
+      if (k.phase == PH_SEND) {  // rank r sends its slice of block j to owner j
+        line_pass<DT, PROTO>(a, [&](int) { return LTerm{a.in[r] + off, nullptr}; }, 1, nullptr,
+                             slot_tile(a, (uint64_t)r * n + j, k.tile), nbytes, epoch, 0, r);
+      } else if (k.phase == PH_RECV_FOLD) {  // owner j sums, keeps and publishes block j
+        line_pass<DT, PROTO>(
+            a,
+            [&](int i) {
+              if ((uint64_t)i == j) return LTerm{a.in[j] + off, nullptr};
+              return LTerm{nullptr, slot_tile(a, (uint64_t)i * n + j, k.tile)};
+            },
+            n, a.out[j] + off, slot_tile(a, nn + j, k.tile), nbytes, epoch, 1, r);
+      } else {  // rank r receives block j's sum
+        line_pass<DT, PROTO>(a, [&](int) { return LTerm{nullptr, slot_tile(a, nn + j, k.tile)}; }, 1,
+                             a.out[r] + off, nullptr, nbytes, epoch, 2, r);
+      }
+    }
+  }
+
+  if constexpr (KIND == K_RS_DIRECT) {
+    const uint64_t j = k.block;
+    const uint64_t in_off = (block_lo(g, j) + k.lo) * es, out_off = k.lo * es;
+    const int r = k.rank;
+    if constexpr (PROTO == PROTO_SIMPLE) {
+      simple_stream<DT>([&](int i) { return a.in[i] + in_off; }, n, a.out[j] + out_off, nbytes);
+    } else {
+      if (k.phase == PH_SEND) {
+        line_pass<DT, PROTO>(a, [&](int) { return LTerm{a.in[r] + in_off, nullptr}; }, 1, nullptr,
+                             slot_tile(a, (uint64_t)r * n + j, k.tile), nbytes, epoch, 0, r);
+      } else {
+        line_pass<DT, PROTO>(
+            a,
+            [&](int i) {
+              if ((uint64_t)i == j) return LTerm{a.in[j] + in_off, nullptr};
+              return LTerm{nullptr, slot_tile(a, (uint64_t)i * n + j, k.tile)};
+            },
+            n, a.out[j] + out_off, nullptr, nbytes, epoch, 1, r);
+      }
+    }
+  }
+
+  if constexpr (KIND == K_AG_DIRECT) {
+    const uint64_t j = k.block;
+    const uint64_t in_off = k.lo * es, out_off = (block_lo(g, j) + k.lo) * es;
+    const int r = k.rank;
+    if constexpr (PROTO == PROTO_SIMPLE) {
+      simple_stream<DT>([&](int) { return a.in[j] + in_off; }, 1, a.out[r] + out_off, nbytes);
+    } else {
+      if (k.phase == PH_SEND) {  // rank j publishes its shard and keeps its own copy
+        line_pass<DT, PROTO>(a, [&](int) { return LTerm{a.in[j] + in_off, nullptr}; }, 1,
+                             a.out[j] + out_off, slot_tile(a, j, k.tile), nbytes, epoch, 0, r);
+      } else {
+        line_pass<DT, PROTO>(a, [&](int) { return LTerm{nullptr, slot_tile(a, j, k.tile)}; }, 1,
+                             a.out[r] + out_off, nullptr, nbytes, epoch, 1, r);
+      }
+    }
+  }
+
+  if constexpr (KIND == K_RING) {
+    const int j = (int)k.block;
+    const int s = k.step, q = k.rank;
+    const int steps = g.steps;
+    const uint64_t boff = (block_lo(g, (uint64_t)j) + k.lo) * es;  // block coordinates
+    const uint64_t loff = k.lo * es;                               // within a per-rank slice
+    auto R = [&](int x) { return rank_mod((int64_t)x, n); };
+    if constexpr (PROTO == PROTO_SIMPLE) {
+      uint64_t* fl = a.flags + k.chain;
+      if (s > 0 && !wg_wait(a, fl, tag + (uint64_t)s, s, q)) return;
+      if (g.op == OP_ALLREDUCE) {
+        if (s < n - 1) {  // reduce step: rank q adds its input to the partial from q-1
+          const char* src = (s == 0) ? a.in[R(j + 1)] + boff : (const char*)a.out[R(j + 1 + s)] + boff;
+          const char* own = a.in[q] + boff;
+          simple_stream<DT>([&](int i) { return i == 0 ? src : own; }, 2, a.out[q] + boff, nbytes);
+        } else {          // copy step: rank q copies the finished block from q-1
+          const char* src = a.out[R(q - 1)] + boff;
+          simple_stream<DT>([&](int) { return src; }, 1, a.out[q] + boff, nbytes);
+        }
+      } else if (g.op == OP_REDUCE_SCATTER) {
+        const char* src = (s == 0) ? a.in[R(j + 1)] + boff
+                                   : (const char*)(a.stage + (uint64_t)R(j + 1 + s) * a.stage_stride + boff);
+        char* dst = (s == n - 2) ? a.out[j] + loff : a.stage + (uint64_t)q * a.stage_stride + boff;
+        const char* own = a.in[q] + boff;
+        simple_stream<DT>([&](int i) { return i == 0 ? src : own; }, 2, dst, nbytes);
+      } else {  // all-gather: step 0 = rank j's own copy, step s = rank j+s receives
+        const char* src = (s <= 1) ? a.in[j] + loff : (const char*)a.out[R(q - 1)] + boff;
+        simple_stream<DT>([&](int) { return src; }, 1, a.out[q] + boff, nbytes);
+      }
+      if (s < steps - 1) wg_signal(a, fl, tag + (uint64_t)s + 1, s, q);
+    } else {
+      // Transfer x of block j (made by step x, read by step x+1) in slot
+      // j*(steps-1)+x.
+      auto wire = [&](int x) { return slot_tile(a, (uint64_t)j * (steps - 1) + x, k.tile); };
+      const bool last = (s == steps - 1);
+      if (g.op == OP_ALLREDUCE) {
+        if (s == 0) {  // rank j+1 puts its block j on the wire
+          line_pass<DT, PROTO>(a, [&](int) { return LTerm{a.in[q] + boff, nullptr}; }, 1, nullptr,
+                               wire(0), nbytes, epoch, s, q);
+        } else if (s <= n - 1) {  // reduce receive; rank j (s = n-1) keeps the sum
+          const bool owner = (s == n - 1);
+          line_pass<DT, PROTO>(
+              a,
+              [&](int i) { return i == 0 ? LTerm{nullptr, wire(s - 1)} : LTerm{a.in[q] + boff, nullptr}; },
+              2, owner ? a.out[q] + boff : nullptr, wire(s), nbytes, epoch, s, q);
+        } else {  // copy receive
+          line_pass<DT, PROTO>(a, [&](int) { return LTerm{nullptr, wire(s - 1)}; }, 1, a.out[q] + boff,
+                               last ? nullptr : wire(s), nbytes, epoch, s, q);
+        }
+      } else if (g.op == OP_REDUCE_SCATTER) {
+        if (s == 0) {
+          line_pass<DT, PROTO>(a, [&](int) { return LTerm{a.in[q] + boff, nullptr}; }, 1, nullptr,
+                               wire(0), nbytes, epoch, s, q);
+        } else {
+          line_pass<DT, PROTO>(
+              a,
+              [&](int i) { return i == 0 ? LTerm{nullptr, wire(s - 1)} : LTerm{a.in[q] + boff, nullptr}; },
+              2, last ? a.out[j] + loff : nullptr, last ? nullptr : wire(s), nbytes, epoch, s, q);
+        }
+      } else {
+        if (s == 0) {  // rank j: own copy and first send
+          line_pass<DT, PROTO>(a, [&](int) { return LTerm{a.in[j] + loff, nullptr}; }, 1, a.out[j] + boff,
+                               wire(0), nbytes, epoch, s, q);
+        } else {
+          line_pass<DT, PROTO>(a, [&](int) { return LTerm{nullptr, wire(s - 1)}; }, 1, a.out[q] + boff,
+                               last ? nullptr : wire(s), nbytes, epoch, s, q);
+        }
+      }
+    }
+  }
+}
+
+// ================================================================== kernel
+template <int DT, int PROTO, int KIND>
+__global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
+  __shared__ uint64_t s_epoch;
+  __shared__ uint32_t s_ticket;
+  if (threadIdx.x == 0) s_epoch = __hip_atomic_load(&a.ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t ntasks = (uint32_t)a.g.ntasks;
+  while (true) {
+    if (threadIdx.x == 0) {
+      uint32_t t = 0xffffffffu;
+      if (!ld_u32(&a.ctl->abort))
+        t = __hip_atomic_fetch_add(&a.ctl->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_ticket = t;
+    }
+    __syncthreads();
+    const uint32_t t = s_ticket;
+    const uint64_t epoch = s_epoch;
+    __syncthreads();
+    if (t >= ntasks) break;
+    const Task k = decode(a.g, t);
+    if (k.phase != PH_NONE) run_task<DT, PROTO, KIND>(a, k, epoch);
+  }
+  if (threadIdx.x == 0) {
+    const uint32_t d = __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == gridDim.x - 1) {  // last workgroup out: rearm for the next call
+      __hip_atomic_store(&a.ctl->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&a.ctl->epoch, 1ull, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Clears a latched error (one thread).
+__global__ void reset_kernel(Ctl* c) {
+  c->abort = 0;
+  c->err_code = 0;
+  c->err_key = 0xffffffffu;
+}
+
+// ============================================================== launching
+using KernelFn = void (*)(KArgs);
+
+template <int DT, int PROTO>
+static KernelFn pick_kind(int kind) {
+  switch (kind) {
+    case K_ONESHOT: return collective_kernel<DT, PROTO, K_ONESHOT>;
+    case K_TWOSHOT: return collective_kernel<DT, PROTO, K_TWOSHOT>;
+    case K_RS_DIRECT: return collective_kernel<DT, PROTO, K_RS_DIRECT>;
+    case K_AG_DIRECT: return collective_kernel<DT, PROTO, K_AG_DIRECT>;
+    case K_RING: return collective_kernel<DT, PROTO, K_RING>;
+    default: return nullptr;
+  }
+}
+
+template <int DT>
+static KernelFn pick_proto(int proto, int kind) {
+  if (kind == K_COPY) return collective_kernel<DT, PROTO_SIMPLE, K_COPY>;
+  switch (proto) {
+    case PROTO_SIMPLE: return pick_kind<DT, PROTO_SIMPLE>(kind);
+    case PROTO_LL: return pick_kind<DT, PROTO_LL>(kind);
+    case PROTO_LL128: return pick_kind<DT, PROTO_LL128>(kind);
+    default: return nullptr;
+  }
+}
+
+KernelFn pick_kernel(int dtype, int proto, int kind) {
+  switch (dtype) {
+    case DT_F32: return pick_proto<DT_F32>(proto, kind);
+    case DT_BF16: return pick_proto<DT_BF16>(proto, kind);
+    case DT_I32: return pick_proto<DT_I32>(proto, kind);
+    default: return nullptr;
+  }
+}
+
+// Workgroups that can be resident at once for kernel f (cached per kernel).
+int resident_workgroups(KernelFn f, int device) {
+  static KernelFn seen[64];
+  static int count[64];
+  static int used = 0;
+  static int dev_seen = -1;
+  if (dev_seen != device) { used = 0; dev_seen = device; }
+  for (int i = 0; i < used; ++i)
+    if (seen[i] == f) return count[i];
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)f, WG_THREADS, 0) != hipSuccess)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) cus = 1;
+  if (per_cu < 1) per_cu = 1;
+  const int total = per_cu * cus;
+  if (used < 64) { seen[used] = f; count[used] = total; ++used; }
+  return total;
+}
+
+hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream) {
+  KernelFn f = pick_kernel(a.g.dtype, a.g.proto, a.g.kind);
+  if (!f) return hipErrorInvalidValue;
+  const uint64_t cap = (uint64_t)resident_workgroups(f, device);
+  uint64_t grid = umin(a.g.ntasks, cap);
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(f, dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reset(Ctl* c, hipStream_t stream) {
+  hipLaunchKernelGGL(reset_kernel, dim3(1), dim3(1), 0, stream, c);
+  return hipGetLastError();
+}
+
+}  // namespace ar

@@ -1,0 +1,243 @@
+// plan.hpp -- host-side planning of one call: schedule kind, block / chunk /
+// tile geometry, ticket counts, staging and flag needs, and the byte
+// accounting reported by ar_plan_bytes.  Pure C++ (no HIP calls).
+#pragma once
+
+#include <stdint.h>
+
+#include "schedule.hpp"
+
+namespace ar {
+
+inline uint64_t floor_pow2(uint64_t x) {
+  uint64_t p = 1;
+  while (p * 2 <= x) p *= 2;
+  return p;
+}
+
+inline uint64_t clampu(uint64_t x, uint64_t lo, uint64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+constexpr uint64_t DEFAULT_CHUNK_BYTES = 512 * 1024;
+constexpr uint64_t LL128_TILE_UNIT = 3840;  // 32 lines of 120 payload bytes: one wave pass
+constexpr uint64_t LL128_ALIGN = 240;       // 2 lines: a multiple of 16 bytes and of 120 bytes
+
+inline int esize_of(int dtype) { return dtype == DT_BF16 ? 2 : 4; }
+
+// Tile size in bytes for a per-rank buffer of `rank_bytes`: aim for >= 128
+// tiles per rank so a call spreads over the 256 CUs, within the per-protocol
+// bounds (Simple up to 64 KiB, LL up to 16 KiB, LL128 whole wave passes).
+inline uint64_t pick_tile_bytes(int proto, uint64_t rank_bytes, bool inplace_oneshot) {
+  const uint64_t want = floor_pow2(rank_bytes / 128 + 1);
+  if (proto == PROTO_SIMPLE) return clampu(want, 4096, inplace_oneshot ? 16384 : 65536);
+  if (proto == PROTO_LL) return clampu(want, 4096, 16384);
+  return LL128_TILE_UNIT * clampu(floor_pow2(want / LL128_TILE_UNIT + 1), 1, 4);
+}
+
+// Fill g for one call.  Returns false on an invalid combination.
+inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, uint64_t count,
+                          uint64_t chunk_bytes, int in_place, Geometry* out) {
+  if (nranks < 1 || nranks > MAX_RANKS) return false;
+  if (op < 0 || op > 2 || algo < 0 || algo > 2 || proto < 0 || proto > 2 || dtype < 0 || dtype > 2)
+    return false;
+  Geometry g = {};
+  g.op = op; g.algo = algo; g.proto = proto; g.dtype = dtype;
+  g.nranks = nranks;
+  g.esize = esize_of(dtype);
+  g.in_place = in_place ? 1 : 0;
+  g.count = count;
+  g.lag = 2;
+  const uint64_t n = (uint64_t)nranks, es = (uint64_t)g.esize, vec = 16 / es;
+  g.line_bytes = proto == PROTO_LL ? LL_LINE : (proto == PROTO_LL128 ? LL128_LINE : 0);
+
+  if (op == OP_ALLREDUCE) {
+    g.total = count;
+    g.block = cdiv(cdiv(count, n), vec) * vec;
+  } else {
+    g.total = n * count;
+    g.block = count;
+  }
+
+  if (nranks == 1) {  // a single rank: its result is its own input
+    g.kind = K_COPY;
+    g.proto = PROTO_SIMPLE;
+    g.line_bytes = 0;
+    g.total = count;
+    g.block = count;
+    g.tile = pick_tile_bytes(PROTO_SIMPLE, count * es, false) / es;
+    g.tiles = cdiv(count, g.tile);
+    g.ntasks = (op == OP_ALLREDUCE && in_place) ? 0 : g.tiles;
+    *out = g;
+    return true;
+  }
+
+  if (op == OP_ALLREDUCE) g.kind = algo == ALGO_ONESHOT ? K_ONESHOT : (algo == ALGO_TWOSHOT ? K_TWOSHOT : K_RING);
+  else if (op == OP_REDUCE_SCATTER) g.kind = algo == ALGO_RING ? K_RING : K_RS_DIRECT;
+  else g.kind = algo == ALGO_RING ? K_RING : K_AG_DIRECT;
+
+  const bool lines = proto != PROTO_SIMPLE;
+  const uint64_t rank_bytes = g.total * es;
+  uint64_t tile_b = pick_tile_bytes(proto, rank_bytes, g.kind == K_ONESHOT && in_place && !lines);
+
+  if (g.kind == K_RING) {
+    uint64_t cb = chunk_bytes ? chunk_bytes : DEFAULT_CHUNK_BYTES;
+    if (proto == PROTO_LL128) cb = (cb / LL128_ALIGN) * LL128_ALIGN;
+    else cb = (cb / 16) * 16;
+    if (cb == 0) cb = proto == PROTO_LL128 ? LL128_ALIGN : 16;
+    tile_b = umin(tile_b, cb);
+    g.chunk = cb / es;
+    g.tile = tile_b / es;
+    g.tiles = cdiv(g.chunk, g.tile);  // tiles per chunk loop
+    g.loops = g.block ? cdiv(g.block, g.chunk) : 0;
+    if (op == OP_ALLREDUCE) g.steps = lines ? 2 * nranks - 1 : 2 * (nranks - 1);
+    else if (op == OP_REDUCE_SCATTER) g.steps = lines ? nranks : nranks - 1;
+    else g.steps = nranks;
+    g.ntasks = g.loops * (uint64_t)g.steps * n * g.tiles;
+    g.nflags = lines ? 0 : n * g.loops * g.tiles;
+    g.tile_lines = lines ? lines_for(g, tile_b) : 0;
+    g.slot_lines = g.loops * g.tiles * g.tile_lines;
+    g.nslots = lines ? n * (uint64_t)(g.steps - 1) : 0;
+    *out = g;
+    return true;
+  }
+
+  g.tile = tile_b / es;
+  g.tile_lines = lines ? lines_for(g, tile_b) : 0;
+  const uint64_t extent = (g.kind == K_ONESHOT) ? g.total : g.block;
+  g.tiles = cdiv(extent, g.tile);
+  const uint64_t lag = (uint64_t)g.lag;
+  switch (g.kind) {
+    case K_ONESHOT:
+      if (!lines) {
+        g.ntasks = g.tiles * n;
+        g.nflags = in_place ? g.tiles * n : 0;
+      } else {
+        g.per_group = 2 * n;
+        g.groups = g.tiles ? g.tiles + lag : 0;
+        g.nslots = n;
+      }
+      break;
+    case K_TWOSHOT:
+      if (!lines) {
+        g.per_group = n * n;
+        g.groups = g.tiles ? g.tiles + lag : 0;
+        g.nflags = n * g.tiles;
+      } else {
+        g.per_group = n * (2 * n - 1);
+        g.groups = g.tiles ? g.tiles + 2 * lag : 0;
+        g.nslots = n * n + n;
+      }
+      break;
+    case K_RS_DIRECT:
+      if (!lines) {
+        g.ntasks = g.tiles * n;
+      } else {
+        g.per_group = n * n;
+        g.groups = g.tiles ? g.tiles + lag : 0;
+        g.nslots = n * n;
+      }
+      break;
+    case K_AG_DIRECT:
+      if (!lines) {
+        g.ntasks = g.tiles * n * n;
+      } else {
+        g.per_group = n * n;
+        g.groups = g.tiles ? g.tiles + lag : 0;
+        g.nslots = n;
+      }
+      break;
+    default:
+      return false;
+  }
+  if (g.per_group) g.ntasks = g.groups * g.per_group;
+  g.slot_lines = g.tiles * g.tile_lines;
+  *out = g;
+  return true;
+}
+
+inline uint64_t staging_bytes(const Geometry& g) { return g.nslots * g.slot_lines * g.line_bytes; }
+
+// Byte accounting of one call: walk every task.  `link` has nranks entries.
+struct Bytes {
+  uint64_t rd = 0, wr = 0;
+  uint64_t link[MAX_RANKS] = {};
+};
+
+inline Bytes account(const Geometry& g) {
+  Bytes b;
+  const int n = g.nranks;
+  const uint64_t es = (uint64_t)g.esize;
+  const bool lines = g.proto != PROTO_SIMPLE;
+  for (uint64_t t = 0; t < g.ntasks; ++t) {
+    const Task k = decode(g, t);
+    if (k.phase == PH_NONE) continue;
+    const uint64_t len = (k.hi - k.lo) * es;
+    const uint64_t w = lines_for(g, len) * g.line_bytes;
+    const int r = k.rank;
+    switch (g.kind) {
+      case K_COPY:
+        b.rd += len; b.wr += len;
+        break;
+      case K_ONESHOT:
+        if (!lines) {
+          b.rd += n * len; b.wr += len; b.link[r] += (n - 1) * len;
+        } else if (k.phase == PH_SEND) {
+          b.rd += len; b.wr += w;
+        } else {
+          b.rd += (n - 1) * w + (g.in_place ? w : len); b.wr += len; b.link[r] += (n - 1) * len;
+        }
+        break;
+      case K_TWOSHOT:
+        if (!lines) {
+          if (k.phase == PH_FOLD) { b.rd += n * len; b.wr += len; b.link[r] += (n - 1) * len; }
+          else { b.rd += len; b.wr += len; b.link[r] += len; }
+        } else if (k.phase == PH_SEND) {
+          b.rd += len; b.wr += w;
+        } else if (k.phase == PH_RECV_FOLD) {
+          b.rd += len + (n - 1) * w; b.wr += len + w; b.link[r] += (n - 1) * len;
+        } else {
+          b.rd += w; b.wr += len; b.link[r] += len;
+        }
+        break;
+      case K_RS_DIRECT:
+        if (!lines) { b.rd += n * len; b.wr += len; b.link[r] += (n - 1) * len; }
+        else if (k.phase == PH_SEND) { b.rd += len; b.wr += w; }
+        else { b.rd += len + (n - 1) * w; b.wr += len; b.link[r] += (n - 1) * len; }
+        break;
+      case K_AG_DIRECT:
+        if (!lines) { b.rd += len; b.wr += len; if (r != k.peer) b.link[r] += len; }
+        else if (k.phase == PH_SEND) { b.rd += len; b.wr += w + len; }
+        else { b.rd += w; b.wr += len; b.link[r] += len; }
+        break;
+      case K_RING: {
+        const int s = k.step, last = g.steps - 1;
+        if (!lines) {
+          if (g.op == OP_ALLGATHER) {
+            b.rd += len; b.wr += len;
+            if (s > 0) b.link[r] += len;
+          } else if (g.op == OP_ALLREDUCE && s >= n - 1) {
+            b.rd += len; b.wr += len; b.link[r] += len;
+          } else {
+            b.rd += 2 * len; b.wr += len; b.link[r] += len;
+          }
+        } else if (s == 0) {
+          b.rd += len; b.wr += w;
+          if (g.op == OP_ALLGATHER) b.wr += len;  // rank j's own copy
+        } else {
+          const bool reduce = g.op != OP_ALLGATHER && s <= n - 1;
+          b.rd += w + (reduce ? len : 0);
+          b.link[r] += len;
+          const bool keeps = !reduce || s == n - 1;  // writes its output buffer
+          if (keeps) b.wr += len;
+          if (s < last) b.wr += w;
+          if (g.op == OP_REDUCE_SCATTER && s == last) {}  // last step: output only
+        }
+        break;
+      }
+      default:
+        break;
+    }
+  }
+  return b;
+}
+
+}  // namespace ar

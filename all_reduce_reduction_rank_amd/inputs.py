@@ -59,3 +59,39 @@ def rank_inputs(nranks: int, count: int, dt: str, dist: str, seed: int = 0, cfg:
     if dt not in _STORAGE:
         raise ValueError(f"unknown payload type {dt!r}")
     return [_draw(rank_rng(seed, cfg, nranks, r), count, dt, dist) for r in range(nranks)]
+
+
+def device_rank_inputs(nranks: int, count: int, dt: str, dist: str, seed: int = 0, cfg: int = 0,
+                       device: str = "cuda"):
+    """N device tensors drawn on the GPU with torch's seeded generator (for
+    buffers too large to draw on the host).  Same distributions as
+    `rank_inputs`, a different (torch) stream of random numbers."""
+    import torch
+
+    out = []
+    for r in range(nranks):
+        g = torch.Generator(device=device)
+        g.manual_seed(((seed * 1000003 + cfg) * 1000003 + nranks) * 1000003 + r)
+        if dist == "ones":
+            t = torch.ones(count, dtype=torch.float32, device=device)
+        elif dist == "int20":
+            t = torch.randint(-(2 ** 20), 2 ** 20 + 1, (count,), generator=g, device=device, dtype=torch.int64)
+            if dt == "i32":
+                out.append(t.to(torch.int32))
+                continue
+            t = t.to(torch.float32)
+        elif dist == "uniform":
+            t = torch.rand(count, generator=g, device=device, dtype=torch.float32) * 2 - 1
+        elif dist == "normal":
+            t = torch.randn(count, generator=g, device=device, dtype=torch.float32)
+        elif dist == "normal_1e-3":
+            t = torch.randn(count, generator=g, device=device, dtype=torch.float32) * 1e-3
+        else:
+            raise ValueError(f"unknown distribution {dist!r}")
+        if dt == "f32":
+            out.append(t)
+        elif dt == "bf16":  # top 16 bits of the fp32 draws, as for the host generator
+            out.append((t.view(torch.int32) >> 16).to(torch.int16).view(torch.bfloat16))
+        else:
+            out.append(torch.round(t * 1024).to(torch.int32))
+    return out

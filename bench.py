@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Benchmark of the all-reduce family on one MI355X.
+
+A step is one call of the collective (one kernel: every rank program of the
+call) over N simulated rank buffers already resident in HBM.  The default
+workload is the gradient-bucket all-reduce: N=8 ranks, 256 MiB of fp32
+N(0, 1e-3) per rank, ring, Simple protocol, 512 KiB chunks.
+
+Prints ONE JSON line:
+  value       algbw = S / t in GB/s (S = bytes per rank, t = time per call)
+  busbw       algbw * 2(N-1)/N (all-reduce) or (N-1)/N (reduce-scatter,
+              all-gather), the nccl-tests convention
+  roofline    the call's kernel against MI355X's 8 TB/s HBM peak: achieved =
+              the schedule's algorithmic HBM bytes per call / the kernel's
+              average duration measured with HIP events on its stream
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+
+WORKLOADS = {
+    # gradient buckets (N=8 fp32 N(0, 1e-3), ring, 512 KiB chunks, Simple)
+    "grad-bucket-256MiB": dict(op="allreduce", nranks=8, bytes=256 << 20, dtype="f32", dist="normal_1e-3",
+                               algo="ring", proto="simple", chunk=512 << 10),
+    "grad-bucket-25MiB": dict(op="allreduce", nranks=8, bytes=25 << 20, dtype="f32", dist="normal_1e-3",
+                              algo="ring", proto="simple", chunk=512 << 10),
+    # TP activations: N=8 bf16 [tokens, 5120]
+    "tp-decode-t1": dict(op="allreduce", nranks=8, bytes=1 * 5120 * 2, dtype="bf16", dist="normal",
+                         algo="oneshot", proto="ll", chunk=0),
+    "tp-prefill-t512": dict(op="allreduce", nranks=8, bytes=512 * 5120 * 2, dtype="bf16", dist="normal",
+                            algo="twoshot", proto="ll128", chunk=0),
+    # integer path: N=8 int32, 64 MiB per rank
+    "int32-64MiB-ring": dict(op="allreduce", nranks=8, bytes=64 << 20, dtype="i32", dist="int20",
+                             algo="ring", proto="simple", chunk=512 << 10),
+}
+DEFAULT_WORKLOAD = "grad-bucket-256MiB"
+KERNEL_SOURCES = ("csrc/kernels.hip", "csrc/device.hpp", "csrc/schedule.hpp", "csrc/plan.hpp")
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "all_reduce_reduction_rank_amd", rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def busbw_factor(op, n):
+    return 2 * (n - 1) / n if op == "allreduce" else (n - 1) / n
+
+
+def counts(w):
+    es = {"f32": 4, "bf16": 2, "i32": 4}[w["dtype"]]
+    n = w["nranks"]
+    if w["op"] == "allreduce":
+        return w["bytes"] // es, w["bytes"] // es, w["bytes"] // es   # count, in elems, out elems
+    per = w["bytes"] // es // n
+    if w["op"] == "reduce_scatter":
+        return per, n * per, per
+    return per, per, n * per
+
+
+def traffic_from_profile(name):
+    """Counter-measured HBM bytes per call from a committed rocprofv3 PMC
+    summary of this workload, or None if absent or taken on other kernels."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
+def cpu_baseline(w, min_seconds):
+    """The oracle as it stands, on a bounded sample: the same collective on
+    the same N and distribution, 32 MiB per rank (or the workload's size if
+    smaller), repeated until `min_seconds` have passed."""
+    from all_reduce_reduction_rank_amd import inputs
+    from oracle import collectives
+
+    es = {"f32": 4, "bf16": 2, "i32": 4}[w["dtype"]]
+    sample_bytes = min(w["bytes"], 32 << 20)
+    n = w["nranks"]
+    per = sample_bytes // es
+    if w["op"] != "allreduce":
+        per //= n
+    host = inputs.rank_inputs(n, per if w["op"] != "reduce_scatter" else n * per, w["dtype"], w["dist"],
+                              seed=1, cfg=9)
+    fn = {"allreduce": collectives.allreduce, "reduce_scatter": collectives.reduce_scatter,
+          "allgather": collectives.allgather}[w["op"]]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn(host, w["dtype"], w["algo"], chunk_bytes=w["chunk"] or collectives.DEFAULT_CHUNK_BYTES)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {
+        "value": round(sample_bytes * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{w['op']} {w['algo']} N={n} {w['dtype']} {w['dist']}, {sample_bytes >> 20} MiB per rank, "
+                  f"{reps} calls in {el:.1f} s (NumPy, single thread)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--algo", choices=("oneshot", "twoshot", "ring"))
+    ap.add_argument("--proto", choices=("simple", "ll", "ll128"))
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample length; 0 skips it")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: the N ranks are simulated inside one MI355X "
+              f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from all_reduce_reduction_rank_amd import Comm, inputs, plan_bytes
+
+    w = dict(WORKLOADS[args.workload])
+    if args.algo:
+        w["algo"] = args.algo
+    if args.proto:
+        w["proto"] = args.proto
+    n, dt, op = w["nranks"], w["dtype"], w["op"]
+    torch.cuda.set_device(0)
+    count, n_in, n_out = counts(w)
+    send = inputs.device_rank_inputs(n, n_in, dt, w["dist"], seed=0, cfg=4)
+    recv = [torch.empty(n_out, dtype=send[0].dtype, device="cuda") for _ in range(n)]
+    comm = Comm(n, w["bytes"], w["bytes"] if w["proto"] != "simple" else 0)
+    call = getattr(comm, op)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        call(send, recv, algo=w["algo"], proto=w["proto"], chunk_bytes=w["chunk"], stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {args.workload}: warmup {args.warmup} done", file=sys.stderr, flush=True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    status = comm.check()
+    if status[0] != "AR_OK":
+        raise SystemExit(f"device error during the timed region: {status}")
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms:.4f} ms per call (wall {wall:.3f} s)", file=sys.stderr, flush=True)
+
+    s = w["bytes"]
+    t = ms / 1e3
+    plan = plan_bytes(n, op, count, dt, w["algo"], w["proto"], chunk_bytes=w["chunk"])
+    algbw = s / t / 1e9
+    achieved = plan["hbm"] / t / 1e9
+    traffic = traffic_from_profile(args.workload)
+    out = {
+        "metric": "all-reduce algbw/busbw GB/s and % of HBM peak vs message size, N=8",
+        "value": round(algbw, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded, generated on the GPU)",
+        "config": {
+            "workload": args.workload, "op": op, "nranks": n, "bytes_per_rank": s, "dtype": dt,
+            "dist": w["dist"], "algo": w["algo"], "proto": w["proto"], "chunk_bytes": w["chunk"],
+            "parallelism": f"{n} simulated ranks on 1 GPU",
+        },
+        "algbw_GBps": round(algbw, 3),
+        "busbw_GBps": round(algbw * busbw_factor(op, n), 3),
+        "hbm_bytes_per_call": plan["hbm"],
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+        "kernel_hash": kernel_hash(),
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    comm.close()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

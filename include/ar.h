@@ -1,0 +1,181 @@
+/*
+ * ar.h -- C ABI of the MI355X all-reduce family library (libar.so).
+ *
+ * One GPU holds N simulated rank buffers in its HBM.  Each call runs every
+ * rank's program of one collective in a single HIP kernel on the caller's
+ * stream; rank programs exchange data only through device memory, guarded by
+ * flags (Simple) or by flag-carrying lines (LL, LL128).
+ *
+ * The operations, algorithms and protocols follow these pages:
+ *   [Q]  "NCCL collectives, ring all-reduce & launching TP/PP", section
+ *        "Direct answer" -- all-reduce sums a tensor every rank holds and every
+ *        rank ends with the result; all-gather concatenates the shards;
+ *        reduce-scatter sums and each rank keeps its slice; ring all-reduce is
+ *        a reduce-scatter followed by an all-gather.
+ *   [H]  "Collective communication: NCCL's algorithms and protocols, and
+ *        custom all-reduce" -- section "Algorithms" (ring, one-shot,
+ *        two-shot), section "Protocols" (LL: 8-byte lines with a 4-byte flag;
+ *        LL128: 128-byte lines with an 8-byte flag; Simple: block, fence,
+ *        flag), exercise 3 (a pre-registered buffer allocated once caps the
+ *        largest message and keeps addresses fixed for graph capture).
+ *   [P]  llama.cpp pull request "Add nccl support for tensor parrallel",
+ *        overview -- a communicator is created once per group of ranks and
+ *        per-tensor collective calls are then made on it.
+ *
+ * Conventions shared by every entry point:
+ *   - Buffers: `sendbufs` / `recvbufs` are HOST arrays of N DEVICE pointers
+ *     (N = the communicator's rank count), all on the communicator's device,
+ *     each 16-byte aligned.  The arrays are read during the call only; the
+ *     caller owns every rank buffer, which must stay alive until the stream
+ *     reaches the call.  Element type and count are given per call.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *     asynchronous and ordered on that stream; a communicator must be used on
+ *     one stream at a time (flags are tagged with a device-resident call
+ *     counter, so calls and HIP-graph replays never need a reset).
+ *   - A call with count 0 does nothing and returns AR_OK (pointers unused).
+ *   - Errors: argument errors return at once and launch nothing.  A device
+ *     wait that exceeds the communicator's time limit stops the call, latches
+ *     AR_ERR_TIMEOUT in device memory and makes later calls no-ops until
+ *     ar_comm_reset; ar_comm_check reports it.  Nothing is printed.
+ */
+#ifndef AR_H
+#define AR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AR_OK = 0,
+  AR_ERR_INVALID = 1,     /* bad argument: N, pointer, alignment, enum, aliasing */
+  AR_ERR_UNSUPPORTED = 2, /* combination not provided */
+  AR_ERR_NOMEM = 3,       /* workspace allocation failed */
+  AR_ERR_TOO_LARGE = 4,   /* message exceeds the communicator's capacity */
+  AR_ERR_HIP = 5,         /* a HIP runtime call failed */
+  AR_ERR_TIMEOUT = 6,     /* a rank program waited past the time limit */
+  AR_ERR_BROKEN = 7       /* communicator holds a latched device error */
+} ar_status;
+
+/* Payload types; the reduction is always SUM ([Q] "Direct answer").
+ * AR_F32: IEEE binary32 adds, round to nearest even, no flush to zero.
+ * AR_BF16: bf16 storage, each add done in fp32, rounded to bf16 (nearest
+ *          even) where the value is stored or put on the wire.
+ * AR_I32: two's-complement adds that wrap. */
+typedef enum { AR_F32 = 0, AR_BF16 = 1, AR_I32 = 2 } ar_dtype;
+
+/* [H] "Algorithms".  For reduce-scatter and all-gather, ONESHOT and TWOSHOT
+ * both name the direct schedule (one exchange: every rank reads its slices
+ * straight from every rank). */
+typedef enum { AR_ONESHOT = 0, AR_TWOSHOT = 1, AR_RING = 2 } ar_algo;
+
+/* [H] "Protocols". */
+typedef enum { AR_SIMPLE = 0, AR_LL = 1, AR_LL128 = 2 } ar_proto;
+
+typedef enum { AR_OP_ALLREDUCE = 0, AR_OP_REDUCE_SCATTER = 1, AR_OP_ALLGATHER = 2 } ar_op;
+
+typedef struct ar_comm* ar_comm_t;
+typedef void* ar_stream_t; /* a hipStream_t */
+
+/* Create a communicator of `nranks` (1..8) simulated ranks on the current HIP
+ * device ([P] overview; [H] exercise 3).  It allocates, once, the workspace
+ * every later call uses: flags, a device call counter, an error record,
+ * staging for ring reduce-scatter partials sized for buffers of up to
+ * `max_bytes_per_rank`, and LL / LL128 line staging sized for payloads of up
+ * to `max_line_bytes_per_rank` per rank (0: LL / LL128 calls are refused).
+ * The per-rank cap applies to the largest buffer of a call: count*esize for
+ * all-reduce, nranks*recvcount*esize (input) for reduce-scatter,
+ * nranks*sendcount*esize (output) for all-gather.
+ * On success *out owns the workspace; release it with ar_comm_destroy.
+ * Errors: AR_ERR_INVALID (nranks out of range, out == NULL), AR_ERR_NOMEM,
+ * AR_ERR_HIP. */
+ar_status ar_comm_create(int nranks, size_t max_bytes_per_rank,
+                         size_t max_line_bytes_per_rank, ar_comm_t* out);
+
+/* Free the workspace.  The caller must have synchronized every stream that
+ * used the communicator.  Errors: AR_ERR_INVALID (NULL), AR_ERR_HIP. */
+ar_status ar_comm_destroy(ar_comm_t comm);
+
+/* Synchronize `stream` and report any latched device error.  On
+ * AR_ERR_TIMEOUT, *err_rank / *err_step (either may be NULL) receive the
+ * rank program and step of the earliest blocked wait.  Steps: ring -- step s
+ * of a block's chain (reduce steps first, run by the receiving rank); two-shot
+ * -- 0 = a rank sums its own block, 1 = it gathers the others; one-shot in
+ * place -- 0 = a rank has read every input tile, 1 = it writes its output.
+ * Returns AR_OK when no error is latched. */
+ar_status ar_comm_check(ar_comm_t comm, ar_stream_t stream, int* err_rank, int* err_step);
+
+/* Clear a latched device error so the communicator can be used again
+ * (stream-ordered; no buffers are touched: flags are tagged per call). */
+ar_status ar_comm_reset(ar_comm_t comm, ar_stream_t stream);
+
+/* Device workspace bytes owned by the communicator. */
+size_t ar_comm_workspace_bytes(ar_comm_t comm);
+
+/* All-reduce (SUM) of `count` elements per rank ([Q] "Direct answer";
+ * [H] "Algorithms").  recvbufs[r] receives the sum of sendbufs[0..N-1].
+ *   ONESHOT: rank r reads all N inputs and sums them in rank order 0..N-1.
+ *   TWOSHOT: rank j sums block j of every rank (same order), then every rank
+ *            reads the N block sums back.
+ *   RING:    N-1 reduce steps then N-1 copy steps; block j's sum starts at
+ *            rank j+1 and ends at rank j; bf16 partials are rounded per hop.
+ * Blocks: B = ceil(count/N) rounded up to a 16-byte vector; block j holds
+ * elements [jB, min((j+1)B, count)).  The ring walks each block in chunks of
+ * `chunk_bytes` (0 = 512 KiB; LL128 rounds it down to a multiple of 240
+ * bytes), which never changes the result.
+ * In place (sendbufs[r] == recvbufs[r] for every r) is allowed; otherwise
+ * send and receive buffers must not overlap.
+ * Errors: AR_ERR_INVALID, AR_ERR_TOO_LARGE, AR_ERR_BROKEN (latched device
+ * error), AR_ERR_HIP (launch failure). */
+ar_status ar_allreduce(ar_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                       size_t count, ar_dtype dtype, ar_algo algo, ar_proto proto,
+                       size_t chunk_bytes, ar_stream_t stream);
+
+/* Reduce-scatter (SUM): sendbufs[i] holds N*recvcount elements; recvbufs[r]
+ * (recvcount elements) receives sum_i sendbufs[i][r*recvcount ...]
+ * ([Q] "Direct answer").  ONESHOT/TWOSHOT: direct, rank r sums in rank order;
+ * RING: the reduce half of the ring (slice j's sum starts at rank j+1, ends
+ * at rank j).  Out of place only (AR_ERR_INVALID otherwise). */
+ar_status ar_reduce_scatter(ar_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                            size_t recvcount, ar_dtype dtype, ar_algo algo, ar_proto proto,
+                            size_t chunk_bytes, ar_stream_t stream);
+
+/* All-gather: sendbufs[j] holds `sendcount` elements; every recvbufs[r]
+ * (N*sendcount elements) receives sendbufs[0] | ... | sendbufs[N-1]
+ * ([Q] "Direct answer").  ONESHOT/TWOSHOT: direct; RING: the copy half of
+ * the ring.  Out of place only. */
+ar_status ar_allgather(ar_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
+                       size_t sendcount, ar_dtype dtype, ar_algo algo, ar_proto proto,
+                       size_t chunk_bytes, ar_stream_t stream);
+
+/* Host-only accounting of one call's schedule (no device work; works
+ * without a GPU).  `count` has the same meaning as in the call for `op`.
+ * Fills (any pointer may be NULL):
+ *   hbm_read / hbm_write -- device-memory bytes all N rank programs load /
+ *       store (payload and lines; flags excluded), summed over tasks;
+ *   link_bytes -- array of nranks: payload bytes each rank receives from its
+ *       peers ([H] "Algorithms": ring 2(N-1)/N S, one-shot (N-1) S, two-shot
+ *       2(N-1)/N S);
+ *   ntasks -- tasks in the call's kernel.
+ * Errors: AR_ERR_INVALID. */
+ar_status ar_plan_bytes(int nranks, ar_op op, size_t count, ar_dtype dtype, ar_algo algo,
+                        ar_proto proto, size_t chunk_bytes, int in_place,
+                        uint64_t* hbm_read, uint64_t* hbm_write, uint64_t* link_bytes,
+                        uint64_t* ntasks);
+
+/* Test hook: from the next call on, the rank program `rank` does not signal
+ * after step `step` (Simple protocol schedules), and waits give up after
+ * `timeout_us` microseconds (0 keeps the default of 5 s).  rank = -1 clears
+ * the injection.  Used to exercise the timeout path from the host. */
+ar_status ar_debug_inject(ar_comm_t comm, int rank, int step, uint64_t timeout_us);
+
+/* Static description of a status code. */
+const char* ar_status_string(ar_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AR_H */

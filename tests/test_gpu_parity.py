@@ -1,0 +1,298 @@
+"""GPU parity: every collective x algorithm x protocol x payload type, through
+the C ABI (libar.so via the ctypes binding), compared element by element
+with the CPU oracle on the same seeded inputs.  Integer and same-order
+floating point results must be bit-exact."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from all_reduce_reduction_rank_amd import ARError, Comm, inputs
+from oracle import collectives as C
+from tests.gpu_util import assert_same, empty, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+ALGOS = ("oneshot", "twoshot", "ring")
+PROTOS = ("simple", "ll", "ll128")
+DTYPES = ("f32", "bf16", "i32")
+MAX_BYTES = 64 << 20
+LINE_BYTES = 16 << 20
+
+_COMMS = {}
+
+
+def comm(n):
+    if n not in _COMMS:
+        _COMMS[n] = Comm(n, MAX_BYTES, LINE_BYTES)
+    return _COMMS[n]
+
+
+def _dist(dt):
+    return "int20" if dt == "i32" else "normal"
+
+
+def _say(*what):
+    print("CASE", *what, flush=True, file=sys.stderr)
+
+
+def run_allreduce(n, count, dt, algo, proto, chunk=0, seed=0, in_place=False, dist=None):
+    host = inputs.rank_inputs(n, count, dt, dist or _dist(dt), seed=seed, cfg=100 + n)
+    send = [to_dev(x, dt) for x in host]
+    recv = send if in_place else [empty(count, dt) for _ in range(n)]
+    _say("allreduce", n, count, dt, algo, proto, chunk, "inplace" if in_place else "")
+    comm(n).allreduce(send, recv, algo=algo, proto=proto, chunk_bytes=chunk)
+    torch.cuda.synchronize()
+    got = [to_host(t, dt) for t in recv]
+    want = C.allreduce(host, dt, algo, chunk_bytes=chunk or C.DEFAULT_CHUNK_BYTES)
+    for r in range(n):
+        assert_same(got[r], want[r], f"allreduce {algo}/{proto} {dt} N={n} count={count} rank {r}")
+    st = comm(n).check()
+    assert st[0] == "AR_OK", st
+
+
+# ---------------------------------------------------------------- all-reduce
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("proto", PROTOS)
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("n", [2, 3, 8])
+def test_allreduce_matrix(n, algo, proto, dt):
+    # 1 element (blocks mostly empty), a ragged tail, several tiles per block.
+    for count in (1, 7, 1000, 70001):
+        run_allreduce(n, count, dt, algo, proto, seed=count)
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+@pytest.mark.parametrize("dt", DTYPES)
+def test_ring_many_chunks(proto, dt):
+    # Small chunks: many chunk loops per block, short last tiles.
+    for chunk in (16, 240, 4096, 100000):
+        run_allreduce(4, 5003, dt, "ring", proto, chunk=chunk, seed=chunk)
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+@pytest.mark.parametrize("algo", ALGOS)
+def test_allreduce_in_place(algo, proto):
+    for dt in DTYPES:
+        for n, count in ((2, 4096), (8, 33333)):
+            run_allreduce(n, count, dt, algo, proto, seed=7, in_place=True)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_all_ones_sum_to_n(algo):
+    # "NCCL collectives..." sanity test: an all-reduce of ones gives N.
+    for n in (2, 5, 8):
+        for proto in PROTOS:
+            for dt in DTYPES:
+                run_allreduce(n, 128, dt, algo, proto, dist="ones")
+
+
+def test_config_small_n2_4096_f32():
+    # N=2, 4096 fp32 uniform[-1,1]: every algorithm and protocol, plus ones.
+    for algo in ALGOS:
+        for proto in PROTOS:
+            run_allreduce(2, 4096, "f32", algo, proto, dist="uniform")
+            run_allreduce(2, 4096, "f32", algo, proto, dist="ones")
+
+
+def test_eight_bytes_per_rank():
+    # 8 B per rank at N=8: most blocks empty, every LL128 line partial.
+    for algo in ALGOS:
+        for proto in PROTOS:
+            run_allreduce(8, 2, "f32", algo, proto)
+            run_allreduce(8, 4, "bf16", algo, proto)
+
+
+def test_empty_and_single_rank():
+    for algo in ALGOS:
+        for proto in PROTOS:
+            run_allreduce(3, 0, "f32", algo, proto)
+            run_allreduce(1, 1000, "bf16", algo, proto)
+            run_allreduce(1, 1000, "i32", algo, proto, in_place=True)
+
+
+# ------------------------------------------------------------ reduce-scatter
+def run_rs(n, rc, dt, algo, proto, chunk=0, seed=0):
+    host = inputs.rank_inputs(n, n * rc, dt, _dist(dt), seed=seed, cfg=200 + n)
+    send = [to_dev(x, dt) for x in host]
+    recv = [empty(rc, dt) for _ in range(n)]
+    _say("reduce_scatter", n, rc, dt, algo, proto, chunk)
+    comm(n).reduce_scatter(send, recv, algo=algo, proto=proto, chunk_bytes=chunk)
+    torch.cuda.synchronize()
+    want = C.reduce_scatter(host, dt, algo, chunk_bytes=chunk or C.DEFAULT_CHUNK_BYTES)
+    for r in range(n):
+        assert_same(to_host(recv[r], dt), want[r], f"reduce_scatter {algo}/{proto} {dt} N={n} rc={rc} rank {r}")
+    assert comm(n).check()[0] == "AR_OK"
+
+
+def run_ag(n, sc, dt, algo, proto, chunk=0, seed=0):
+    host = inputs.rank_inputs(n, sc, dt, _dist(dt), seed=seed, cfg=300 + n)
+    send = [to_dev(x, dt) for x in host]
+    recv = [empty(n * sc, dt) for _ in range(n)]
+    _say("allgather", n, sc, dt, algo, proto, chunk)
+    comm(n).allgather(send, recv, algo=algo, proto=proto, chunk_bytes=chunk)
+    torch.cuda.synchronize()
+    want = C.allgather(host, dt, algo, chunk_bytes=chunk or C.DEFAULT_CHUNK_BYTES)
+    for r in range(n):
+        assert_same(to_host(recv[r], dt), want[r], f"allgather {algo}/{proto} {dt} N={n} sc={sc} rank {r}")
+    assert comm(n).check()[0] == "AR_OK"
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("proto", PROTOS)
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("n", [2, 3, 8])
+def test_reduce_scatter_matrix(n, algo, proto, dt):
+    # odd counts leave every slice after the first misaligned (bf16: 2-byte)
+    for rc in (1, 7, 1000, 17001):
+        run_rs(n, rc, dt, algo, proto, seed=rc)
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("proto", PROTOS)
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("n", [2, 3, 8])
+def test_allgather_matrix(n, algo, proto, dt):
+    for sc in (1, 7, 1000, 17001):
+        run_ag(n, sc, dt, algo, proto, seed=sc)
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+def test_rs_ag_ring_chunks(proto):
+    for chunk in (16, 240, 4096):
+        run_rs(4, 3001, "f32", "ring", proto, chunk=chunk)
+        run_ag(4, 3001, "bf16", "ring", proto, chunk=chunk)
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+def test_reduce_scatter_then_allgather_equals_allreduce(proto):
+    n, rc = 8, 4096
+    for dt in DTYPES:
+        host = inputs.rank_inputs(n, n * rc, dt, _dist(dt), seed=3)
+        send = [to_dev(x, dt) for x in host]
+        for algo in ("twoshot", "ring"):
+            shard = [empty(rc, dt) for _ in range(n)]
+            full = [empty(n * rc, dt) for _ in range(n)]
+            ar = [empty(n * rc, dt) for _ in range(n)]
+            comm(n).reduce_scatter(send, shard, algo=algo, proto=proto)
+            comm(n).allgather(shard, full, algo=algo, proto=proto)
+            comm(n).allreduce(send, ar, algo=algo, proto=proto)
+            torch.cuda.synchronize()
+            for r in range(n):
+                assert_same(to_host(full[r], dt), to_host(ar[r], dt), f"RS+AG vs AR {algo}/{proto} {dt}")
+
+
+# ------------------------------------------------------ repeated calls, graphs
+@pytest.mark.parametrize("proto", PROTOS)
+@pytest.mark.parametrize("algo", ALGOS)
+def test_back_to_back_calls_never_see_stale_flags(algo, proto):
+    # The same buffers and staging, new data every call, no reset in between.
+    n, count, dt = 8, 50000, "f32"
+    send = [empty(count, dt) for _ in range(n)]
+    recv = [empty(count, dt) for _ in range(n)]
+    for it in range(6):
+        host = inputs.rank_inputs(n, count, dt, "normal", seed=1000 + it)
+        for t, x in zip(send, host):
+            t.copy_(to_dev(x, dt))
+        comm(n).allreduce(send, recv, algo=algo, proto=proto, chunk_bytes=64 << 10)
+        torch.cuda.synchronize()
+        want = C.allreduce(host, dt, algo, chunk_bytes=64 << 10)
+        for r in range(n):
+            assert_same(to_host(recv[r], dt), want[r], f"call {it} {algo}/{proto} rank {r}")
+
+
+@pytest.mark.parametrize("proto", PROTOS)
+@pytest.mark.parametrize("algo", ALGOS)
+def test_hip_graph_replays(algo, proto):
+    # Captured once; every replay must advance the device call counter, so a
+    # replay never accepts the previous replay's flags.
+    n, count, dt = 4, 20000, "bf16"
+    send = [empty(count, dt) for _ in range(n)]
+    recv = [empty(count, dt) for _ in range(n)]
+    c = comm(n)
+    stream = torch.cuda.Stream()
+    c.allreduce(send, recv, algo=algo, proto=proto)  # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        c.allreduce(send, recv, algo=algo, proto=proto)
+    torch.cuda.synchronize()
+    for it in range(4):
+        host = inputs.rank_inputs(n, count, dt, "normal", seed=2000 + it)
+        for t, x in zip(send, host):
+            t.copy_(to_dev(x, dt))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = C.allreduce(host, dt, algo)
+        for r in range(n):
+            assert_same(to_host(recv[r], dt), want[r], f"replay {it} {algo}/{proto} rank {r}")
+        # eager work on the same communicator between replays
+        c.allreduce(send, [empty(count, dt) for _ in range(n)], algo="ring", proto=proto)
+        torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------- error paths
+def test_argument_errors_are_reported():
+    n = 4
+    c = comm(n)
+    good = [empty(64, "f32") for _ in range(n)]
+    out = [empty(64, "f32") for _ in range(n)]
+    with pytest.raises(ValueError):
+        c.allreduce(good[:3], out[:3])
+    with pytest.raises(ARError) as e:  # misaligned pointer
+        c.allreduce([t[1:] for t in good], [t[1:] for t in out])
+    assert e.value.status == 1
+    with pytest.raises(ARError) as e:  # partial in place
+        c.allreduce(good, [good[0]] + out[1:])
+    assert e.value.status == 1
+    with pytest.raises(ARError) as e:  # in-place reduce-scatter
+        c.reduce_scatter(good, [t[:16] for t in good])
+    assert e.value.status == 1
+    with pytest.raises(ARError) as e:  # outputs overlap
+        c.allreduce(good, [out[0]] * n)
+    assert e.value.status == 1
+    small = Comm(n, 1024, 0)
+    with pytest.raises(ARError) as e:
+        small.allreduce(good, out, proto="ll")  # no line staging provisioned
+    assert e.value.status == 4
+    big = [empty(1024, "f32") for _ in range(n)]
+    with pytest.raises(ARError) as e:
+        small.allreduce(big, [empty(1024, "f32") for _ in range(n)])
+    assert e.value.status == 4
+    small.close()
+    assert c.check()[0] == "AR_OK"
+
+
+@pytest.mark.parametrize("algo,n,rank,step", [("ring", 4, 1, 2), ("ring", 8, 5, 9), ("twoshot", 4, 2, 0)])
+def test_withheld_signal_times_out_and_names_the_blocked_rank(algo, n, rank, step):
+    # Forced from the host: one rank program skips one signal and waits are
+    # limited to 50 ms, so every wave of the kernel still exits.
+    from oracle import sim
+
+    c = Comm(n, 1 << 20, 0)
+    count = 64 * n  # one tile per block: nothing else is still running at the timeout
+    host = inputs.rank_inputs(n, count, "f32", "normal", seed=4)
+    send = [to_dev(x, "f32") for x in host]
+    recv = [empty(count, "f32") for _ in range(n)]
+    c.inject(rank, step, timeout_us=50_000)
+    _say("inject", algo, n, rank, step)
+    c.allreduce(send, recv, algo=algo)
+    status, r, s = c.check()
+    assert status == "AR_ERR_TIMEOUT"
+    _, first = sim.blocked("allreduce", algo, n, withheld=(rank, step))
+    assert (r, s) == first
+    with pytest.raises(ARError) as e:
+        c.allreduce(send, recv, algo=algo)
+    assert e.value.status == 7
+    c.inject(-1, -1)
+    c.reset()
+    run_ok = [empty(count, "f32") for _ in range(n)]
+    c.allreduce(send, run_ok, algo=algo)
+    torch.cuda.synchronize()
+    want = C.allreduce(host, "f32", algo)
+    assert_same(to_host(run_ok[0], "f32"), want[0], "after reset")
+    assert c.check()[0] == "AR_OK"
+    c.close()
