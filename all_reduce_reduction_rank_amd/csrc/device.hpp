@@ -147,14 +147,19 @@ __device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMI
 
 // ---------------------------------------------------------- control block
 // Lives at the start of the communicator's workspace (zeroed at creation).
+// Each hot word on its own 128-byte line: the ticket counter is hammered by
+// every workgroup, the abort word is polled, the epoch is read at start.
 struct Ctl {
   uint32_t ticket;    // next task ticket of the running call
+  uint32_t pad0[31];
   uint32_t done;      // workgroups of the running call that have finished
+  uint32_t pad1[31];
   uint64_t epoch;     // calls completed on this communicator
+  uint64_t pad2[15];
   uint32_t abort;     // a wait timed out: every rank program gives up
   uint32_t err_code;  // 0 or the ar_status of the latched error
   uint32_t err_key;   // min over blocked waits of (step << 8 | rank), ~0 if none
-  uint32_t pad;
+  uint32_t pad3[29];
 };
 
 struct KArgs {
@@ -168,6 +173,7 @@ struct KArgs {
   uint64_t stage_stride;
   uint64_t timeout;     // wall-clock ticks (100 MHz) a wait may last
   int32_t inj_rank, inj_step;
+  uint32_t batch;       // tickets a workgroup takes per fetch
 };
 
 __device__ __forceinline__ void note_blocked(Ctl* c, int step, int rank) {
@@ -182,16 +188,22 @@ __device__ __forceinline__ void raise_timeout(Ctl* c, int step, int rank) {
 }
 
 // Bounded spin of ONE thread until *f >= target.  Returns false if the call
-// is aborted (by this wait timing out or by another one).
+// is aborted (by this wait timing out or by another one).  Back-off doubles
+// the sleep up to ~1 us, and the shared abort word is read only every 8th
+// poll, so thousands of waiting workgroups do not flood one memory channel.
 __device__ __forceinline__ bool wait_ge(const uint64_t* f, uint64_t target, const KArgs& a, int step,
                                         int rank) {
   if (ld_flag(f) >= target) return true;
   const uint64_t t0 = wall_clock64();
+  uint32_t polls = 0;
   while (true) {
-    __builtin_amdgcn_s_sleep(1);
+    const uint32_t level = polls < 6 ? polls : 6;
+    for (uint32_t i = 0; i < (1u << level); ++i) __builtin_amdgcn_s_sleep(8);
     if (ld_flag(f) >= target) return true;
-    if (ld_u32(&a.ctl->abort)) { note_blocked(a.ctl, step, rank); return false; }
-    if (wall_clock64() - t0 > a.timeout) { raise_timeout(a.ctl, step, rank); return false; }
+    if ((++polls & 7) == 0) {
+      if (ld_u32(&a.ctl->abort)) { note_blocked(a.ctl, step, rank); return false; }
+      if (wall_clock64() - t0 > a.timeout) { raise_timeout(a.ctl, step, rank); return false; }
+    }
   }
 }
 

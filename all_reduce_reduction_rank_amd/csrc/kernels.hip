@@ -17,6 +17,14 @@
 
 namespace ar {
 
+// Values every thread of a workgroup holds equal (read back from LDS), made
+// visibly uniform to the compiler.
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+  return ((uint64_t)uniform((uint32_t)(x >> 32)) << 32) | uniform((uint32_t)x);
+}
+
 constexpr int U_SIMPLE = 4;  // 16-byte vectors in flight per thread per source
 constexpr int U_LL = 4;      // LL words per thread per pass
 constexpr int U_LL128 = 4;   // LL128 line groups (8 lines of a wave) per pass
@@ -80,23 +88,30 @@ __device__ __forceinline__ void simple_stream(Term term, int nterms, char* dst, 
   }
 }
 
-// Workgroup waits until *f >= target (thread 0 polls); false if aborted.
+// Workgroup waits until *f >= target (thread 0 polls with back-off); false
+// if the call is aborted.  Thread 0's verdict is broadcast, so all waves take
+// the same path through the barriers that follow.
 __device__ __forceinline__ bool wg_wait(const KArgs& a, const uint64_t* f, uint64_t target, int step,
                                         int rank) {
   __shared__ int s_ok;
   if (threadIdx.x == 0) s_ok = wait_ge(f, target, a, step, rank) ? 1 : 0;
   __syncthreads();
-  const bool ok = s_ok != 0;
+  // readfirstlane: the outcome is the same for the whole workgroup, and the
+  // compiler must know it, or it may split the surrounding loop by lane.
+  const bool ok = uniform(s_ok) != 0;
   fence_acquire();
   __syncthreads();  // s_ok may be rewritten by the next wait
   return ok;
 }
 
-// Workgroup publishes everything it stored, then sets *f = v.
+// Workgroup publishes everything it stored, then sets *f = v.  Every thread
+// stores the same value to the same word (one write per wave): a store left
+// to thread 0 alone at the end of a task lets the compiler defer it past the
+// next loop iteration's barrier, stranding the other lanes on a stale ticket.
 __device__ __forceinline__ void wg_signal(const KArgs& a, uint64_t* f, uint64_t v, int step, int rank) {
   fence_release();
   __syncthreads();
-  if (threadIdx.x == 0 && !(rank == a.inj_rank && step == a.inj_step)) st_flag(f, v);
+  if (!(rank == a.inj_rank && step == a.inj_step)) st_flag(f, v);
 }
 
 // ============================================================ LL / LL128 path
@@ -549,20 +564,33 @@ __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
   __shared__ uint32_t s_ticket;
   if (threadIdx.x == 0) s_epoch = __hip_atomic_load(&a.ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t ntasks = (uint32_t)a.g.ntasks;
-  while (true) {
+  const uint32_t batch = a.batch;
+  bool more = true;
+  while (more) {
     if (threadIdx.x == 0) {
       uint32_t t = 0xffffffffu;
       if (!ld_u32(&a.ctl->abort))
-        t = __hip_atomic_fetch_add(&a.ctl->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        t = __hip_atomic_fetch_add(&a.ctl->ticket, batch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_ticket = t;
     }
     __syncthreads();
-    const uint32_t t = s_ticket;
-    const uint64_t epoch = s_epoch;
+    // Broadcast through readfirstlane so every branch below is a scalar
+    // (workgroup-uniform) branch: barriers inside tasks then always sit in
+    // uniform control flow.
+    const uint32_t first = uniform(s_ticket);
+    const uint64_t epoch = uniform64(s_epoch);
     __syncthreads();
-    if (t >= ntasks) break;
-    const Task k = decode(a.g, t);
-    if (k.phase != PH_NONE) run_task<DT, PROTO, KIND>(a, k, epoch);
+    // A batch of consecutive tickets, run in order: the smallest unfinished
+    // ticket always belongs to a running workgroup that has finished its
+    // earlier tickets, so batching keeps the schedule deadlock-free.
+    for (uint32_t i = 0; i < batch; ++i) {
+      if (first >= ntasks || ntasks - first <= i) { more = false; break; }
+      const Task k = decode(a.g, first + i);
+      if (k.phase != PH_NONE) run_task<DT, PROTO, KIND>(a, k, epoch);
+      // Reconverge every lane before the next task or ticket fetch, so
+      // thread 0's fetch never shares a divergent path with a task's tail.
+      __syncthreads();
+    }
   }
   if (threadIdx.x == 0) {
     const uint32_t d = __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
@@ -639,9 +667,15 @@ hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream) {
   KernelFn f = pick_kernel(a.g.dtype, a.g.proto, a.g.kind);
   if (!f) return hipErrorInvalidValue;
   const uint64_t cap = (uint64_t)resident_workgroups(f, device);
-  uint64_t grid = umin(a.g.ntasks, cap);
+  KArgs b = a;
+  // Tickets per fetch: up to 4 when there are many tasks per workgroup.  The
+  // one-shot in-place barrier waits on LATER tickets of its group, so it
+  // must take them one at a time.
+  const bool barrier = a.g.kind == K_ONESHOT && a.g.proto == PROTO_SIMPLE && a.g.in_place;
+  b.batch = barrier ? 1u : (uint32_t)umax(1, umin(4, a.g.ntasks / (8 * cap)));
+  uint64_t grid = umin(cdiv(a.g.ntasks, b.batch), cap);
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(f, dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, a);
+  hipLaunchKernelGGL(f, dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, b);
   return hipGetLastError();
 }
 

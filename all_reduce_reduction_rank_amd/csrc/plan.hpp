@@ -18,6 +18,9 @@ inline uint64_t floor_pow2(uint64_t x) {
 inline uint64_t clampu(uint64_t x, uint64_t lo, uint64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 constexpr uint64_t DEFAULT_CHUNK_BYTES = 512 * 1024;
+// Workgroups an MI355X keeps resident for these kernels (256 CUs x up to 8):
+// the tickets between a task and its predecessor should exceed it.
+constexpr uint64_t RESIDENT_HINT = 2048;
 constexpr uint64_t LL128_TILE_UNIT = 3840;  // 32 lines of 120 payload bytes: one wave pass
 constexpr uint64_t LL128_ALIGN = 240;       // 2 lines: a multiple of 16 bytes and of 120 bytes
 
@@ -88,6 +91,8 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
     g.tile = tile_b / es;
     g.tiles = cdiv(g.chunk, g.tile);  // tiles per chunk loop
     g.loops = g.block ? cdiv(g.block, g.chunk) : 0;
+    // window: one step of a window spans ~2x the resident workgroups
+    g.window = umax(1, umin(g.loops, cdiv(2 * RESIDENT_HINT, n * g.tiles)));
     if (op == OP_ALLREDUCE) g.steps = lines ? 2 * nranks - 1 : 2 * (nranks - 1);
     else if (op == OP_REDUCE_SCATTER) g.steps = lines ? nranks : nranks - 1;
     else g.steps = nranks;
@@ -104,6 +109,10 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
   g.tile_lines = lines ? lines_for(g, tile_b) : 0;
   const uint64_t extent = (g.kind == K_ONESHOT) ? g.total : g.block;
   g.tiles = cdiv(extent, g.tile);
+  // Receivers of tile g run `lag` groups after its senders: about one
+  // resident grid of tasks in between, never more than the tiles there are.
+  const uint64_t per_group_hint = g.kind == K_TWOSHOT ? n * n : (g.kind == K_ONESHOT ? 2 * n : n * n);
+  g.lag = (int32_t)umax(1, umin(g.tiles, cdiv(RESIDENT_HINT, per_group_hint)));
   const uint64_t lag = (uint64_t)g.lag;
   switch (g.kind) {
     case K_ONESHOT:

@@ -22,7 +22,8 @@
 //   K_RS_DIRECT rank r sums slice r of every rank (reduce-scatter).
 //   K_AG_DIRECT rank r copies shard j of every rank (all-gather).
 //   K_RING      chain per (block, chunk loop, tile): N-1 reduce steps and/or
-//               N-1 copy steps, each run by the receiving rank.
+//               N-1 copy steps, each run by the receiving rank; tickets go
+//               window by window, step by step inside a window.
 //   K_COPY      a single rank: output = input.
 //
 // With LL / LL128 a transfer is lines written by the sender into staging
@@ -76,6 +77,7 @@ struct Geometry {
   uint64_t chunk;       // ring: elements per chunk loop
   uint64_t tiles;       // tiles per block (direct kinds, K_ONESHOT: per buffer) or per chunk (ring)
   uint64_t loops;       // ring: chunk loops per block
+  uint64_t window;      // ring: chunk loops per ticket window
   uint64_t groups;      // phased kinds: ticket groups
   uint64_t per_group;   // phased kinds: tasks per group
   uint64_t ntasks;
@@ -113,34 +115,20 @@ AR_HD void tile_range(const Geometry& g, uint64_t len, uint64_t k, uint64_t* lo,
   *hi = umin((k + 1) * g.tile, len);
 }
 
-// Ring: the p-th (loop, step) cell of a `loops` x `steps` grid in diagonal
-// order (loop + step ascending, then step ascending), so a chain's step s-1
-// always precedes its step s and consecutive chunks stream through the steps
-// like a pipeline.  Diagonal d holds min(d+1, m) cells while it grows, m in
-// the middle, and shrinks by one per diagonal at the end (m = min(loops,
-// steps) <= 15), so the two ramps are walked and the middle is solved.
-AR_HD void ring_cell(uint64_t p, uint64_t loops, uint64_t steps, uint64_t* loop, uint64_t* step) {
-  const uint64_t m = umin(loops, steps), big = umax(loops, steps);
-  uint64_t d = 0, before = 0;  // diagonal and cells before it
-  const uint64_t ramp = m * (m + 1) / 2;   // cells in diagonals [0, m)
-  if (p < ramp) {
-    while (before + d + 1 <= p) { before += d + 1; ++d; }
-  } else {
-    const uint64_t flat = (big - m) * m;   // cells in diagonals [m, big)
-    if (p < ramp + flat) {
-      d = m + (p - ramp) / m;
-      before = ramp + (d - m) * m;
-    } else {
-      d = big;
-      before = ramp + flat;
-      uint64_t size = m - 1;               // diagonal `big` holds m-1 cells
-      while (before + size <= p) { before += size; --size; ++d; }
-    }
-  }
-  const uint64_t s_first = (d + 1 > loops) ? d + 1 - loops : 0;
-  const uint64_t s = s_first + (p - before);
-  *step = s;
-  *loop = d - s;
+// Ring: the p-th (loop, step) cell.  Loops are cut into windows of
+// `window` loops; windows are taken in order and, inside a window, step by
+// step (all loops of step 0, then of step 1, ...).  A chain's step s-1 thus
+// always precedes its step s, and they sit a whole window-step apart, so
+// with windows wider than the set of resident workgroups a task's
+// predecessor has almost always finished when the task is taken.
+AR_HD void ring_cell(uint64_t p, uint64_t loops, uint64_t steps, uint64_t window, uint64_t* loop,
+                     uint64_t* step) {
+  const uint64_t per_window = steps * window;
+  const uint64_t w = p / per_window, r = p % per_window;
+  const uint64_t first = w * window;
+  const uint64_t width = umin(window, loops - first);  // the last window may be narrower
+  *step = r / width;
+  *loop = first + r % width;
 }
 
 AR_HD int32_t rank_mod(int64_t x, int32_t n) { return (int32_t)(((x % n) + n) % n); }
@@ -168,7 +156,7 @@ AR_HD Task decode(const Geometry& g, uint64_t t) {
     const uint64_t per_cell = (uint64_t)n * g.tiles;
     const uint64_t p = t / per_cell, rem = t % per_cell;
     uint64_t loop, step;
-    ring_cell(p, g.loops, (uint64_t)g.steps, &loop, &step);
+    ring_cell(p, g.loops, (uint64_t)g.steps, g.window, &loop, &step);
     const uint64_t j = rem / g.tiles, kk = rem % g.tiles;
     k.block = j;
     k.step = (int32_t)step;

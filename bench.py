@@ -159,7 +159,9 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
+    status = comm.check()
+    if status[0] != "AR_OK":
+        raise SystemExit(f"device error during warm-up: {status}")
     print(f"[bench] {args.workload}: warmup {args.warmup} done", file=sys.stderr, flush=True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

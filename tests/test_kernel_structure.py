@@ -1,0 +1,64 @@
+"""Structure of the compiled gfx950 kernels (CPU only: compiles to assembly).
+
+Regression guard for a hang: when thread 0's ticket fetch (top of the
+persistent task loop) and a thread-0-only store (end of a task) sat in one
+lane-divergent region around the loop's back edge, the compiler split the
+loop by lane.  Lanes 1..63 then re-ran the task on a stale ticket at the
+barrier while lane 0 waited for them outside: an endless loop.  The kernels
+now keep every barrier of a task in the same loop as the ticket fetch.
+Also checks that no kernel spills to scratch memory.
+"""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "all_reduce_reduction_rank_amd", "csrc", "kernels.hip")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "kernels.s"
+    cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-S", "--cuda-device-only",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", str(out), SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        pytest.fail(res.stderr)
+    return out.read_text()
+
+
+def _kernels(text):
+    return list(re.finditer(r"^(_ZN2ar17collective_kernel\w+):(.*?)s_endpgm", text, re.S | re.M))
+
+
+def test_every_kernel_compiled(asm):
+    # 3 payload types x (3 protocols x 5 schedules + 1 copy kernel)
+    assert len(_kernels(asm)) == 48
+
+
+def test_ticket_fetch_and_barriers_share_one_loop(asm):
+    for m in _kernels(asm):
+        name, body = m.group(1), m.group(2)
+        header = None
+        fetch_loop = barrier_loop = None
+        for line in body.split("\n"):
+            if line.startswith(".LBB"):
+                h = re.search(r"Header=BB(\w+) Depth=(\d)", line)
+                if h:
+                    header = h.groups()
+                elif "Loop Header" in line:
+                    header = (line.split(":")[0][4:], re.search(r"Depth=(\d)", line).group(1))
+            if fetch_loop is None and re.search(r"global_atomic_add v\d+, v\d+, v\d+, s\[\d+:\d+\] sc0$", line):
+                fetch_loop = header
+            elif fetch_loop is not None and barrier_loop is None and "s_barrier" in line:
+                barrier_loop = header
+        assert fetch_loop is not None, name
+        assert barrier_loop == fetch_loop, f"{name}: first barrier in loop {barrier_loop}, fetch in {fetch_loop}"
+
+
+def test_no_scratch(asm):
+    sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)
+    assert sizes and all(int(x) == 0 for x in sizes)
