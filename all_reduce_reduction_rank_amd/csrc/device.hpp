@@ -102,22 +102,29 @@ __device__ __forceinline__ uint4 ld16(const char* p) { return *(const uint4*)p; 
 __device__ __forceinline__ void st16(char* p, const uint4& v) { *(uint4*)p = v; }
 
 // Load a 16-byte vector of which only `nbytes` (< 16, whole elements) exist;
-// the rest reads as zero.  `esize` = 2 or 4.
+// the rest reads as zero.  `esize` = 2 or 4.  Fixed-trip unrolled loops keep
+// every index a constant, so the vector stays in registers.
 __device__ __forceinline__ uint4 ld_partial(const char* p, uint32_t nbytes, int esize) {
   uint32_t w[4] = {0, 0, 0, 0};
-  for (uint32_t b = 0; b < nbytes; b += esize) {
-    uint32_t v = (esize == 2) ? (uint32_t)(*(const uint16_t*)(p + b)) : *(const uint32_t*)(p + b);
-    w[b >> 2] |= v << ((b & 3) * 8);
+#pragma unroll
+  for (int b = 0; b < 16; b += 2) {
+    if ((uint32_t)b < nbytes && (esize == 2 || (b & 3) == 0)) {
+      const uint32_t v = (esize == 2) ? (uint32_t)(*(const uint16_t*)(p + b)) : *(const uint32_t*)(p + b);
+      w[b >> 2] |= v << ((b & 3) * 8);
+    }
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 __device__ __forceinline__ void st_partial(char* p, const uint4& v, uint32_t nbytes, int esize) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  for (uint32_t b = 0; b < nbytes; b += esize) {
-    const uint32_t x = w[b >> 2] >> ((b & 3) * 8);
-    if (esize == 2) *(uint16_t*)(p + b) = (uint16_t)x;
-    else *(uint32_t*)(p + b) = x;
+#pragma unroll
+  for (int b = 0; b < 16; b += 2) {
+    if ((uint32_t)b < nbytes && (esize == 2 || (b & 3) == 0)) {
+      const uint32_t x = w[b >> 2] >> ((b & 3) * 8);
+      if (esize == 2) *(uint16_t*)(p + b) = (uint16_t)x;
+      else *(uint32_t*)(p + b) = x;
+    }
   }
 }
 

@@ -123,17 +123,15 @@ struct LTerm {
 
 __device__ __forceinline__ uint32_t ld_word(const char* p, uint32_t nb, int es) {
   if (nb == 4 && ((uintptr_t)p & 3) == 0) return *(const uint32_t*)p;
-  uint32_t w = 0;
-  for (uint32_t b = 0; b < nb; b += es)
-    w |= (es == 2 ? (uint32_t)(*(const uint16_t*)(p + b)) : *(const uint32_t*)(p + b)) << (8 * b);
+  uint32_t w = 0;  // es == 2 here: one or two 2-byte elements
+  if (nb > 0) w = *(const uint16_t*)p;
+  if (nb > 2) w |= (uint32_t)(*(const uint16_t*)(p + 2)) << 16;
   return w;
 }
 __device__ __forceinline__ void st_word(char* p, uint32_t w, uint32_t nb, int es) {
   if (nb == 4 && ((uintptr_t)p & 3) == 0) { *(uint32_t*)p = w; return; }
-  for (uint32_t b = 0; b < nb; b += es) {
-    if (es == 2) *(uint16_t*)(p + b) = (uint16_t)(w >> (8 * b));
-    else *(uint32_t*)(p + b) = w;
-  }
+  if (nb > 0) *(uint16_t*)p = (uint16_t)w;
+  if (nb > 2) *(uint16_t*)(p + 2) = (uint16_t)(w >> 16);
 }
 
 // LL: 8-byte lines {payload word, flag}, written and read as one 64-bit

@@ -6,7 +6,7 @@ lane-divergent region around the loop's back edge, the compiler split the
 loop by lane.  Lanes 1..63 then re-ran the task on a stale ticket at the
 barrier while lane 0 waited for them outside: an endless loop.  The kernels
 now keep every barrier of a task in the same loop as the ticket fetch.
-Also checks that no kernel spills to scratch memory.
+Also checks that no kernel spills vector registers to scratch memory.
 """
 
 import os
@@ -59,6 +59,7 @@ def test_ticket_fetch_and_barriers_share_one_loop(asm):
         assert barrier_loop == fetch_loop, f"{name}: first barrier in loop {barrier_loop}, fetch in {fetch_loop}"
 
 
-def test_no_scratch(asm):
-    sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)
-    assert sizes and all(int(x) == 0 for x in sizes)
+def test_no_spills_to_memory(asm):
+    spills = re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm)
+    assert spills and all(int(x) == 0 for x in spills)
+    assert not re.search(r"^\s+scratch_(load|store)", asm, re.M)
