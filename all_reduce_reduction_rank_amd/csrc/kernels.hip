@@ -30,27 +30,37 @@ constexpr int U_LL = 4;      // LL words per thread per pass
 constexpr int U_LL128 = 4;   // LL128 line groups (8 lines of a wave) per pass
 
 // =============================================================== Simple path
-// dst = fold(term(0), ..., term(n-1)) over `nbytes` (whole elements); a term
-// is a plain pointer.  One term = raw copy (bit-exact for every type).
-template <int DT, class Term>
+// dst = fold(term(0), ..., term(n-1)) over `nbytes` (whole elements, at most
+// 64 KiB: one tile).  One term = raw copy (bit-exact for every type).
+// COH_FIRST: term(0) was written by another rank program during this call
+// (read at device scope).  COH_DST: dst will be read by another rank program
+// during this call (written at device scope).  Other terms are inputs.
+template <int DT, bool COH_FIRST, bool COH_DST, class Term>
 __device__ __forceinline__ void simple_stream(Term term, int nterms, char* dst, uint64_t nbytes) {
   const int es = Elem<DT>::size;
-  bool aligned = ((uintptr_t)dst & 15) == 0;
-  for (int i = 0; i < nterms; ++i) aligned = aligned && (((uintptr_t)term(i) & 15) == 0);
-  const uint64_t nfull = aligned ? nbytes / 16 : 0;
-  for (uint64_t base = threadIdx.x; base < nfull; base += (uint64_t)U_SIMPLE * WG_THREADS) {
+  const char* t0 = term(0);
+  const Rsrc r0 = make_rsrc(t0, (uint32_t)nbytes);
+  const Rsrc rd = make_rsrc(dst, (uint32_t)nbytes);
+  bool aligned = (((uintptr_t)dst | (uintptr_t)t0) & 15) == 0;
+  for (int i = 1; i < nterms; ++i) aligned = aligned && (((uintptr_t)term(i) & 15) == 0);
+  const uint32_t nfull = aligned ? (uint32_t)(nbytes / 16) : 0u;
+  for (uint32_t base = threadIdx.x; base < nfull; base += U_SIMPLE * WG_THREADS) {
     uint4 x[U_SIMPLE];
     Vec<DT> acc[U_SIMPLE];
 #pragma unroll
     for (int u = 0; u < U_SIMPLE; ++u) {
-      const uint64_t v = base + (uint64_t)u * WG_THREADS;
-      x[u] = (v < nfull) ? ld16(term(0) + v * 16) : make_uint4(0, 0, 0, 0);
+      const uint32_t v = base + u * WG_THREADS;
+      x[u] = make_uint4(0, 0, 0, 0);
+      if (v < nfull) x[u] = COH_FIRST ? cld16(r0, v * 16) : ld16(t0 + (uint64_t)v * 16);
     }
     if (nterms == 1) {
 #pragma unroll
       for (int u = 0; u < U_SIMPLE; ++u) {
-        const uint64_t v = base + (uint64_t)u * WG_THREADS;
-        if (v < nfull) st16(dst + v * 16, x[u]);
+        const uint32_t v = base + u * WG_THREADS;
+        if (v < nfull) {
+          if (COH_DST) cst16(rd, v * 16, x[u]);
+          else st16(dst + (uint64_t)v * 16, x[u]);
+        }
       }
       continue;
     }
@@ -60,56 +70,80 @@ __device__ __forceinline__ void simple_stream(Term term, int nterms, char* dst, 
       const char* p = term(i);
 #pragma unroll
       for (int u = 0; u < U_SIMPLE; ++u) {
-        const uint64_t v = base + (uint64_t)u * WG_THREADS;
-        x[u] = (v < nfull) ? ld16(p + v * 16) : make_uint4(0, 0, 0, 0);
+        const uint32_t v = base + u * WG_THREADS;
+        x[u] = (v < nfull) ? ld16(p + (uint64_t)v * 16) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < U_SIMPLE; ++u) acc[u].add(Vec<DT>::widen(x[u]));
     }
 #pragma unroll
     for (int u = 0; u < U_SIMPLE; ++u) {
-      const uint64_t v = base + (uint64_t)u * WG_THREADS;
-      if (v < nfull) st16(dst + v * 16, acc[u].narrow());
+      const uint32_t v = base + u * WG_THREADS;
+      if (v < nfull) {
+        if (COH_DST) cst16(rd, v * 16, acc[u].narrow());
+        else st16(dst + (uint64_t)v * 16, acc[u].narrow());
+      }
     }
   }
   // Remainder (and every vector of a misaligned range): element-exact path.
-  const uint64_t done = nfull * 16;
-  const uint64_t nrest = cdiv(nbytes - done, 16);
-  for (uint64_t v = threadIdx.x; v < nrest; v += WG_THREADS) {
-    const uint64_t off = done + v * 16;
+  const uint32_t done = nfull * 16;
+  const uint32_t nrest = (uint32_t)cdiv(nbytes - done, 16);
+  for (uint32_t v = threadIdx.x; v < nrest; v += WG_THREADS) {
+    const uint32_t off = done + v * 16;
     const uint32_t nb = (uint32_t)umin(16, nbytes - off);
-    uint4 x = ld_any(term(0) + off, nb, es);
+    uint4 x = COH_FIRST ? cld_partial(r0, off, nb, es) : ld_any(t0 + off, nb, es);
     if (nterms > 1) {
       Vec<DT> acc = Vec<DT>::widen(x);
       for (int i = 1; i < nterms; ++i) acc.add(Vec<DT>::widen(ld_any(term(i) + off, nb, es)));
       x = acc.narrow();
     }
-    st_any(dst + off, x, nb, es);
+    if (COH_DST) cst_partial(rd, off, x, nb, es);
+    else st_any(dst + off, x, nb, es);
+  }
+}
+
+// simple_stream with the coherence choices made at run time (uniform values).
+template <int DT, class Term>
+__device__ __forceinline__ void stream(bool coh_first, bool coh_dst, Term term, int nterms, char* dst,
+                                       uint64_t nbytes) {
+  if (coh_first) {
+    if (coh_dst) simple_stream<DT, true, true>(term, nterms, dst, nbytes);
+    else simple_stream<DT, true, false>(term, nterms, dst, nbytes);
+  } else {
+    if (coh_dst) simple_stream<DT, false, true>(term, nterms, dst, nbytes);
+    else simple_stream<DT, false, false>(term, nterms, dst, nbytes);
   }
 }
 
 // Workgroup waits until *f >= target (thread 0 polls with back-off); false
 // if the call is aborted.  Thread 0's verdict is broadcast, so all waves take
-// the same path through the barriers that follow.
+// the same path through the barriers that follow.  The data the flag guards
+// is then read at device scope; the (cheap) acquire fence additionally drops
+// any stale cached copies.
 __device__ __forceinline__ bool wg_wait(const KArgs& a, const uint64_t* f, uint64_t target, int step,
                                         int rank) {
   __shared__ int s_ok;
-  if (threadIdx.x == 0) s_ok = wait_ge(f, target, a, step, rank) ? 1 : 0;
+  if (threadIdx.x == 0) {
+    const bool ok = wait_ge(f, target, a, step, rank);
+    if (ok) fence_acquire();
+    s_ok = ok ? 1 : 0;
+  }
   __syncthreads();
   // readfirstlane: the outcome is the same for the whole workgroup, and the
   // compiler must know it, or it may split the surrounding loop by lane.
   const bool ok = uniform(s_ok) != 0;
-  fence_acquire();
   __syncthreads();  // s_ok may be rewritten by the next wait
   return ok;
 }
 
-// Workgroup publishes everything it stored, then sets *f = v.  Every thread
-// stores the same value to the same word (one write per wave): a store left
-// to thread 0 alone at the end of a task lets the compiler defer it past the
-// next loop iteration's barrier, stranding the other lanes on a stale ticket.
+// Workgroup signals *f = v once every access of its task has completed: the
+// device-scope data stores are then visible device-wide (and, for a read-done
+// signal, every load has returned).  Every thread stores the same value to
+// the same word (one write per wave): a store left to thread 0 alone at the
+// end of a task lets the compiler defer it past the next loop iteration's
+// barrier, stranding the other lanes on a stale ticket.
 __device__ __forceinline__ void wg_signal(const KArgs& a, uint64_t* f, uint64_t v, int step, int rank) {
-  fence_release();
+  wait_mem();
   __syncthreads();
   if (!(rank == a.inj_rank && step == a.inj_step)) st_flag(f, v);
 }
@@ -285,13 +319,14 @@ __device__ __forceinline__ void ll128_pass(const KArgs& a, Terms terms, int nter
             if (wall_clock64() - t0 > a.timeout) { raise_timeout(a.ctl, step, rank); break; }
           }
         }
-        fence_acquire();
+        // Flags seen: read the payload at device scope.
+        const Rsrc rl = make_rsrc(tm.lines, (uint32_t)(nlines * LL128_LINE));
 #pragma unroll
         for (int u = 0; u < U_LL128; ++u) {
-          const char* p = tm.lines + line[u] * LL128_LINE + 16ull * q;
+          const uint32_t off = (uint32_t)(line[u] * LL128_LINE + 16ull * q);
           if (!nb[u]) val[u] = make_uint4(0, 0, 0, 0);
-          else if (q < 7) val[u] = ld16(p);
-          else { const uint2 lo = *(const uint2*)p; val[u] = make_uint4(lo.x, lo.y, 0, 0); }
+          else if (q < 7) val[u] = cld16(rl, off);
+          else { const uint2 lo = cld8(rl, off); val[u] = make_uint4(lo.x, lo.y, 0, 0); }
         }
       }
       if (nterms > 1) {
@@ -311,16 +346,18 @@ __device__ __forceinline__ void ll128_pass(const KArgs& a, Terms terms, int nter
         if (nb[u]) st_piece(out_plain + line[u] * LL128_DATA + 16ull * q, res[u], nb[u], es);
     }
     if (out_lines) {
-      // Payload of every line first (a partial lane stores zero padding) ...
+      // Payload of every line first, at device scope (a partial lane stores
+      // zero padding) ...
+      const Rsrc rl = make_rsrc(out_lines, (uint32_t)(nlines * LL128_LINE));
 #pragma unroll
       for (int u = 0; u < U_LL128; ++u) {
         if (line[u] >= nlines) continue;
-        char* p = out_lines + line[u] * LL128_LINE + 16ull * q;
-        if (q < 7) st16(p, res[u]);
-        else *(uint2*)p = make_uint2(res[u].x, res[u].y);
+        const uint32_t off = (uint32_t)(line[u] * LL128_LINE + 16ull * q);
+        if (q < 7) cst16(rl, off, res[u]);
+        else cst8(rl, off, make_uint2(res[u].x, res[u].y));
       }
-      // ... made visible device-wide, then the flags.
-      fence_release();
+      // ... complete (visible device-wide), then the flags.
+      wait_mem();
 #pragma unroll
       for (int u = 0; u < U_LL128; ++u)
         if (q == 7 && line[u] < nlines)
@@ -358,7 +395,7 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
 
   if constexpr (KIND == K_COPY) {
     const uint64_t off = k.lo * es;
-    simple_stream<DT>([&](int) { return a.in[0] + off; }, 1, a.out[0] + off, nbytes);
+    simple_stream<DT, false, false>([&](int) { return a.in[0] + off; }, 1, a.out[0] + off, nbytes);
   }
 
   if constexpr (KIND == K_ONESHOT) {
@@ -366,7 +403,7 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
     const int r = k.rank;
     if constexpr (PROTO == PROTO_SIMPLE) {
       if (!g.in_place) {
-        simple_stream<DT>([&](int i) { return a.in[i] + off; }, n, a.out[r] + off, nbytes);
+        simple_stream<DT, false, false>([&](int i) { return a.in[i] + off; }, n, a.out[r] + off, nbytes);
         return;
       }
       // In place: every rank program of this tile reads all N inputs into
@@ -418,11 +455,13 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
     if constexpr (PROTO == PROTO_SIMPLE) {
       uint64_t* fl = a.flags + j * g.tiles + k.tile;
       if (k.phase == PH_FOLD) {  // shot 1: rank j sums block j of every rank
-        simple_stream<DT>([&](int i) { return a.in[i] + off; }, n, a.out[j] + off, nbytes);
+        // block j's sum is read back by the other ranks: device scope
+        simple_stream<DT, false, true>([&](int i) { return a.in[i] + off; }, n, a.out[j] + off, nbytes);
         wg_signal(a, fl, tag + 1, 0, r);
       } else {  // shot 2: rank r reads block j's sum back
         if (!wg_wait(a, fl, tag + 1, 1, r)) return;
-        simple_stream<DT>([&](int) { return (const char*)a.out[j] + off; }, 1, a.out[r] + off, nbytes);
+        simple_stream<DT, true, false>([&](int) { return (const char*)a.out[j] + off; }, 1, a.out[r] + off,
+                                        nbytes);
       }
     } else {
       const uint64_t nn = (uint64_t)n * n;
@@ -449,7 +488,7 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
     const uint64_t in_off = (block_lo(g, j) + k.lo) * es, out_off = k.lo * es;
     const int r = k.rank;
     if constexpr (PROTO == PROTO_SIMPLE) {
-      simple_stream<DT>([&](int i) { return a.in[i] + in_off; }, n, a.out[j] + out_off, nbytes);
+      simple_stream<DT, false, false>([&](int i) { return a.in[i] + in_off; }, n, a.out[j] + out_off, nbytes);
     } else {
       if (k.phase == PH_SEND) {
         line_pass<DT, PROTO>(a, [&](int) { return LTerm{a.in[r] + in_off, nullptr}; }, 1, nullptr,
@@ -471,7 +510,7 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
     const uint64_t in_off = k.lo * es, out_off = (block_lo(g, j) + k.lo) * es;
     const int r = k.rank;
     if constexpr (PROTO == PROTO_SIMPLE) {
-      simple_stream<DT>([&](int) { return a.in[j] + in_off; }, 1, a.out[r] + out_off, nbytes);
+      simple_stream<DT, false, false>([&](int) { return a.in[j] + in_off; }, 1, a.out[r] + out_off, nbytes);
     } else {
       if (k.phase == PH_SEND) {  // rank j publishes its shard and keeps its own copy
         line_pass<DT, PROTO>(a, [&](int) { return LTerm{a.in[j] + in_off, nullptr}; }, 1,
@@ -493,24 +532,27 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
     if constexpr (PROTO == PROTO_SIMPLE) {
       uint64_t* fl = a.flags + k.chain;
       if (s > 0 && !wg_wait(a, fl, tag + (uint64_t)s, s, q)) return;
+      // A partial or copied block read by the next step's rank moves at
+      // device scope; inputs and the last step's output do not.
+      const bool last = (s == steps - 1);
       if (g.op == OP_ALLREDUCE) {
         if (s < n - 1) {  // reduce step: rank q adds its input to the partial from q-1
           const char* src = (s == 0) ? a.in[R(j + 1)] + boff : (const char*)a.out[R(j + 1 + s)] + boff;
           const char* own = a.in[q] + boff;
-          simple_stream<DT>([&](int i) { return i == 0 ? src : own; }, 2, a.out[q] + boff, nbytes);
+          stream<DT>(s > 0, true, [&](int i) { return i == 0 ? src : own; }, 2, a.out[q] + boff, nbytes);
         } else {          // copy step: rank q copies the finished block from q-1
           const char* src = a.out[R(q - 1)] + boff;
-          simple_stream<DT>([&](int) { return src; }, 1, a.out[q] + boff, nbytes);
+          stream<DT>(true, !last, [&](int) { return src; }, 1, a.out[q] + boff, nbytes);
         }
       } else if (g.op == OP_REDUCE_SCATTER) {
         const char* src = (s == 0) ? a.in[R(j + 1)] + boff
                                    : (const char*)(a.stage + (uint64_t)R(j + 1 + s) * a.stage_stride + boff);
         char* dst = (s == n - 2) ? a.out[j] + loff : a.stage + (uint64_t)q * a.stage_stride + boff;
         const char* own = a.in[q] + boff;
-        simple_stream<DT>([&](int i) { return i == 0 ? src : own; }, 2, dst, nbytes);
+        stream<DT>(s > 0, !last, [&](int i) { return i == 0 ? src : own; }, 2, dst, nbytes);
       } else {  // all-gather: step 0 = rank j's own copy, step s = rank j+s receives
         const char* src = (s <= 1) ? a.in[j] + loff : (const char*)a.out[R(q - 1)] + boff;
-        simple_stream<DT>([&](int) { return src; }, 1, a.out[q] + boff, nbytes);
+        stream<DT>(s >= 2, s >= 1 && !last, [&](int) { return src; }, 1, a.out[q] + boff, nbytes);
       }
       if (s < steps - 1) wg_signal(a, fl, tag + (uint64_t)s + 1, s, q);
     } else {
