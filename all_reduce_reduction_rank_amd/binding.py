@@ -36,7 +36,7 @@ STATUS = {
 SYMBOLS = (
     "ar_comm_create", "ar_comm_destroy", "ar_comm_check", "ar_comm_reset",
     "ar_comm_workspace_bytes", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
-    "ar_plan_bytes", "ar_debug_inject", "ar_status_string",
+    "ar_plan_bytes", "ar_debug_inject", "ar_debug_state", "ar_status_string",
 )
 
 
@@ -63,6 +63,7 @@ def _declare(lib):
     lib.ar_plan_bytes.argtypes = [I, I, S, I, I, I, S, I, ctypes.POINTER(U64), ctypes.POINTER(U64),
                                   ctypes.POINTER(U64), ctypes.POINTER(U64)]
     lib.ar_debug_inject.argtypes = [P, I, I, U64]
+    lib.ar_debug_state.argtypes = [P, P, ctypes.POINTER(U64), I]
     lib.ar_status_string.argtypes = [I]
     lib.ar_status_string.restype = ctypes.c_char_p
     for name in SYMBOLS:
@@ -180,6 +181,14 @@ class Comm:
 
     def reset(self, stream=None):
         _check(_lib().ar_comm_reset(self._h, _stream_handle(stream)), "ar_comm_reset")
+
+    def debug_state(self, stream=None):
+        """Device control block: see ar_debug_state in include/ar.h."""
+        out = (ctypes.c_uint64 * 10)()
+        _check(_lib().ar_debug_state(self._h, _stream_handle(stream), out, 10), "ar_debug_state")
+        keys = ("timeouts", "flag_index", "seen", "awaited", "epoch_then", "tasks_done", "calls", "ticket",
+                "done", "abort")
+        return dict(zip(keys, list(out)))
 
     def inject(self, rank: int, step: int, timeout_us: int = 0):
         _check(_lib().ar_debug_inject(self._h, rank, step, timeout_us), "ar_debug_inject")

@@ -144,6 +144,17 @@ ar_status ar_comm_check(ar_comm_t c, ar_stream_t stream, int* err_rank, int* err
   return (ar_status)h.err_code;
 }
 
+ar_status ar_debug_state(ar_comm_t c, ar_stream_t stream, uint64_t* out, int n) {
+  if (!c || !out || n < 0) return AR_ERR_INVALID;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return AR_ERR_HIP;
+  Ctl h;
+  if (hipMemcpy(&h, c->ctl, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return AR_ERR_HIP;
+  const uint64_t words[10] = {h.diag[0], h.diag[1], h.diag[2], h.diag[3], h.diag[4], h.diag[5],
+                              h.epoch, h.ticket, h.done, h.abort};
+  for (int i = 0; i < n && i < 10; ++i) out[i] = words[i];
+  return AR_OK;
+}
+
 ar_status ar_comm_reset(ar_comm_t c, ar_stream_t stream) {
   if (!c) return AR_ERR_INVALID;
   if (ar::launch_reset(c->ctl, (hipStream_t)stream) != hipSuccess) return AR_ERR_HIP;

@@ -146,6 +146,12 @@ __device__ __forceinline__ uint64_t ld_flag(const uint64_t* p) {
 __device__ __forceinline__ void st_flag(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Raise a flag to v: flag values only grow within and across calls, so an
+// atomic max can never move a flag backwards, whatever the order in which
+// signals land.
+__device__ __forceinline__ void raise_flag(uint64_t* p, uint64_t v) {
+  __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -234,6 +240,10 @@ struct Ctl {
   uint32_t err_code;  // 0 or the ar_status of the latched error
   uint32_t err_key;   // min over blocked waits of (step << 8 | rank), ~0 if none
   uint32_t pad3[29];
+  // Diagnostics of the first wait that timed out: set, flag word index,
+  // value seen, value awaited, call counter; then tasks finished this call.
+  uint64_t diag[6];
+  uint64_t pad4[10];
 };
 
 struct KArgs {
@@ -253,6 +263,17 @@ struct KArgs {
 __device__ __forceinline__ void note_blocked(Ctl* c, int step, int rank) {
   __hip_atomic_fetch_min(&c->err_key, (uint32_t)((step << 8) | rank), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void record_timeout(Ctl* c, const uint64_t* base, const uint64_t* f, uint64_t seen,
+                                               uint64_t target) {
+  if (__hip_atomic_fetch_add(&c->diag[0], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+    __hip_atomic_store(&c->diag[1], (uint64_t)(f - base), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&c->diag[2], seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&c->diag[3], target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&c->diag[4], __hip_atomic_load(&c->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 __device__ __forceinline__ void raise_timeout(Ctl* c, int step, int rank) {
@@ -276,7 +297,11 @@ __device__ __forceinline__ bool wait_ge(const uint64_t* f, uint64_t target, cons
     if (ld_flag(f) >= target) return true;
     if ((++polls & 7) == 0) {
       if (ld_u32(&a.ctl->abort)) { note_blocked(a.ctl, step, rank); return false; }
-      if (wall_clock64() - t0 > a.timeout) { raise_timeout(a.ctl, step, rank); return false; }
+      if (wall_clock64() - t0 > a.timeout) {
+        record_timeout(a.ctl, a.flags, f, ld_flag(f), target);
+        raise_timeout(a.ctl, step, rank);
+        return false;
+      }
     }
   }
 }

@@ -13,6 +13,8 @@
 // all-reduce & launching TP/PP", section "Direct answer" (reduce-scatter,
 // all-gather, ring = reduce-scatter + all-gather); the transfer encodings
 // follow the former page's section "Protocols" (see device.hpp).
+#include <stdlib.h>
+
 #include "device.hpp"
 
 namespace ar {
@@ -136,16 +138,17 @@ __device__ __forceinline__ bool wg_wait(const KArgs& a, const uint64_t* f, uint6
   return ok;
 }
 
-// Workgroup signals *f = v once every access of its task has completed: the
-// device-scope data stores are then visible device-wide (and, for a read-done
-// signal, every load has returned).  Every thread stores the same value to
-// the same word (one write per wave): a store left to thread 0 alone at the
-// end of a task lets the compiler defer it past the next loop iteration's
-// barrier, stranding the other lanes on a stale ticket.
+// Workgroup raises *f to v once every access of its task has completed: the
+// device-scope data stores are then visible device-wide (and, for a
+// read-done signal, every load has returned).  Exactly one lane signals: if
+// every wave stored the flag, a late wave's store of step s could land after
+// the next step's store of s+1 and move the flag backwards.  The barrier that
+// ends every task in the ticket loop keeps this lane-0 store from sharing a
+// divergent path with the next ticket fetch.
 __device__ __forceinline__ void wg_signal(const KArgs& a, uint64_t* f, uint64_t v, int step, int rank) {
   wait_mem();
   __syncthreads();
-  if (!(rank == a.inj_rank && step == a.inj_step)) st_flag(f, v);
+  if (threadIdx.x == 0 && !(rank == a.inj_rank && step == a.inj_step)) raise_flag(f, v);
 }
 
 // ============================================================ LL / LL128 path
@@ -627,6 +630,8 @@ __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
       if (first >= ntasks || ntasks - first <= i) { more = false; break; }
       const Task k = decode(a.g, first + i);
       if (k.phase != PH_NONE) run_task<DT, PROTO, KIND>(a, k, epoch);
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(&a.ctl->diag[5], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // Reconverge every lane before the next task or ticket fetch, so
       // thread 0's fetch never shares a divergent path with a task's tail.
       __syncthreads();
@@ -647,6 +652,7 @@ __global__ void reset_kernel(Ctl* c) {
   c->abort = 0;
   c->err_code = 0;
   c->err_key = 0xffffffffu;
+  c->diag[0] = 0;
 }
 
 // ============================================================== launching
@@ -712,7 +718,12 @@ hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream) {
   // one-shot in-place barrier waits on LATER tickets of its group, so it
   // must take them one at a time.
   const bool barrier = a.g.kind == K_ONESHOT && a.g.proto == PROTO_SIMPLE && a.g.in_place;
-  b.batch = barrier ? 1u : (uint32_t)umax(1, umin(4, a.g.ntasks / (8 * cap)));
+  static const int max_batch = [] {
+    const char* e = getenv("AR_BATCH");
+    const int v = e ? atoi(e) : 4;
+    return v < 1 ? 1 : (v > 16 ? 16 : v);
+  }();
+  b.batch = barrier ? 1u : (uint32_t)umax(1, umin((uint64_t)max_batch, a.g.ntasks / (8 * cap)));
   uint64_t grid = umin(cdiv(a.g.ntasks, b.batch), cap);
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(f, dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, b);

@@ -171,6 +171,13 @@ ar_status ar_plan_bytes(int nranks, ar_op op, size_t count, ar_dtype dtype, ar_a
  * the injection.  Used to exercise the timeout path from the host. */
 ar_status ar_debug_inject(ar_comm_t comm, int rank, int step, uint64_t timeout_us);
 
+/* Test hook: synchronize `stream` and copy up to n (<= 10) words of the
+ * communicator's device control block into out: [0] timed-out waits,
+ * [1] flag index, [2] value seen and [3] value awaited by the first of them,
+ * [4] the call counter then, [5] tasks finished (all calls), [6] calls
+ * completed, [7] ticket counter, [8] finished workgroups, [9] abort word. */
+ar_status ar_debug_state(ar_comm_t comm, ar_stream_t stream, uint64_t* out, int n);
+
 /* Static description of a status code. */
 const char* ar_status_string(ar_status status);
 

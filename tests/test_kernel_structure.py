@@ -31,7 +31,7 @@ def asm(tmp_path_factory):
 
 
 def _kernels(text):
-    return list(re.finditer(r"^(_ZN2ar17collective_kernel\w+):(.*?)s_endpgm", text, re.S | re.M))
+    return list(re.finditer(r"^(_ZN2ar17collective_kernel\w+):(.*?)^\.Lfunc_end", text, re.S | re.M))
 
 
 def test_every_kernel_compiled(asm):
@@ -57,6 +57,35 @@ def test_ticket_fetch_and_barriers_share_one_loop(asm):
                 barrier_loop = header
         assert fetch_loop is not None, name
         assert barrier_loop == fetch_loop, f"{name}: first barrier in loop {barrier_loop}, fetch in {fetch_loop}"
+
+
+def _blocks_by_loop(body):
+    """Map each line to the innermost loop header of its basic block."""
+    header, out = None, []
+    for line in body.split("\n"):
+        if line.startswith(".LBB"):
+            h = re.search(r"Header=BB(\w+) Depth=(\d)", line)
+            if h:
+                header = h.groups()
+            elif "Loop Header" in line:
+                header = (line.split(":")[0][4:], re.search(r"Depth=(\d)", line).group(1))
+        out.append((header, line))
+    return out
+
+
+def test_flag_raise_stays_in_its_task_loop(asm):
+    # A signal (the flag's atomic max) must sit in a loop that also holds a
+    # barrier -- the task's own iteration -- not be deferred to an outer
+    # loop behind the next ticket fetch.
+    seen = 0
+    for m in _kernels(asm):
+        lines = _blocks_by_loop(m.group(2))
+        barrier_loops = {h for h, l in lines if "s_barrier" in l}
+        for h, l in lines:
+            if "global_atomic_umax_x2" in l:
+                seen += 1
+                assert h in barrier_loops, f"{m.group(1)}: signal in loop {h} without a barrier"
+    assert seen >= 9  # ring, two-shot, one-shot-in-place signals of the Simple kernels
 
 
 def test_no_spills_to_memory(asm):
