@@ -71,7 +71,7 @@ def device_rank_inputs(nranks: int, count: int, dt: str, dist: str, seed: int = 
     out = []
     for r in range(nranks):
         g = torch.Generator(device=device)
-        g.manual_seed(((seed * 1000003 + cfg) * 1000003 + nranks) * 1000003 + r)
+        g.manual_seed((((seed * 1000003 + cfg) * 1000003 + nranks) * 1000003 + r) % (2 ** 63 - 1))
         if dist == "ones":
             t = torch.ones(count, dtype=torch.float32, device=device)
         elif dist == "int20":
