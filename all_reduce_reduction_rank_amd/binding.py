@@ -19,7 +19,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libar.so")
+# AR_LIBRARY points at another build of the same library (measurements only).
+LIB_PATH = os.environ.get("AR_LIBRARY") or os.path.join(HERE, "libar.so")
 
 OPS = {"allreduce": 0, "reduce_scatter": 1, "allgather": 2}
 ALGOS = {"oneshot": 0, "twoshot": 1, "ring": 2}

@@ -29,13 +29,14 @@ def _hipcc():
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libar.so; returns its path."""
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source and link the library (libar.so next to this file
+    unless `out` says otherwise); `defines` are extra -D options."""
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="ar_build_") as tmp:
         def compile_one(src):
             obj = os.path.join(tmp, src + ".o")
-            cmd = [hipcc, *HIPFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *HIPFLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
             res = subprocess.run(cmd, capture_output=True, text=True)
             if res.returncode != 0:
                 raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
@@ -45,13 +46,13 @@ def build(verbose: bool = False) -> str:
 
         with ThreadPoolExecutor(len(SOURCES)) as pool:
             objs = list(pool.map(compile_one, SOURCES))
-        tmp_lib = LIB + ".tmp"
+        tmp_lib = out + ".tmp"
         cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"link failed:\n{res.stderr}")
-        os.replace(tmp_lib, LIB)
-    return LIB
+        os.replace(tmp_lib, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -12,6 +12,7 @@
 // Ctl, flags and lines are zeroed at creation; flags and lines are tagged
 // with the device call counter, so they are never cleared again.
 #include <hip/hip_runtime.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/ar.h"
@@ -45,6 +46,19 @@ struct ar_comm {
 };
 
 static uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }
+
+// Tuning overrides read once from the environment (for measurements; they
+// never change results): AR_TILE_KB, AR_RING_SKEW, AR_RING_WINDOW.
+static const Tuning& tuning() {
+  static const Tuning t = [] {
+    Tuning x;
+    if (const char* e = getenv("AR_TILE_KB")) x.tile_bytes = strtoull(e, nullptr, 10) * 1024;
+    if (const char* e = getenv("AR_RING_SKEW")) { x.ring_skew = strtoull(e, nullptr, 10); x.ring_skew_set = true; }
+    if (const char* e = getenv("AR_RING_WINDOW")) x.ring_window = strtoull(e, nullptr, 10);
+    return x;
+  }();
+  return t;
+}
 
 // Largest staging any LL / LL128 call on payloads of up to `line_bytes` per
 // rank can need (the ring all-reduce dominates; checked again per call).
@@ -226,7 +240,7 @@ static ar_status run(ar_comm_t c, int op, const void* const* send, void* const* 
   }
 
   Geometry g;
-  if (!make_geometry(op, algo, proto, dtype, n, count, chunk_bytes, in_place, &g)) return AR_ERR_INVALID;
+  if (!make_geometry(op, algo, proto, dtype, n, count, chunk_bytes, in_place, &g, tuning())) return AR_ERR_INVALID;
   if (g.ntasks == 0) return AR_OK;
   if (g.ntasks >= (1ull << 31)) return AR_ERR_TOO_LARGE;
   if (g.nflags > c->nflags || staging_bytes(g) > c->lines_bytes) return AR_ERR_TOO_LARGE;

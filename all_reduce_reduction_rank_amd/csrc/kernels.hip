@@ -37,7 +37,8 @@ constexpr int U_LL128 = 4;   // LL128 line groups (8 lines of a wave) per pass
 // COH_FIRST: term(0) was written by another rank program during this call
 // (read at device scope).  COH_DST: dst will be read by another rank program
 // during this call (written at device scope).  Other terms are inputs.
-template <int DT, bool COH_FIRST, bool COH_DST, class Term>
+// NT_IN: inputs are read once per call; NT_OUT: a plain dst is final output.
+template <int DT, bool COH_FIRST, bool COH_DST, bool NT_IN = true, bool NT_OUT = true, class Term>
 __device__ __forceinline__ void simple_stream(Term term, int nterms, char* dst, uint64_t nbytes) {
   const int es = Elem<DT>::size;
   const char* t0 = term(0);
@@ -53,7 +54,7 @@ __device__ __forceinline__ void simple_stream(Term term, int nterms, char* dst, 
     for (int u = 0; u < U_SIMPLE; ++u) {
       const uint32_t v = base + u * WG_THREADS;
       x[u] = make_uint4(0, 0, 0, 0);
-      if (v < nfull) x[u] = COH_FIRST ? cld16(r0, v * 16) : ld16(t0 + (uint64_t)v * 16);
+      if (v < nfull) x[u] = COH_FIRST ? cld16(r0, v * 16) : ld16_hint<NT_IN>(t0 + (uint64_t)v * 16);
     }
     if (nterms == 1) {
 #pragma unroll
@@ -61,7 +62,7 @@ __device__ __forceinline__ void simple_stream(Term term, int nterms, char* dst, 
         const uint32_t v = base + u * WG_THREADS;
         if (v < nfull) {
           if (COH_DST) cst16(rd, v * 16, x[u]);
-          else st16(dst + (uint64_t)v * 16, x[u]);
+          else st16_hint<NT_OUT>(dst + (uint64_t)v * 16, x[u]);
         }
       }
       continue;
@@ -73,7 +74,7 @@ __device__ __forceinline__ void simple_stream(Term term, int nterms, char* dst, 
 #pragma unroll
       for (int u = 0; u < U_SIMPLE; ++u) {
         const uint32_t v = base + u * WG_THREADS;
-        x[u] = (v < nfull) ? ld16(p + (uint64_t)v * 16) : make_uint4(0, 0, 0, 0);
+        x[u] = (v < nfull) ? ld16_hint<NT_IN>(p + (uint64_t)v * 16) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < U_SIMPLE; ++u) acc[u].add(Vec<DT>::widen(x[u]));
@@ -83,7 +84,7 @@ __device__ __forceinline__ void simple_stream(Term term, int nterms, char* dst, 
       const uint32_t v = base + u * WG_THREADS;
       if (v < nfull) {
         if (COH_DST) cst16(rd, v * 16, acc[u].narrow());
-        else st16(dst + (uint64_t)v * 16, acc[u].narrow());
+        else st16_hint<NT_OUT>(dst + (uint64_t)v * 16, acc[u].narrow());
       }
     }
   }
@@ -120,14 +121,15 @@ __device__ __forceinline__ void stream(bool coh_first, bool coh_dst, Term term, 
 // Workgroup waits until *f >= target (thread 0 polls with back-off); false
 // if the call is aborted.  Thread 0's verdict is broadcast, so all waves take
 // the same path through the barriers that follow.  The data the flag guards
-// is then read at device scope; the (cheap) acquire fence additionally drops
-// any stale cached copies.
+// is read afterwards with device-scope (sc1) loads, issued only once thread
+// 0's flag load has returned, so no acquire fence is needed: an agent-scope
+// acquire would invalidate the XCD's whole L2 on every task (measured: 3% of
+// ring bandwidth) and drop lines other tasks are about to reuse.
 __device__ __forceinline__ bool wg_wait(const KArgs& a, const uint64_t* f, uint64_t target, int step,
                                         int rank) {
   __shared__ int s_ok;
   if (threadIdx.x == 0) {
     const bool ok = wait_ge(f, target, a, step, rank);
-    if (ok) fence_acquire();
     s_ok = ok ? 1 : 0;
   }
   __syncthreads();
@@ -299,7 +301,7 @@ __device__ __forceinline__ void ll128_pass(const KArgs& a, Terms terms, int nter
           val[u] = nb[u] ? ld_piece(tm.plain + line[u] * LL128_DATA + 16ull * q, nb[u], es)
                          : make_uint4(0, 0, 0, 0);
       } else {
-        // Every lane polls its own line's flag word, then acquire, then reads.
+        // Every lane polls its own line's flag word, then reads the payload.
         bool ready = true;
 #pragma unroll
         for (int u = 0; u < U_LL128; ++u) {
@@ -406,7 +408,8 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
     const int r = k.rank;
     if constexpr (PROTO == PROTO_SIMPLE) {
       if (!g.in_place) {
-        simple_stream<DT, false, false>([&](int i) { return a.in[i] + off; }, n, a.out[r] + off, nbytes);
+        // every rank program of this tile re-reads the same inputs: keep them cached
+        simple_stream<DT, false, false, false>([&](int i) { return a.in[i] + off; }, n, a.out[r] + off, nbytes);
         return;
       }
       // In place: every rank program of this tile reads all N inputs into
@@ -513,7 +516,8 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
     const uint64_t in_off = k.lo * es, out_off = (block_lo(g, j) + k.lo) * es;
     const int r = k.rank;
     if constexpr (PROTO == PROTO_SIMPLE) {
-      simple_stream<DT, false, false>([&](int) { return a.in[j] + in_off; }, 1, a.out[r] + out_off, nbytes);
+      // shard j is read by every rank: keep it cached
+      simple_stream<DT, false, false, false>([&](int) { return a.in[j] + in_off; }, 1, a.out[r] + out_off, nbytes);
     } else {
       if (k.phase == PH_SEND) {  // rank j publishes its shard and keeps its own copy
         line_pass<DT, PROTO>(a, [&](int) { return LTerm{a.in[j] + in_off, nullptr}; }, 1,
@@ -608,6 +612,7 @@ __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
   if (threadIdx.x == 0) s_epoch = __hip_atomic_load(&a.ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t ntasks = (uint32_t)a.g.ntasks;
   const uint32_t batch = a.batch;
+  uint32_t finished = 0;  // tasks this workgroup ran (diagnostics)
   bool more = true;
   while (more) {
     if (threadIdx.x == 0) {
@@ -630,14 +635,14 @@ __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
       if (first >= ntasks || ntasks - first <= i) { more = false; break; }
       const Task k = decode(a.g, first + i);
       if (k.phase != PH_NONE) run_task<DT, PROTO, KIND>(a, k, epoch);
-      if (threadIdx.x == 0)
-        __hip_atomic_fetch_add(&a.ctl->diag[5], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ++finished;
       // Reconverge every lane before the next task or ticket fetch, so
       // thread 0's fetch never shares a divergent path with a task's tail.
       __syncthreads();
     }
   }
   if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(&a.ctl->diag[5], (uint64_t)finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t d = __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (d == gridDim.x - 1) {  // last workgroup out: rearm for the next call
       __hip_atomic_store(&a.ctl->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

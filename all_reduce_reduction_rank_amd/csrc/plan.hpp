@@ -21,24 +21,38 @@ constexpr uint64_t DEFAULT_CHUNK_BYTES = 512 * 1024;
 // Workgroups an MI355X keeps resident for these kernels (256 CUs x up to 8):
 // the tickets between a task and its predecessor should exceed it.
 constexpr uint64_t RESIDENT_HINT = 2048;
+// Bytes that one step of a ring window moves over all ranks: a quarter of
+// the 256 MB last-level cache (MALL), so a step's staged chunks are still
+// there when the next step reads them.
+constexpr uint64_t RING_WINDOW_BYTES = 64ull << 20;
 constexpr uint64_t LL128_TILE_UNIT = 3840;  // 32 lines of 120 payload bytes: one wave pass
 constexpr uint64_t LL128_ALIGN = 240;       // 2 lines: a multiple of 16 bytes and of 120 bytes
 
 inline int esize_of(int dtype) { return dtype == DT_BF16 ? 2 : 4; }
 
+// Tuning knobs (no effect on results): 0 keeps the built-in choice.
+struct Tuning {
+  uint64_t tile_bytes = 0;  // Simple tile size
+  uint64_t ring_skew = 0;   // ring order: 0 windowed, k >= 1 skewed diagonal
+  uint64_t ring_window = 0; // ring window (loops) for the windowed order
+  bool ring_skew_set = false;
+};
+
 // Tile size in bytes for a per-rank buffer of `rank_bytes`: aim for >= 128
 // tiles per rank so a call spreads over the 256 CUs, within the per-protocol
-// bounds (Simple up to 64 KiB, LL up to 16 KiB, LL128 whole wave passes).
-inline uint64_t pick_tile_bytes(int proto, uint64_t rank_bytes, bool inplace_oneshot) {
+// bounds (Simple up to 64 KiB on the ring, 128 KiB for the direct schedules,
+// whose tasks each do more flag work per byte; LL up to 16 KiB; LL128 whole
+// wave passes).
+inline uint64_t pick_tile_bytes(int proto, uint64_t rank_bytes, bool inplace_oneshot, bool ring) {
   const uint64_t want = floor_pow2(rank_bytes / 128 + 1);
-  if (proto == PROTO_SIMPLE) return clampu(want, 4096, inplace_oneshot ? 16384 : 65536);
+  if (proto == PROTO_SIMPLE) return clampu(want, 4096, inplace_oneshot ? 16384 : (ring ? 65536 : 131072));
   if (proto == PROTO_LL) return clampu(want, 4096, 16384);
   return LL128_TILE_UNIT * clampu(floor_pow2(want / LL128_TILE_UNIT + 1), 1, 4);
 }
 
 // Fill g for one call.  Returns false on an invalid combination.
 inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, uint64_t count,
-                          uint64_t chunk_bytes, int in_place, Geometry* out) {
+                          uint64_t chunk_bytes, int in_place, Geometry* out, const Tuning& tune = Tuning()) {
   if (nranks < 1 || nranks > MAX_RANKS) return false;
   if (op < 0 || op > 2 || algo < 0 || algo > 2 || proto < 0 || proto > 2 || dtype < 0 || dtype > 2)
     return false;
@@ -66,7 +80,7 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
     g.line_bytes = 0;
     g.total = count;
     g.block = count;
-    g.tile = pick_tile_bytes(PROTO_SIMPLE, count * es, false) / es;
+    g.tile = pick_tile_bytes(PROTO_SIMPLE, count * es, false, false) / es;
     g.tiles = cdiv(count, g.tile);
     g.ntasks = (op == OP_ALLREDUCE && in_place) ? 0 : g.tiles;
     *out = g;
@@ -79,7 +93,9 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
 
   const bool lines = proto != PROTO_SIMPLE;
   const uint64_t rank_bytes = g.total * es;
-  uint64_t tile_b = pick_tile_bytes(proto, rank_bytes, g.kind == K_ONESHOT && in_place && !lines);
+  uint64_t tile_b = pick_tile_bytes(proto, rank_bytes, g.kind == K_ONESHOT && in_place && !lines, g.kind == K_RING);
+  if (tune.tile_bytes && !lines && !(g.kind == K_ONESHOT && in_place))
+    tile_b = clampu(tune.tile_bytes / 16 * 16, 4096, 512 * 1024);
 
   if (g.kind == K_RING) {
     uint64_t cb = chunk_bytes ? chunk_bytes : DEFAULT_CHUNK_BYTES;
@@ -91,8 +107,11 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
     g.tile = tile_b / es;
     g.tiles = cdiv(g.chunk, g.tile);  // tiles per chunk loop
     g.loops = g.block ? cdiv(g.block, g.chunk) : 0;
-    // window: one step of a window spans ~2x the resident workgroups
-    g.window = umax(1, umin(g.loops, cdiv(2 * RESIDENT_HINT, n * g.tiles)));
+    // window: the loops whose chunks one step of a window moves fit
+    // RING_WINDOW_BYTES (for 512 KiB chunks at N=8: 16 loops, 1024 tasks)
+    g.window = umax(1, umin(g.loops, RING_WINDOW_BYTES / (n * cb)));
+    if (tune.ring_window) g.window = umax(1, umin(g.loops, tune.ring_window));
+    g.skew = tune.ring_skew_set ? tune.ring_skew : 0;
     if (op == OP_ALLREDUCE) g.steps = lines ? 2 * nranks - 1 : 2 * (nranks - 1);
     else if (op == OP_REDUCE_SCATTER) g.steps = lines ? nranks : nranks - 1;
     else g.steps = nranks;

@@ -77,7 +77,8 @@ struct Geometry {
   uint64_t chunk;       // ring: elements per chunk loop
   uint64_t tiles;       // tiles per block (direct kinds, K_ONESHOT: per buffer) or per chunk (ring)
   uint64_t loops;       // ring: chunk loops per block
-  uint64_t window;      // ring: chunk loops per ticket window
+  uint64_t window;      // ring: chunk loops per ticket window (skew == 0)
+  uint64_t skew;        // ring: 0 = windowed order; k >= 1 = order by loop + k*step
   uint64_t groups;      // phased kinds: ticket groups
   uint64_t per_group;   // phased kinds: tasks per group
   uint64_t ntasks;
@@ -115,20 +116,43 @@ AR_HD void tile_range(const Geometry& g, uint64_t len, uint64_t k, uint64_t* lo,
   *hi = umin((k + 1) * g.tile, len);
 }
 
-// Ring: the p-th (loop, step) cell.  Loops are cut into windows of
-// `window` loops; windows are taken in order and, inside a window, step by
-// step (all loops of step 0, then of step 1, ...).  A chain's step s-1 thus
-// always precedes its step s, and they sit a whole window-step apart, so
-// with windows wider than the set of resident workgroups a task's
-// predecessor has almost always finished when the task is taken.
-AR_HD void ring_cell(uint64_t p, uint64_t loops, uint64_t steps, uint64_t window, uint64_t* loop,
-                     uint64_t* step) {
-  const uint64_t per_window = steps * window;
-  const uint64_t w = p / per_window, r = p % per_window;
-  const uint64_t first = w * window;
-  const uint64_t width = umin(window, loops - first);  // the last window may be narrower
-  *step = r / width;
-  *loop = first + r % width;
+// Ring: the p-th (loop, step) cell of a `loops` x `steps` grid, in one of
+// two orders; both put a chain's step s-1 before its step s.
+//
+// skew == 0, windowed: loops are cut into windows of `window` loops; windows
+//   are taken in order and, inside one, step by step (all loops of step 0,
+//   then of step 1, ...).  Predecessors sit a whole window-step earlier.
+// skew k >= 1, skewed diagonal: cells ordered by loop + k*step (then step).
+//   Step s+1 of a loop follows step s after about k*steps cells, so data a
+//   step writes is read again soon (while still in the device cache) and
+//   chunks stream through the steps like a pipeline.
+AR_HD uint64_t ring_cells_below(uint64_t key, uint64_t loops, uint64_t steps, uint64_t skew) {
+  uint64_t n = 0;  // cells with loop + skew*step < key
+  for (uint64_t s = 0; s < steps && skew * s < key; ++s) n += umin(key - skew * s, loops);
+  return n;
+}
+
+AR_HD void ring_cell(uint64_t p, uint64_t loops, uint64_t steps, uint64_t window, uint64_t skew,
+                     uint64_t* loop, uint64_t* step) {
+  if (skew == 0) {
+    const uint64_t per_window = steps * window;
+    const uint64_t w = p / per_window, r = p % per_window;
+    const uint64_t first = w * window;
+    const uint64_t width = umin(window, loops - first);  // the last window may be narrower
+    *step = r / width;
+    *loop = first + r % width;
+    return;
+  }
+  uint64_t lo = 0, hi = loops + skew * (steps - 1);  // largest key with cells_below(key) <= p
+  while (hi - lo > 1) {
+    const uint64_t mid = (lo + hi) / 2;
+    if (ring_cells_below(mid, loops, steps, skew) <= p) lo = mid; else hi = mid;
+  }
+  const uint64_t key = lo;
+  const uint64_t s_lo = key + 1 > loops ? (key + 1 - loops + skew - 1) / skew : 0;
+  const uint64_t s = s_lo + (p - ring_cells_below(key, loops, steps, skew));
+  *step = s;
+  *loop = key - skew * s;
 }
 
 AR_HD int32_t rank_mod(int64_t x, int32_t n) { return (int32_t)(((x % n) + n) % n); }
@@ -156,7 +180,7 @@ AR_HD Task decode(const Geometry& g, uint64_t t) {
     const uint64_t per_cell = (uint64_t)n * g.tiles;
     const uint64_t p = t / per_cell, rem = t % per_cell;
     uint64_t loop, step;
-    ring_cell(p, g.loops, (uint64_t)g.steps, g.window, &loop, &step);
+    ring_cell(p, g.loops, (uint64_t)g.steps, g.window, g.skew, &loop, &step);
     const uint64_t j = rem / g.tiles, kk = rem % g.tiles;
     k.block = j;
     k.step = (int32_t)step;

@@ -19,7 +19,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -45,17 +44,15 @@ WORKLOADS = {
     # integer path: N=8 int32, 64 MiB per rank
     "int32-64MiB-ring": dict(op="allreduce", nranks=8, bytes=64 << 20, dtype="i32", dist="int20",
                              algo="ring", proto="simple", chunk=512 << 10),
+    # calibration: one rank, whose all-reduce is a copy of 256 MiB (read S,
+    # write S); its counter readings scale the others' to bytes
+    "copy-256MiB": dict(op="allreduce", nranks=1, bytes=256 << 20, dtype="f32", dist="normal",
+                        algo="ring", proto="simple", chunk=0),
 }
+MALL_BYTES = 256 << 20
 DEFAULT_WORKLOAD = "grad-bucket-256MiB"
-KERNEL_SOURCES = ("csrc/kernels.hip", "csrc/device.hpp", "csrc/schedule.hpp", "csrc/plan.hpp")
 
-
-def kernel_hash():
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "all_reduce_reduction_rank_amd", rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+from all_reduce_reduction_rank_amd.profiling import kernel_hash  # noqa: E402
 
 
 def busbw_factor(op, n):
@@ -71,6 +68,10 @@ def counts(w):
     if w["op"] == "reduce_scatter":
         return per, n * per, per
     return per, per, n * per
+
+
+def traffic_name(workload, w):
+    return f"{workload}_{w['algo']}_{w['proto']}"
 
 
 def traffic_from_profile(name):
@@ -163,19 +164,22 @@ def main():
     if status[0] != "AR_OK":
         raise SystemExit(f"device error during warm-up: {status}")
     print(f"[bench] {args.workload}: warmup {args.warmup} done", file=sys.stderr, flush=True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one HIP event before every call and one after the last, all on the
+    # stream the kernels run on: the total gives the mean, the gaps each call
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        evs[i].record(stream)
         step()
-    ev1.record(stream)
+    evs[-1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     status = comm.check()
     if status[0] != "AR_OK":
         raise SystemExit(f"device error during the timed region: {status}")
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_call = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     print(f"[bench] timed {args.steps} steps: {ms:.4f} ms per call (wall {wall:.3f} s)", file=sys.stderr, flush=True)
 
     s = w["bytes"]
@@ -183,7 +187,7 @@ def main():
     plan = plan_bytes(n, op, count, dt, w["algo"], w["proto"], chunk_bytes=w["chunk"])
     algbw = s / t / 1e9
     achieved = plan["hbm"] / t / 1e9
-    traffic = traffic_from_profile(args.workload)
+    traffic = traffic_from_profile(traffic_name(args.workload, w))
     out = {
         "metric": "all-reduce algbw/busbw GB/s and % of HBM peak vs message size, N=8",
         "value": round(algbw, 3),
@@ -202,6 +206,9 @@ def main():
             "dist": w["dist"], "algo": w["algo"], "proto": w["proto"], "chunk_bytes": w["chunk"],
             "parallelism": f"{n} simulated ranks on 1 GPU",
         },
+        "us_median": round(per_call[len(per_call) // 2] * 1e3, 2),
+        "us_min": round(per_call[0] * 1e3, 2),
+        "cache_resident": 2 * n * s < 2 * MALL_BYTES,
         "algbw_GBps": round(algbw, 3),
         "busbw_GBps": round(algbw * busbw_factor(op, n), 3),
         "hbm_bytes_per_call": plan["hbm"],
@@ -215,6 +222,9 @@ def main():
         },
         "kernel_hash": kernel_hash(),
     }
+    if traffic:
+        out["hbm_measured_GBps"] = round(traffic / t / 1e9, 1)
+        out["hbm_measured_frac"] = round(traffic / t / 1e9 / HBM_PEAK_GBPS, 4)
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     comm.close()
