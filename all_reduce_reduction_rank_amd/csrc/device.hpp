@@ -303,26 +303,53 @@ __device__ __forceinline__ void raise_timeout(Ctl* c, int step, int rank) {
   __hip_atomic_store(&c->abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Every poll loop reads the shared abort word and the real-time clock only
+// once per POLL_CHECK_EVERY polls.  Both are slow to read (the abort word is
+// one address that every waiting wave shares; the clock is a scalar memory
+// message): read at every poll, they made each step of a small ring cost
+// 10-20 us.  A wait's time limit starts at its first check.
+constexpr uint32_t POLL_CHECK_EVERY = 64;
+enum PollState { POLL_GO = 0, POLL_ABORTED = 1, POLL_TIMED_OUT = 2 };
+
+struct PollClock {
+  uint32_t polls = 0;
+  bool started = false;
+  uint64_t t0 = 0;
+  __device__ __forceinline__ int tick(const KArgs& a) {
+    if (++polls % POLL_CHECK_EVERY) return POLL_GO;
+    if (ld_u32(&a.ctl->abort)) return POLL_ABORTED;
+    const uint64_t now = wall_clock64();
+    if (!started) { started = true; t0 = now; return POLL_GO; }
+    return (now - t0 > a.timeout) ? POLL_TIMED_OUT : POLL_GO;
+  }
+};
+
+// Sleep before the next poll of a wait that is not yet satisfied: from ~50 ns
+// doubling up to ~0.85 us (s_sleep counts 64 clocks per unit).  Every poll
+// loop backs off: a line or flag being polled sits in the same memory channel
+// as the producer's stores to it, and thousands of lanes re-polling at full
+// rate would queue ahead of those stores and starve the producers.
+__device__ __forceinline__ void poll_sleep(uint32_t& level) {
+  for (uint32_t i = 0; i < (1u << level); ++i) __builtin_amdgcn_s_sleep(2);
+  if (level < 4) ++level;
+}
+
 // Bounded spin of ONE thread until *f >= target.  Returns false if the call
-// is aborted (by this wait timing out or by another one).  Back-off doubles
-// the sleep up to ~1 us, and the shared abort word is read only every 8th
-// poll, so thousands of waiting workgroups do not flood one memory channel.
+// is aborted (by this wait timing out or by another one).
 __device__ __forceinline__ bool wait_ge(const uint64_t* f, uint64_t target, const KArgs& a, int step,
                                         int rank) {
   if (ld_flag(f) >= target) return true;
-  const uint64_t t0 = wall_clock64();
-  uint32_t polls = 0;
+  PollClock clock;
+  uint32_t level = 0;
   while (true) {
-    const uint32_t level = polls < 6 ? polls : 6;
-    for (uint32_t i = 0; i < (1u << level); ++i) __builtin_amdgcn_s_sleep(8);
+    poll_sleep(level);
     if (ld_flag(f) >= target) return true;
-    if ((++polls & 7) == 0) {
-      if (ld_u32(&a.ctl->abort)) { note_blocked(a.ctl, step, rank); return false; }
-      if (wall_clock64() - t0 > a.timeout) {
-        record_timeout(a.ctl, a.flags, f, ld_flag(f), target);
-        raise_timeout(a.ctl, step, rank);
-        return false;
-      }
+    const int st = clock.tick(a);
+    if (st == POLL_ABORTED) { note_blocked(a.ctl, step, rank); return false; }
+    if (st == POLL_TIMED_OUT) {
+      record_timeout(a.ctl, a.flags, f, ld_flag(f), target);
+      raise_timeout(a.ctl, step, rank);
+      return false;
     }
   }
 }

@@ -207,9 +207,10 @@ __device__ __forceinline__ void ll_pass(const KArgs& a, Terms terms, int nterms,
           ready = ready && (uint32_t)(got[u] >> 32) == flag;
         }
         if (!ready) {
-          const uint64_t t0 = wall_clock64();
+          PollClock clock;
+          uint32_t level = 0;
           while (true) {
-            __builtin_amdgcn_s_sleep(1);
+            poll_sleep(level);
             ready = true;
 #pragma unroll
             for (int u = 0; u < U_LL; ++u) {
@@ -218,8 +219,9 @@ __device__ __forceinline__ void ll_pass(const KArgs& a, Terms terms, int nterms,
               ready = ready && (uint32_t)(got[u] >> 32) == flag;
             }
             if (ready) break;
-            if (ld_u32(&a.ctl->abort)) { note_blocked(a.ctl, step, rank); break; }
-            if (wall_clock64() - t0 > a.timeout) { raise_timeout(a.ctl, step, rank); break; }
+            const int st = clock.tick(a);
+            if (st == POLL_ABORTED) { note_blocked(a.ctl, step, rank); break; }
+            if (st == POLL_TIMED_OUT) { raise_timeout(a.ctl, step, rank); break; }
           }
         }
 #pragma unroll
@@ -309,9 +311,10 @@ __device__ __forceinline__ void ll128_pass(const KArgs& a, Terms terms, int nter
             ready = ready && ld_flag((const uint64_t*)(tm.lines + line[u] * LL128_LINE + LL128_DATA)) == flag;
         }
         if (!ready) {
-          const uint64_t t0 = wall_clock64();
+          PollClock clock;
+          uint32_t level = 0;
           while (true) {
-            __builtin_amdgcn_s_sleep(1);
+            poll_sleep(level);
             ready = true;
 #pragma unroll
             for (int u = 0; u < U_LL128; ++u) {
@@ -320,8 +323,9 @@ __device__ __forceinline__ void ll128_pass(const KArgs& a, Terms terms, int nter
                         ld_flag((const uint64_t*)(tm.lines + line[u] * LL128_LINE + LL128_DATA)) == flag;
             }
             if (ready) break;
-            if (ld_u32(&a.ctl->abort)) { note_blocked(a.ctl, step, rank); break; }
-            if (wall_clock64() - t0 > a.timeout) { raise_timeout(a.ctl, step, rank); break; }
+            const int st = clock.tick(a);
+            if (st == POLL_ABORTED) { note_blocked(a.ctl, step, rank); break; }
+            if (st == POLL_TIMED_OUT) { raise_timeout(a.ctl, step, rank); break; }
           }
         }
         // Flags seen: read the payload at device scope.
@@ -615,6 +619,12 @@ __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
   uint32_t finished = 0;  // tasks this workgroup ran (diagnostics)
   bool more = true;
   while (more) {
+    // Every ticket, the first included, comes from the shared counter, so a
+    // workgroup takes work only once it is running.  Handing out the first
+    // batch by workgroup index instead deadlocks whenever fewer workgroups
+    // fit on the GPU than the occupancy estimate says: the running ones then
+    // take every later ticket and wait on tickets held by workgroups that
+    // cannot be dispatched until one of them exits.
     if (threadIdx.x == 0) {
       uint32_t t = 0xffffffffu;
       if (!ld_u32(&a.ctl->abort))
@@ -640,14 +650,20 @@ __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
       // thread 0's fetch never shares a divergent path with a task's tail.
       __syncthreads();
     }
+    // Tickets are handed out in increasing order: once a batch reaches the
+    // end, every later fetch would come back empty.
+    if (first >= ntasks || ntasks - first <= batch) more = false;
   }
   if (threadIdx.x == 0) {
+    // Relaxed is enough: every ticket fetch and the epoch load of this
+    // workgroup have returned before this add is issued, and the next call's
+    // kernel starts after this one's end-of-kernel cache write-back.
     __hip_atomic_fetch_add(&a.ctl->diag[5], (uint64_t)finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t d = __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t d = __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d == gridDim.x - 1) {  // last workgroup out: rearm for the next call
       __hip_atomic_store(&a.ctl->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&a.ctl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(&a.ctl->epoch, 1ull, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&a.ctl->epoch, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

@@ -39,24 +39,49 @@ def test_every_kernel_compiled(asm):
     assert len(_kernels(asm)) == 48
 
 
+def _label_of(line):
+    m = re.match(r"^\.(LBB\w+):", line)
+    return m.group(1) if m else None
+
+
 def test_ticket_fetch_and_barriers_share_one_loop(asm):
+    # The fetch must run once per iteration of the loop that holds the first
+    # barrier after it: either inside that loop, or in a block that the loop's
+    # back edge branches to and that falls through into the loop header (the
+    # layout the compiler picks when the first iteration skips the fetch).
     for m in _kernels(asm):
         name, body = m.group(1), m.group(2)
-        header = None
-        fetch_loop = barrier_loop = None
+        header = label = None
+        fetch_loop = fetch_label = barrier_loop = None
+        branches = []  # (loop of the branching block, target label)
         for line in body.split("\n"):
-            if line.startswith(".LBB"):
+            lab = _label_of(line)
+            if lab:
+                label = lab
+                header = None
+            if line.startswith(".LBB") or line.startswith("; %bb"):
                 h = re.search(r"Header=BB(\w+) Depth=(\d)", line)
                 if h:
                     header = h.groups()
                 elif "Loop Header" in line:
                     header = (line.split(":")[0][4:], re.search(r"Depth=(\d)", line).group(1))
-            if fetch_loop is None and re.search(r"global_atomic_add v\d+, v\d+, v\d+, s\[\d+:\d+\] sc0$", line):
-                fetch_loop = header
-            elif fetch_loop is not None and barrier_loop is None and "s_barrier" in line:
+                elif line.startswith("; %bb"):
+                    header = None
+            br = re.search(r"s_(?:c)?branch\w* \.(LBB\w+)$", line)
+            if br:
+                branches.append((header, br.group(1)))
+            if fetch_loop is None and fetch_label is None and \
+                    re.search(r"global_atomic_add v\d+, v\d+, v\d+, s\[\d+:\d+\] sc0$", line):
+                fetch_loop, fetch_label = header, label
+            elif (fetch_loop or fetch_label) and barrier_loop is None and "s_barrier" in line:
                 barrier_loop = header
-        assert fetch_loop is not None, name
-        assert barrier_loop == fetch_loop, f"{name}: first barrier in loop {barrier_loop}, fetch in {fetch_loop}"
+        assert fetch_label is not None or fetch_loop is not None, name
+        assert barrier_loop is not None, name
+        if fetch_loop is not None:
+            assert barrier_loop == fetch_loop, f"{name}: first barrier in loop {barrier_loop}, fetch in {fetch_loop}"
+        else:
+            assert (barrier_loop, fetch_label) in branches, \
+                f"{name}: fetch block {fetch_label} is not re-entered from loop {barrier_loop}"
 
 
 def _blocks_by_loop(body):
