@@ -16,6 +16,7 @@
 #include <stdlib.h>
 
 #include "device.hpp"
+#include "plan.hpp"
 
 namespace ar {
 
@@ -735,16 +736,16 @@ hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream) {
   if (!f) return hipErrorInvalidValue;
   const uint64_t cap = (uint64_t)resident_workgroups(f, device);
   KArgs b = a;
-  // Tickets per fetch: up to 4 when there are many tasks per workgroup.  The
-  // one-shot in-place barrier waits on LATER tickets of its group, so it
-  // must take them one at a time.
+  // Tickets per fetch (pick_batch).  The one-shot in-place barrier waits on
+  // LATER tickets of its group, so it must take them one at a time.
   const bool barrier = a.g.kind == K_ONESHOT && a.g.proto == PROTO_SIMPLE && a.g.in_place;
   static const int max_batch = [] {
     const char* e = getenv("AR_BATCH");
     const int v = e ? atoi(e) : 4;
     return v < 1 ? 1 : (v > 16 ? 16 : v);
   }();
-  b.batch = barrier ? 1u : (uint32_t)umax(1, umin((uint64_t)max_batch, a.g.ntasks / (8 * cap)));
+  static const bool forced = getenv("AR_BATCH") != nullptr;
+  b.batch = barrier ? 1u : (forced ? (uint32_t)max_batch : pick_batch(a.g, cap, (uint32_t)max_batch));
   uint64_t grid = umin(cdiv(a.g.ntasks, b.batch), cap);
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(f, dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, b);

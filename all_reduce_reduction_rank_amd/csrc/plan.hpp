@@ -39,15 +39,38 @@ struct Tuning {
 };
 
 // Tile size in bytes for a per-rank buffer of `rank_bytes`: aim for >= 128
-// tiles per rank so a call spreads over the 256 CUs, within the per-protocol
-// bounds (Simple up to 64 KiB on the ring, 128 KiB for the direct schedules,
-// whose tasks each do more flag work per byte; LL up to 16 KiB; LL128 whole
-// wave passes).
-inline uint64_t pick_tile_bytes(int proto, uint64_t rank_bytes, bool inplace_oneshot, bool ring) {
+// tiles per rank so a call spreads over the 256 CUs, within per-schedule
+// bounds.  Simple: 32 KiB on the ring and two-shot (measured at 256 MiB,
+// N=8 fp32: ring 0.87 of HBM peak at 32 KiB against 0.79 at 64 KiB and 0.72
+// at 128 KiB; two-shot equal at 32 and 128 KiB, and 23% faster at 25 MiB
+// with 32 KiB), 128 KiB for one-shot (each task reads N tiles) and the
+// direct reduce-scatter / all-gather, 16 KiB for the in-place one-shot (its
+// tile lives in registers).  LL up to 16 KiB; LL128 whole wave passes.
+inline uint64_t pick_tile_bytes(int proto, uint64_t rank_bytes, int kind, bool in_place) {
   const uint64_t want = floor_pow2(rank_bytes / 128 + 1);
-  if (proto == PROTO_SIMPLE) return clampu(want, 4096, inplace_oneshot ? 16384 : (ring ? 65536 : 131072));
+  if (proto == PROTO_SIMPLE) {
+    uint64_t hi = 131072;
+    if (kind == K_RING || kind == K_TWOSHOT) hi = 32768;
+    if (kind == K_ONESHOT && in_place) hi = 16384;
+    return clampu(want, 4096, hi);
+  }
   if (proto == PROTO_LL) return clampu(want, 4096, 16384);
   return LL128_TILE_UNIT * clampu(floor_pow2(want / LL128_TILE_UNIT + 1), 1, 4);
+}
+
+// Tickets a workgroup takes per fetch.  Every fetch is an atomic on one
+// counter, which serializes at about one per ~10 ns: a 256 MiB ring with
+// 16 KiB tiles and one ticket per fetch spends more time in the counter than
+// in HBM (0.43 of peak).  A fetch should cover about 64 KiB of tiles, and a
+// workgroup should still see >= 8 fetches, so work stays balanced.
+constexpr uint64_t BYTES_PER_FETCH = 65536;
+inline uint32_t pick_batch(const Geometry& g, uint64_t resident, uint32_t max_batch) {
+  const uint64_t tile_b = g.proto == PROTO_SIMPLE ? g.tile * (uint64_t)g.esize
+                                                  : g.tile_lines * (uint64_t)g.line_bytes;
+  uint64_t b = tile_b ? BYTES_PER_FETCH / tile_b : 1;
+  b = clampu(b, 1, max_batch);
+  const uint64_t spread = resident ? g.ntasks / (8 * resident) : 1;
+  return (uint32_t)clampu(b, 1, spread > 0 ? spread : 1);
 }
 
 // Fill g for one call.  Returns false on an invalid combination.
@@ -80,7 +103,7 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
     g.line_bytes = 0;
     g.total = count;
     g.block = count;
-    g.tile = pick_tile_bytes(PROTO_SIMPLE, count * es, false, false) / es;
+    g.tile = pick_tile_bytes(PROTO_SIMPLE, count * es, K_COPY, false) / es;
     g.tiles = cdiv(count, g.tile);
     g.ntasks = (op == OP_ALLREDUCE && in_place) ? 0 : g.tiles;
     *out = g;
@@ -93,7 +116,7 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
 
   const bool lines = proto != PROTO_SIMPLE;
   const uint64_t rank_bytes = g.total * es;
-  uint64_t tile_b = pick_tile_bytes(proto, rank_bytes, g.kind == K_ONESHOT && in_place && !lines, g.kind == K_RING);
+  uint64_t tile_b = pick_tile_bytes(proto, rank_bytes, g.kind, in_place != 0);
   if (tune.tile_bytes && !lines && !(g.kind == K_ONESHOT && in_place))
     tile_b = clampu(tune.tile_bytes / 16 * 16, 4096, 512 * 1024);
 
