@@ -5,10 +5,11 @@ supplies device memory (tensors) and the stream.  The entry points keep the
 C names (``include/ar.h``):
 
     comm = Comm(nranks, max_bytes_per_rank, max_line_bytes_per_rank)
-    comm.allreduce(send, recv, algo="ring", proto="simple", chunk_bytes=0)
+    comm.allreduce(send, recv, algo="ring", proto="simple", chunk_bytes=0)   # or "auto"
     comm.reduce_scatter(send, recv, ...)
     comm.allgather(send, recv, ...)
     plan_bytes(nranks, op, count, dtype, algo, proto, ...)
+    select(nranks, op, count, dtype, algo="auto", proto="auto", max_line_bytes_per_rank=0)
 
 ``send`` / ``recv`` are lists of N contiguous CUDA (HIP) tensors on the
 communicator's device.  If the library is missing it is built once with hipcc;
@@ -25,6 +26,7 @@ LIB_PATH = os.environ.get("AR_LIBRARY") or os.path.join(HERE, "libar.so")
 OPS = {"allreduce": 0, "reduce_scatter": 1, "allgather": 2}
 ALGOS = {"oneshot": 0, "twoshot": 1, "ring": 2}
 PROTOS = {"simple": 0, "ll": 1, "ll128": 2}
+AUTO = 3  # AR_ALGO_AUTO / AR_PROTO_AUTO: the library picks (ar_select)
 DTYPES = {"f32": 0, "bf16": 1, "i32": 2}
 ESIZE = {"f32": 4, "bf16": 2, "i32": 4}
 
@@ -37,7 +39,7 @@ STATUS = {
 SYMBOLS = (
     "ar_comm_create", "ar_comm_destroy", "ar_comm_check", "ar_comm_reset",
     "ar_comm_workspace_bytes", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
-    "ar_plan_bytes", "ar_debug_inject", "ar_debug_state", "ar_status_string",
+    "ar_plan_bytes", "ar_select", "ar_debug_inject", "ar_debug_state", "ar_status_string",
 )
 
 
@@ -63,6 +65,8 @@ def _declare(lib):
         getattr(lib, name).argtypes = [P, PP, PP, S, I, I, I, S, P]
     lib.ar_plan_bytes.argtypes = [I, I, S, I, I, I, S, I, ctypes.POINTER(U64), ctypes.POINTER(U64),
                                   ctypes.POINTER(U64), ctypes.POINTER(U64)]
+    lib.ar_select.argtypes = [I, I, S, I, I, I, S, ctypes.POINTER(I), ctypes.POINTER(I),
+                              ctypes.POINTER(ctypes.c_double)]
     lib.ar_debug_inject.argtypes = [P, I, I, U64]
     lib.ar_debug_state.argtypes = [P, P, ctypes.POINTER(U64), I]
     lib.ar_status_string.argtypes = [I]
@@ -91,6 +95,14 @@ def library():
 def _check(status, what):
     if status != 0:
         raise ARError(status, what)
+
+
+def _algo(name):
+    return AUTO if name == "auto" else ALGOS[name]
+
+
+def _proto(name):
+    return AUTO if name == "auto" else PROTOS[name]
 
 
 def _dtype_name(t):
@@ -154,7 +166,7 @@ class Comm:
             if _dtype_name(t) != dt:
                 raise TypeError("all rank buffers must share one dtype")
         s, r = _ptrs(send, self.nranks, self.device), _ptrs(recv, self.nranks, self.device)
-        status = getattr(_lib(), name)(self._h, s, r, count, DTYPES[dt], ALGOS[algo], PROTOS[proto],
+        status = getattr(_lib(), name)(self._h, s, r, count, DTYPES[dt], _algo(algo), _proto(proto),
                                        chunk_bytes, _stream_handle(stream))
         _check(status, name)
 
@@ -193,6 +205,17 @@ class Comm:
 
     def inject(self, rank: int, step: int, timeout_us: int = 0):
         _check(_lib().ar_debug_inject(self._h, rank, step, timeout_us), "ar_debug_inject")
+
+
+def select(nranks, op, count, dtype, algo="auto", proto="auto", max_line_bytes_per_rank=0):
+    """The library's choice for a call: (algo, proto, predicted_us)."""
+    a, p, t = ctypes.c_int(), ctypes.c_int(), ctypes.c_double()
+    _check(_lib().ar_select(nranks, OPS[op], count, DTYPES[dtype], _algo(algo), _proto(proto),
+                            max_line_bytes_per_rank, ctypes.byref(a), ctypes.byref(p), ctypes.byref(t)),
+           "ar_select")
+    names_a = {v: k for k, v in ALGOS.items()}
+    names_p = {v: k for k, v in PROTOS.items()}
+    return names_a[a.value], names_p[p.value], t.value
 
 
 def plan_bytes(nranks, op, count, dtype, algo, proto, chunk_bytes=0, in_place=False):

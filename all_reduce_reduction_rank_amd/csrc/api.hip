@@ -184,6 +184,27 @@ ar_status ar_debug_inject(ar_comm_t c, int rank, int step, uint64_t timeout_us) 
   return AR_OK;
 }
 
+ar_status ar_select(int nranks, ar_op op, size_t count, ar_dtype dtype, ar_algo algo, ar_proto proto,
+                    size_t max_line_bytes_per_rank, ar_algo* chosen_algo, ar_proto* chosen_proto,
+                    double* predicted_us) {
+  if (!chosen_algo || !chosen_proto) return AR_ERR_INVALID;
+  if ((int)op < 0 || (int)op > 2 || (int)dtype < 0 || (int)dtype > 2) return AR_ERR_INVALID;
+  if (nranks < 1 || nranks > MAX_RANKS) return AR_ERR_INVALID;
+  const uint64_t es = (uint64_t)esize_of((int)dtype);
+  const uint64_t in_bytes = ((int)op == OP_REDUCE_SCATTER ? (uint64_t)nranks * count : count) * es;
+  const uint64_t out_bytes = ((int)op == OP_ALLGATHER ? (uint64_t)nranks * count : count) * es;
+  const uint64_t rank_bytes = umax(in_bytes, out_bytes);
+  int a = 0, p = 0;
+  double t = -1.0;
+  if (!select_schedule((int)op, nranks, (int)dtype, rank_bytes, (int)algo, (int)proto,
+                       nranks > 1 && rank_bytes <= max_line_bytes_per_rank, &a, &p, &t))
+    return AR_ERR_INVALID;
+  *chosen_algo = (ar_algo)a;
+  *chosen_proto = (ar_proto)p;
+  if (predicted_us) *predicted_us = t;
+  return AR_OK;
+}
+
 ar_status ar_plan_bytes(int nranks, ar_op op, size_t count, ar_dtype dtype, ar_algo algo, ar_proto proto,
                         size_t chunk_bytes, int in_place, uint64_t* hbm_read, uint64_t* hbm_write,
                         uint64_t* link_bytes, uint64_t* ntasks) {
@@ -211,7 +232,8 @@ static ar_status run(ar_comm_t c, int op, const void* const* send, void* const* 
                      int dtype, int algo, int proto, uint64_t chunk_bytes, ar_stream_t stream) {
   if (!c || !send || !recv) return AR_ERR_INVALID;
   if (c->broken) return AR_ERR_BROKEN;
-  if (dtype < 0 || dtype > 2 || algo < 0 || algo > 2 || proto < 0 || proto > 2) return AR_ERR_INVALID;
+  if (dtype < 0 || dtype > 2 || algo < 0 || algo > ALGO_AUTO || proto < 0 || proto > PROTO_AUTO)
+    return AR_ERR_INVALID;
   if (count == 0) return AR_OK;  // nothing to move; buffers may be null
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != c->device) return AR_ERR_INVALID;
@@ -220,8 +242,14 @@ static ar_status run(ar_comm_t c, int op, const void* const* send, void* const* 
   const uint64_t in_bytes = (op == OP_REDUCE_SCATTER ? (uint64_t)n * count : count) * es;
   const uint64_t out_bytes = (op == OP_ALLGATHER ? (uint64_t)n * count : count) * es;
   if (count > (1ull << 40)) return AR_ERR_TOO_LARGE;
-  if (umax(in_bytes, out_bytes) > c->max_bytes) return AR_ERR_TOO_LARGE;
-  if (proto != PROTO_SIMPLE && n > 1 && umax(in_bytes, out_bytes) > c->max_line_bytes) return AR_ERR_TOO_LARGE;
+  const uint64_t rank_bytes = umax(in_bytes, out_bytes);
+  if (rank_bytes > c->max_bytes) return AR_ERR_TOO_LARGE;
+  if (algo == ALGO_AUTO || proto == PROTO_AUTO) {
+    const bool line_ok = n > 1 && rank_bytes <= c->max_line_bytes;
+    if (!select_schedule(op, n, dtype, rank_bytes, algo, proto, line_ok, &algo, &proto, nullptr))
+      return AR_ERR_INVALID;
+  }
+  if (proto != PROTO_SIMPLE && n > 1 && rank_bytes > c->max_line_bytes) return AR_ERR_TOO_LARGE;
 
   int in_place = 0, same = 0;
   for (int r = 0; r < n; ++r) {

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "schedule.hpp"
+#include "tuning_table.hpp"
 
 namespace ar {
 
@@ -29,6 +30,73 @@ constexpr uint64_t LL128_TILE_UNIT = 3840;  // 32 lines of 120 payload bytes: on
 constexpr uint64_t LL128_ALIGN = 240;       // 2 lines: a multiple of 16 bytes and of 120 bytes
 
 inline int esize_of(int dtype) { return dtype == DT_BF16 ? 2 : 4; }
+
+// AR_ALGO_AUTO / AR_PROTO_AUTO in the C ABI.
+constexpr int ALGO_AUTO = 3;
+constexpr int PROTO_AUTO = 3;
+constexpr uint64_t MALL_BYTES = 256ull << 20;
+
+// Fitted time (us) of one call with S = `rank_bytes` per rank, from the
+// measured cost table: t = alpha + S * gamma, alpha and gamma interpolated
+// linearly in N between the rank counts measured (clamped outside them).
+// The cache band is 0 when the call's inputs and outputs fit in the MALL
+// (2 N S <= 256 MiB).  Reduce-scatter and all-gather use the all-reduce fits
+// of the same algorithm and protocol when none of their own were measured.
+// Negative when the table has nothing for this combination.
+inline double predict_us(int op, int nranks, int esize, int algo, int proto, uint64_t rank_bytes) {
+  const int band = 2ull * (uint64_t)nranks * rank_bytes <= MALL_BYTES ? 0 : 1;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int o = pass == 0 ? op : OP_ALLREDUCE;
+    int lo = -1, hi = -1;
+    for (int i = 0; i < N_COST_FITS; ++i) {
+      const CostFit& f = COST_FITS[i];
+      if (f.op != o || f.esize != esize || f.algo != algo || f.proto != proto || f.band != band) continue;
+      if (f.nranks <= nranks && (lo < 0 || f.nranks > COST_FITS[lo].nranks)) lo = i;
+      if (f.nranks >= nranks && (hi < 0 || f.nranks < COST_FITS[hi].nranks)) hi = i;
+    }
+    if (lo < 0 && hi < 0) continue;
+    if (lo < 0) lo = hi;
+    if (hi < 0) hi = lo;
+    const CostFit& a = COST_FITS[lo];
+    const CostFit& b = COST_FITS[hi];
+    const double w = b.nranks == a.nranks ? 0.0 : double(nranks - a.nranks) / double(b.nranks - a.nranks);
+    const double alpha = a.alpha_us + w * (b.alpha_us - a.alpha_us);
+    const double gamma = a.us_per_byte + w * (b.us_per_byte - a.us_per_byte);
+    return alpha + gamma * (double)rank_bytes;
+  }
+  return -1.0;
+}
+
+// Resolve ALGO_AUTO / PROTO_AUTO to the candidate with the smallest fitted
+// time (fixed choices are kept).  LL and LL128 are candidates only when
+// `line_ok` (the message fits the communicator's line staging).  On ties, or
+// with no fit at all, the earlier candidate wins: Simple before LL before
+// LL128, one-shot before two-shot before ring.  Returns false on a bad
+// argument.
+inline bool select_schedule(int op, int nranks, int dtype, uint64_t rank_bytes, int algo, int proto,
+                            bool line_ok, int* out_algo, int* out_proto, double* out_us) {
+  if (op < 0 || op > 2 || dtype < 0 || dtype > 2 || nranks < 1 || nranks > MAX_RANKS) return false;
+  if (algo < 0 || algo > ALGO_AUTO || proto < 0 || proto > PROTO_AUTO) return false;
+  int best_a = algo == ALGO_AUTO ? ALGO_ONESHOT : algo;
+  int best_p = proto == PROTO_AUTO ? PROTO_SIMPLE : proto;
+  double best_t = -1.0;
+  for (int a = 0; a < 3; ++a) {
+    if (algo != ALGO_AUTO && a != algo) continue;
+    // reduce-scatter / all-gather: two-shot names the same direct schedule
+    if (algo == ALGO_AUTO && op != OP_ALLREDUCE && a == ALGO_TWOSHOT) continue;
+    for (int p = 0; p < 3; ++p) {
+      if (proto != PROTO_AUTO && p != proto) continue;
+      if (proto == PROTO_AUTO && p != PROTO_SIMPLE && !line_ok) continue;
+      const double t = predict_us(op, nranks, esize_of(dtype), a, p, rank_bytes);
+      if (t < 0) continue;
+      if (best_t < 0 || t < best_t) { best_t = t; best_a = a; best_p = p; }
+    }
+  }
+  *out_algo = best_a;
+  *out_proto = best_p;
+  if (out_us) *out_us = best_t;
+  return true;
+}
 
 // Tuning knobs (no effect on results): 0 keeps the built-in choice.
 struct Tuning {

@@ -8,7 +8,7 @@ Each point is timed over at least 20 calls and 200 ms after 2 warm-up calls
 (one event per call: median and minimum), and below 1 MiB also as a replay
 of a HIP graph of 100 captured calls, which removes the host's launch cost.
 
-    python -m all_reduce_reduction_rank_amd.sweep run --out sweep.jsonl [--n 2 4 8] [--dtype bf16 f32]
+    python -m all_reduce_reduction_rank_amd.sweep run --out sweep.jsonl [--op allreduce] [--n 2 4 8] [--dtype bf16 f32]
     python -m all_reduce_reduction_rank_amd.sweep summary sweep.jsonl
 
 ``run`` writes one JSON object per point as it goes; ``summary`` prints the
@@ -69,12 +69,18 @@ def _time_graph(call, stream, reps=100):
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
-def run(out_path, ns, dtypes, sizes=SIZES, graphs=True):
+def run(out_path, ns, dtypes, sizes=SIZES, graphs=True, op="allreduce"):
+    """Time every (algorithm, protocol) at every size.  S = `bytes` is the
+    full per-rank buffer: a reduce-scatter sends S and keeps S/N, an
+    all-gather sends S/N and receives S (sizes whose shard is under one
+    element are skipped).  For reduce-scatter and all-gather one-shot and
+    two-shot name the same direct schedule, so only one-shot is timed."""
     import torch
 
     from . import Comm, inputs
 
     torch.cuda.set_device(0)
+    algos = ALGOS if op == "allreduce" else ("oneshot", "ring")
     with open(out_path, "a") as out:
         for n in ns:
             for dt in dtypes:
@@ -85,13 +91,21 @@ def run(out_path, ns, dtypes, sizes=SIZES, graphs=True):
                 comm = Comm(n, top, top)
                 side = torch.cuda.Stream()
                 for nbytes in sizes:
-                    count = nbytes // es
-                    s_in = [t[:count] for t in send]
-                    s_out = [t[:count] for t in recv]
-                    for algo in ALGOS:
+                    full = nbytes // es
+                    shard = full // n
+                    if op == "allreduce":
+                        count, s_in, s_out = full, [t[:full] for t in send], [t[:full] for t in recv]
+                    elif shard == 0:
+                        continue
+                    elif op == "reduce_scatter":
+                        count, s_in, s_out = shard, [t[:n * shard] for t in send], [t[:shard] for t in recv]
+                    else:
+                        count, s_in, s_out = shard, [t[:shard] for t in send], [t[:n * shard] for t in recv]
+                    fn = getattr(comm, op)
+                    for algo in algos:
                         for proto in PROTOS:
                             def call():
-                                comm.allreduce(s_in, s_out, algo=algo, proto=proto, stream=side)
+                                fn(s_in, s_out, algo=algo, proto=proto, stream=side)
 
                             with torch.cuda.stream(side):
                                 rec = _time_calls(call, side)
@@ -99,12 +113,12 @@ def run(out_path, ns, dtypes, sizes=SIZES, graphs=True):
                                     rec["us_graph"] = _time_graph(call, side)
                             st = comm.check(side)
                             if st[0] != "AR_OK":
-                                raise SystemExit(f"device error at N={n} {dt} {nbytes} B {algo}/{proto}: {st}")
-                            rec.update(n=n, dtype=dt, bytes=nbytes, algo=algo, proto=proto,
+                                raise SystemExit(f"device error at {op} N={n} {dt} {nbytes} B {algo}/{proto}: {st}")
+                            rec.update(op=op, n=n, dtype=dt, bytes=nbytes, algo=algo, proto=proto,
                                        cache_resident=2 * n * nbytes < 2 * MALL_BYTES)
                             out.write(json.dumps(rec) + "\n")
                             out.flush()
-                    print(f"[sweep] N={n} {dt} {nbytes} B done", file=sys.stderr, flush=True)
+                    print(f"[sweep] {op} N={n} {dt} {nbytes} B done", file=sys.stderr, flush=True)
                 comm.close()
                 del send, recv, s_in, s_out
                 torch.cuda.empty_cache()
@@ -121,21 +135,37 @@ def best_time(rec):
     return rec.get("us_graph", rec["us_median"])
 
 
-def summary(recs):
+def summary(recs, table_ranks=None):
+    """Markdown: per (operation, N, dtype) the crossover sizes, and the full
+    timing table where N is in `table_ranks` (None: every N)."""
     lines = []
-    keys = sorted({(r["n"], r["dtype"]) for r in recs})
-    for n, dt in keys:
-        rows = [r for r in recs if r["n"] == n and r["dtype"] == dt]
+    keys = sorted({(r.get("op", "allreduce"), r["n"], r["dtype"]) for r in recs})
+    for op, n, dt in keys:
+        rows = [r for r in recs if r.get("op", "allreduce") == op and r["n"] == n and r["dtype"] == dt]
         sizes = sorted({r["bytes"] for r in rows})
-        lines.append(f"\n### N={n}, {dt}\n")
-        lines.append("| bytes/rank | " + " | ".join(f"{a}/{p}" for a in ALGOS for p in PROTOS) + " | fastest |")
-        lines.append("|---:|" + "---:|" * (len(ALGOS) * len(PROTOS)) + "---|")
+        algos = [a for a in ALGOS if any(r["algo"] == a for r in rows)]
+        lines.append(f"\n### {op}, N={n}, {dt} (µs per call)\n")
+        if table_ranks is None or n in table_ranks:
+            lines.append("| bytes/rank | " + " | ".join(f"{a}/{p}" for a in algos for p in PROTOS) + " | fastest |")
+            lines.append("|---:|" + "---:|" * (len(algos) * len(PROTOS)) + "---|")
         for s in sizes:
+            if table_ranks is not None and n not in table_ranks:
+                break
             t = {(r["algo"], r["proto"]): best_time(r) for r in rows if r["bytes"] == s}
             fast = min(t, key=t.get)
-            cells = [f"{t[(a, p)]:.1f}" if (a, p) in t else "" for a in ALGOS for p in PROTOS]
+            cells = [f"{t[(a, p)]:.1f}" if (a, p) in t else "" for a in algos for p in PROTOS]
             lines.append(f"| {s} | " + " | ".join(cells) + f" | {fast[0]}/{fast[1]} |")
         lines.append("")
+        t_all = {}
+        for r in rows:
+            t_all.setdefault(r["bytes"], {})[(r["algo"], r["proto"])] = best_time(r)
+        prev, cross = None, []
+        for s in sizes:
+            k = min(t_all[s], key=t_all[s].get)
+            if k != prev:
+                cross.append(f"{k[0]}/{k[1]} from {s} B")
+                prev = k
+        lines.append("- fastest overall: " + ", ".join(cross))
         for p in PROTOS:
             prev, cross = None, []
             for s in sizes:
@@ -157,13 +187,16 @@ def main():
     r.add_argument("--dtype", nargs="+", default=["bf16", "f32"])
     r.add_argument("--max-bytes", type=int, default=1 << 30)
     r.add_argument("--no-graphs", action="store_true")
+    r.add_argument("--op", default="allreduce", choices=("allreduce", "reduce_scatter", "allgather"))
     s = sub.add_parser("summary")
     s.add_argument("path")
+    s.add_argument("--tables", type=int, nargs="*", help="rank counts that get a full table (default: all)")
     args = ap.parse_args()
     if args.what == "run":
-        run(args.out, args.n, args.dtype, [x for x in SIZES if x <= args.max_bytes], graphs=not args.no_graphs)
+        run(args.out, args.n, args.dtype, [x for x in SIZES if x <= args.max_bytes], graphs=not args.no_graphs,
+            op=args.op)
     else:
-        print(summary(load(args.path)))
+        print(summary(load(args.path), args.tables))
 
 
 if __name__ == "__main__":

@@ -127,8 +127,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
-    ap.add_argument("--algo", choices=("oneshot", "twoshot", "ring"))
-    ap.add_argument("--proto", choices=("simple", "ll", "ll128"))
+    ap.add_argument("--algo", choices=("oneshot", "twoshot", "ring", "auto"))
+    ap.add_argument("--proto", choices=("simple", "ll", "ll128", "auto"))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample length; 0 skips it")
     args = ap.parse_args()
 
@@ -139,7 +139,7 @@ def main():
 
     import torch
 
-    from all_reduce_reduction_rank_amd import Comm, inputs, plan_bytes
+    from all_reduce_reduction_rank_amd import Comm, inputs, plan_bytes, select
 
     w = dict(WORKLOADS[args.workload])
     if args.algo:
@@ -149,14 +149,19 @@ def main():
     n, dt, op = w["nranks"], w["dtype"], w["op"]
     torch.cuda.set_device(0)
     count, n_in, n_out = counts(w)
+    auto = "auto" in (w["algo"], w["proto"])
+    line_cap = w["bytes"] if w["proto"] != "simple" else 0
+    req_algo, req_proto = w["algo"], w["proto"]  # what each timed call asks for
+    if auto:  # the library's choice (ar_select), resolved here for the report
+        w["algo"], w["proto"], _ = select(n, op, count, dt, w["algo"], w["proto"], line_cap)
     send = inputs.device_rank_inputs(n, n_in, dt, w["dist"], seed=0, cfg=4)
     recv = [torch.empty(n_out, dtype=send[0].dtype, device="cuda") for _ in range(n)]
-    comm = Comm(n, w["bytes"], w["bytes"] if w["proto"] != "simple" else 0)
+    comm = Comm(n, w["bytes"], line_cap)
     call = getattr(comm, op)
     stream = torch.cuda.current_stream()
 
     def step():
-        call(send, recv, algo=w["algo"], proto=w["proto"], chunk_bytes=w["chunk"], stream=stream)
+        call(send, recv, algo=req_algo, proto=req_proto, chunk_bytes=w["chunk"], stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -204,6 +209,7 @@ def main():
         "config": {
             "workload": args.workload, "op": op, "nranks": n, "bytes_per_rank": s, "dtype": dt,
             "dist": w["dist"], "algo": w["algo"], "proto": w["proto"], "chunk_bytes": w["chunk"],
+            "selection": "auto" if auto else "fixed",
             "parallelism": f"{n} simulated ranks on 1 GPU",
         },
         "us_median": round(per_call[len(per_call) // 2] * 1e3, 2),

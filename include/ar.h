@@ -68,11 +68,11 @@ typedef enum { AR_F32 = 0, AR_BF16 = 1, AR_I32 = 2 } ar_dtype;
 
 /* [H] "Algorithms".  For reduce-scatter and all-gather, ONESHOT and TWOSHOT
  * both name the direct schedule (one exchange: every rank reads its slices
- * straight from every rank). */
-typedef enum { AR_ONESHOT = 0, AR_TWOSHOT = 1, AR_RING = 2 } ar_algo;
+ * straight from every rank).  AR_ALGO_AUTO: the library picks (ar_select). */
+typedef enum { AR_ONESHOT = 0, AR_TWOSHOT = 1, AR_RING = 2, AR_ALGO_AUTO = 3 } ar_algo;
 
-/* [H] "Protocols". */
-typedef enum { AR_SIMPLE = 0, AR_LL = 1, AR_LL128 = 2 } ar_proto;
+/* [H] "Protocols".  AR_PROTO_AUTO: the library picks (ar_select). */
+typedef enum { AR_SIMPLE = 0, AR_LL = 1, AR_LL128 = 2, AR_PROTO_AUTO = 3 } ar_proto;
 
 typedef enum { AR_OP_ALLREDUCE = 0, AR_OP_REDUCE_SCATTER = 1, AR_OP_ALLGATHER = 2 } ar_op;
 
@@ -149,6 +149,25 @@ ar_status ar_reduce_scatter(ar_comm_t comm, const void* const* sendbufs, void* c
 ar_status ar_allgather(ar_comm_t comm, const void* const* sendbufs, void* const* recvbufs,
                        size_t sendcount, ar_dtype dtype, ar_algo algo, ar_proto proto,
                        size_t chunk_bytes, ar_stream_t stream);
+
+/* Host-only choice of algorithm and protocol ([H] "Algorithms": the latency
+ * plus bytes-over-bandwidth model, t = alpha + S / beta, decides which
+ * algorithm and protocol win at which message size).  alpha and beta are
+ * fitted per (operation, N, element size, algorithm, protocol) to a
+ * message-size sweep measured on MI355X, separately for calls whose inputs
+ * and outputs fit in the 256 MB MALL (2 N S <= 256 MiB) and for larger ones;
+ * S = bytes per rank (the larger of a rank's send and receive buffers).
+ * Rank counts between the measured ones (2, 4, 8) interpolate linearly.
+ * `algo` / `proto` may each be a fixed value (kept) or AUTO (chosen).  LL
+ * and LL128 are candidates only when S <= max_line_bytes_per_rank (the
+ * communicator's line capacity; 0 = none) and N > 1.  The calls resolve
+ * AUTO the same way with their communicator's capacity.  Fills
+ * chosen_algo / chosen_proto (required) and predicted_us (may be NULL; a
+ * negative value means no fit covered the choice).  `count` has the same
+ * meaning as in the call for `op`.  Errors: AR_ERR_INVALID. */
+ar_status ar_select(int nranks, ar_op op, size_t count, ar_dtype dtype, ar_algo algo, ar_proto proto,
+                    size_t max_line_bytes_per_rank, ar_algo* chosen_algo, ar_proto* chosen_proto,
+                    double* predicted_us);
 
 /* Host-only accounting of one call's schedule (no device work; works
  * without a GPU).  `count` has the same meaning as in the call for `op`.

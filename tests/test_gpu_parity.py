@@ -296,3 +296,42 @@ def test_withheld_signal_times_out_and_names_the_blocked_rank(algo, n, rank, ste
     assert_same(to_host(run_ok[0], "f32"), want[0], "after reset")
     assert c.check()[0] == "AR_OK"
     c.close()
+
+
+# ------------------------------------------------------ automatic choice
+@pytest.mark.parametrize("n", [2, 3, 8])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "i32"])
+def test_auto_choice_matches_the_oracle_of_the_chosen_schedule(n, dt):
+    from all_reduce_reduction_rank_amd import select
+
+    c = comm(n)
+    for count in (3, 4096, 70001, 1 << 18):
+        host = inputs.rank_inputs(n, count, dt, _dist(dt), seed=count, cfg=40)
+        send = [to_dev(x, dt) for x in host]
+        recv = [empty(count, dt) for _ in range(n)]
+        algo, proto, _ = select(n, "allreduce", count, dt, max_line_bytes_per_rank=LINE_BYTES)
+        print("CASE auto", n, dt, count, algo, proto, flush=True, file=sys.stderr)
+        c.allreduce(send, recv, algo="auto", proto="auto")
+        torch.cuda.synchronize()
+        want = C.allreduce(host, dt, algo)
+        for r in range(n):
+            assert_same(to_host(recv[r], dt), want[r], f"auto ({algo}/{proto}) N={n} {dt} count={count} rank {r}")
+    assert c.check()[0] == "AR_OK"
+
+
+@pytest.mark.parametrize("op", ["reduce_scatter", "allgather"])
+def test_auto_choice_for_reduce_scatter_and_all_gather(op):
+    from all_reduce_reduction_rank_amd import select
+
+    n, dt, cnt = 4, "f32", 5000
+    c = comm(n)
+    total = n * cnt
+    host = inputs.rank_inputs(n, total if op == "reduce_scatter" else cnt, dt, "normal", seed=5, cfg=41)
+    send = [to_dev(x, dt) for x in host]
+    recv = [empty(cnt if op == "reduce_scatter" else total, dt) for _ in range(n)]
+    algo, proto, _ = select(n, op, cnt, dt, max_line_bytes_per_rank=LINE_BYTES)
+    getattr(c, op)(send, recv, algo="auto", proto="auto")
+    torch.cuda.synchronize()
+    want = getattr(C, op)(host, dt, algo)
+    for r in range(n):
+        assert_same(to_host(recv[r], dt), want[r], f"auto {op} ({algo}/{proto}) rank {r}")
