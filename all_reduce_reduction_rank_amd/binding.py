@@ -38,7 +38,7 @@ STATUS = {
 # Every symbol include/ar.h declares.
 SYMBOLS = (
     "ar_comm_create", "ar_comm_destroy", "ar_comm_check", "ar_comm_reset",
-    "ar_comm_workspace_bytes", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
+    "ar_comm_workspace_bytes", "ar_comm_set_max_workgroups", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
     "ar_plan_bytes", "ar_select", "ar_debug_inject", "ar_debug_state", "ar_status_string",
 )
 
@@ -61,6 +61,7 @@ def _declare(lib):
     lib.ar_comm_reset.argtypes = [P, P]
     lib.ar_comm_workspace_bytes.argtypes = [P]
     lib.ar_comm_workspace_bytes.restype = S
+    lib.ar_comm_set_max_workgroups.argtypes = [P, ctypes.c_uint]
     for name in ("ar_allreduce", "ar_reduce_scatter", "ar_allgather"):
         getattr(lib, name).argtypes = [P, PP, PP, S, I, I, I, S, P]
     lib.ar_plan_bytes.argtypes = [I, I, S, I, I, I, S, I, ctypes.POINTER(U64), ctypes.POINTER(U64),
@@ -159,6 +160,10 @@ class Comm:
     @property
     def workspace_bytes(self) -> int:
         return _lib().ar_comm_workspace_bytes(self._h)
+
+    def set_max_workgroups(self, max_workgroups: int):
+        """Workgroup budget of later calls (0: as many as fit)."""
+        _check(_lib().ar_comm_set_max_workgroups(self._h, max_workgroups), "ar_comm_set_max_workgroups")
 
     def _call(self, name, send, recv, count, algo, proto, chunk_bytes, stream):
         dt = _dtype_name(send[0])

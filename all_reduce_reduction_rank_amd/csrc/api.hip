@@ -20,7 +20,7 @@
 #include "plan.hpp"
 
 namespace ar {
-hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream);
+hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uint32_t max_workgroups);
 hipError_t launch_reset(Ctl* c, hipStream_t stream);
 }  // namespace ar
 
@@ -42,6 +42,7 @@ struct ar_comm {
   uint64_t ticks_per_us = 100;
   uint64_t timeout_ticks = 0;
   int inj_rank = -1, inj_step = -1;
+  uint32_t max_workgroups = 0;  // 0: as many as fit on the GPU
   bool broken = false;
 };
 
@@ -156,6 +157,12 @@ ar_status ar_comm_check(ar_comm_t c, ar_stream_t stream, int* err_rank, int* err
   if (err_rank) *err_rank = h.err_key == 0xffffffffu ? -1 : (int)(h.err_key & 0xff);
   if (err_step) *err_step = h.err_key == 0xffffffffu ? -1 : (int)(h.err_key >> 8);
   return (ar_status)h.err_code;
+}
+
+ar_status ar_comm_set_max_workgroups(ar_comm_t c, unsigned max_workgroups) {
+  if (!c) return AR_ERR_INVALID;
+  c->max_workgroups = max_workgroups;
+  return AR_OK;
 }
 
 ar_status ar_debug_state(ar_comm_t c, ar_stream_t stream, uint64_t* out, int n) {
@@ -288,7 +295,8 @@ static ar_status run(ar_comm_t c, int op, const void* const* send, void* const* 
   a.timeout = c->timeout_ticks;
   a.inj_rank = c->inj_rank;
   a.inj_step = c->inj_step;
-  return ar::launch_collective(a, c->device, (hipStream_t)stream) == hipSuccess ? AR_OK : AR_ERR_HIP;
+  return ar::launch_collective(a, c->device, (hipStream_t)stream, c->max_workgroups) == hipSuccess ? AR_OK
+                                                                                             : AR_ERR_HIP;
 }
 
 extern "C" {

@@ -731,10 +731,14 @@ int resident_workgroups(KernelFn f, int device) {
   return total;
 }
 
-hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream) {
+hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uint32_t max_workgroups) {
   KernelFn f = pick_kernel(a.g.dtype, a.g.proto, a.g.kind);
   if (!f) return hipErrorInvalidValue;
-  const uint64_t cap = (uint64_t)resident_workgroups(f, device);
+  uint64_t cap = (uint64_t)resident_workgroups(f, device);
+  // A workgroup budget (NCCL's channel count) leaves the other CUs to
+  // concurrent kernels.  The one-shot in-place barrier needs the N rank
+  // programs of a tile resident together, so it never gets fewer than N.
+  if (max_workgroups) cap = umin(cap, umax((uint64_t)max_workgroups, (uint64_t)a.g.nranks));
   KArgs b = a;
   // Tickets per fetch (pick_batch).  The one-shot in-place barrier waits on
   // LATER tickets of its group, so it must take them one at a time.

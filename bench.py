@@ -130,6 +130,8 @@ def main():
     ap.add_argument("--algo", choices=("oneshot", "twoshot", "ring", "auto"))
     ap.add_argument("--proto", choices=("simple", "ll", "ll128", "auto"))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample length; 0 skips it")
+    ap.add_argument("--max-workgroups", type=int, default=0,
+                    help="workgroup budget of the collective's kernel (0: as many as fit)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -157,6 +159,8 @@ def main():
     send = inputs.device_rank_inputs(n, n_in, dt, w["dist"], seed=0, cfg=4)
     recv = [torch.empty(n_out, dtype=send[0].dtype, device="cuda") for _ in range(n)]
     comm = Comm(n, w["bytes"], line_cap)
+    if args.max_workgroups:
+        comm.set_max_workgroups(args.max_workgroups)
     call = getattr(comm, op)
     stream = torch.cuda.current_stream()
 
@@ -187,6 +191,28 @@ def main():
     per_call = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     print(f"[bench] timed {args.steps} steps: {ms:.4f} ms per call (wall {wall:.3f} s)", file=sys.stderr, flush=True)
 
+    us_graph = None
+    if w["bytes"] < (1 << 20):
+        # Small calls are latency-bound: a HIP graph of 100 captured calls,
+        # replayed, times the device side without the host's launch cost.
+        side = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(100):
+                call(send, recv, algo=req_algo, proto=req_proto, chunk_bytes=w["chunk"], stream=side)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):  # replay() launches on the current stream
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record(side)
+            g.replay()
+            e1.record(side)
+        torch.cuda.synchronize()
+        us_graph = round(e0.elapsed_time(e1) * 1e3 / 100, 2)
+        status = comm.check()
+        if status[0] != "AR_OK":
+            raise SystemExit(f"device error during the graph replays: {status}")
+
     s = w["bytes"]
     t = ms / 1e3
     plan = plan_bytes(n, op, count, dt, w["algo"], w["proto"], chunk_bytes=w["chunk"])
@@ -210,10 +236,12 @@ def main():
             "workload": args.workload, "op": op, "nranks": n, "bytes_per_rank": s, "dtype": dt,
             "dist": w["dist"], "algo": w["algo"], "proto": w["proto"], "chunk_bytes": w["chunk"],
             "selection": "auto" if auto else "fixed",
+            "max_workgroups": args.max_workgroups or "all",
             "parallelism": f"{n} simulated ranks on 1 GPU",
         },
         "us_median": round(per_call[len(per_call) // 2] * 1e3, 2),
         "us_min": round(per_call[0] * 1e3, 2),
+        "us_graph": us_graph,
         "cache_resident": 2 * n * s < 2 * MALL_BYTES,
         "algbw_GBps": round(algbw, 3),
         "busbw_GBps": round(algbw * busbw_factor(op, n), 3),

@@ -150,6 +150,19 @@ ar_status ar_allgather(ar_comm_t comm, const void* const* sendbufs, void* const*
                        size_t sendcount, ar_dtype dtype, ar_algo algo, ar_proto proto,
                        size_t chunk_bytes, ar_stream_t stream);
 
+/* Workgroup budget of the communicator's calls (NCCL's channel count): each
+ * call's kernel runs at most `max_workgroups` workgroups of 256 threads
+ * (0 = as many as fit on the GPU, the default), leaving the remaining CUs to
+ * kernels running concurrently on other streams ([H] "Protocols", the
+ * paragraph on channels: each channel runs as one block, so communication
+ * occupies SMs that compute could use; "Common environment variables and
+ * debugging": the channel count sets both bandwidth and the SMs used).
+ * Any budget is deadlock-free (every ticket is taken by a running
+ * workgroup); an in-place one-shot call still gets at least N.  Results do
+ * not depend on it.  Takes effect for calls issued afterwards.  Errors:
+ * AR_ERR_INVALID (null comm). */
+ar_status ar_comm_set_max_workgroups(ar_comm_t comm, unsigned max_workgroups);
+
 /* Host-only choice of algorithm and protocol ([H] "Algorithms": the latency
  * plus bytes-over-bandwidth model, t = alpha + S / beta, decides which
  * algorithm and protocol win at which message size).  alpha and beta are

@@ -335,3 +335,32 @@ def test_auto_choice_for_reduce_scatter_and_all_gather(op):
     want = getattr(C, op)(host, dt, algo)
     for r in range(n):
         assert_same(to_host(recv[r], dt), want[r], f"auto {op} ({algo}/{proto}) rank {r}")
+
+
+# ------------------------------------------------------ workgroup budget
+@pytest.mark.parametrize("budget", [1, 2, 5, 64])
+def test_workgroup_budget_keeps_results(budget):
+    n, dt, count = 4, "f32", 300001
+    c = Comm(n, count * 4, count * 4)
+    c.set_max_workgroups(budget)
+    host = inputs.rank_inputs(n, count, dt, "normal", seed=budget, cfg=42)
+    send = [to_dev(x, dt) for x in host]
+    for algo in ("oneshot", "twoshot", "ring"):
+        want = C.allreduce(host, dt, algo)
+        for proto in ("simple", "ll", "ll128"):
+            print("CASE budget", budget, algo, proto, flush=True, file=sys.stderr)
+            recv = [empty(count, dt) for _ in range(n)]
+            c.allreduce(send, recv, algo=algo, proto=proto)
+            torch.cuda.synchronize()
+            for r in range(n):
+                assert_same(to_host(recv[r], dt), want[r], f"budget {budget} {algo}/{proto} rank {r}")
+    # in place one-shot: the read-done barrier still gets N workgroups
+    print("CASE budget in-place", budget, flush=True, file=sys.stderr)
+    inplace = [to_dev(x, dt) for x in host]
+    c.allreduce(inplace, None, algo="oneshot")
+    torch.cuda.synchronize()
+    want = C.allreduce(host, dt, "oneshot")
+    for r in range(n):
+        assert_same(to_host(inplace[r], dt), want[r], f"budget {budget} in-place rank {r}")
+    assert c.check()[0] == "AR_OK"
+    c.close()
