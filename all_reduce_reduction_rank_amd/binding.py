@@ -162,7 +162,7 @@ class Comm:
         return _lib().ar_comm_workspace_bytes(self._h)
 
     def set_max_workgroups(self, max_workgroups: int):
-        """Workgroup budget of later calls (0: as many as fit)."""
+        """Workgroup budget of later calls (0: the default, up to 3 per CU)."""
         _check(_lib().ar_comm_set_max_workgroups(self._h, max_workgroups), "ar_comm_set_max_workgroups")
 
     def _call(self, name, send, recv, count, algo, proto, chunk_bytes, stream):

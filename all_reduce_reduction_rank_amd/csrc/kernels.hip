@@ -712,7 +712,20 @@ KernelFn pick_kernel(int dtype, int proto, int kind) {
   }
 }
 
-// Workgroups that can be resident at once for kernel f (cached per kernel).
+// Workgroups per CU a call runs by default.  Measured at N=8 (fractions of
+// HBM peak, grid = this x 256 CUs; "all" = every workgroup that fits, 6-7
+// per CU for most kernels):
+//   per CU          2      3      4    all
+//   ring 256 MiB  0.845  0.887  0.893  0.870
+//   ring 25 MiB   0.786  0.800  0.628  0.579
+//   int32 64 MiB  0.834  0.866  0.856  0.811
+//   two-shot 256  0.799  0.856  0.877  0.876
+//   LL128 5 MiB   126us  114us  175us  175us
+// More resident workgroups than this only add polling and contention.
+constexpr int DEFAULT_WG_PER_CU = 3;
+
+// Workgroups of kernel f a call may run at once on `device`: those that fit
+// (occupancy x CUs), at most DEFAULT_WG_PER_CU per CU (cached per kernel).
 int resident_workgroups(KernelFn f, int device) {
   static KernelFn seen[64];
   static int count[64];
@@ -726,6 +739,7 @@ int resident_workgroups(KernelFn f, int device) {
     per_cu = 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) cus = 1;
   if (per_cu < 1) per_cu = 1;
+  if (per_cu > DEFAULT_WG_PER_CU) per_cu = DEFAULT_WG_PER_CU;
   const int total = per_cu * cus;
   if (used < 64) { seen[used] = f; count[used] = total; ++used; }
   return total;

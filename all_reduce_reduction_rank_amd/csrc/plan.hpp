@@ -130,14 +130,14 @@ inline uint64_t pick_tile_bytes(int proto, uint64_t rank_bytes, int kind, bool i
 // counter, which serializes at about one per ~10 ns: a 256 MiB ring with
 // 16 KiB tiles and one ticket per fetch spends more time in the counter than
 // in HBM (0.43 of peak).  A fetch should cover about 64 KiB of tiles, and a
-// workgroup should still see >= 8 fetches, so work stays balanced.
+// workgroup should still see >= 4 fetches, so work stays balanced.
 constexpr uint64_t BYTES_PER_FETCH = 65536;
 inline uint32_t pick_batch(const Geometry& g, uint64_t resident, uint32_t max_batch) {
   const uint64_t tile_b = g.proto == PROTO_SIMPLE ? g.tile * (uint64_t)g.esize
                                                   : g.tile_lines * (uint64_t)g.line_bytes;
   uint64_t b = tile_b ? BYTES_PER_FETCH / tile_b : 1;
   b = clampu(b, 1, max_batch);
-  const uint64_t spread = resident ? g.ntasks / (8 * resident) : 1;
+  const uint64_t spread = resident ? g.ntasks / (4 * resident) : 1;
   return (uint32_t)clampu(b, 1, spread > 0 ? spread : 1);
 }
 

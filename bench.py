@@ -131,7 +131,7 @@ def main():
     ap.add_argument("--proto", choices=("simple", "ll", "ll128", "auto"))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample length; 0 skips it")
     ap.add_argument("--max-workgroups", type=int, default=0,
-                    help="workgroup budget of the collective's kernel (0: as many as fit)")
+                    help="workgroup budget of the collective's kernel (0: the default, up to 3 per CU)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -236,7 +236,7 @@ def main():
             "workload": args.workload, "op": op, "nranks": n, "bytes_per_rank": s, "dtype": dt,
             "dist": w["dist"], "algo": w["algo"], "proto": w["proto"], "chunk_bytes": w["chunk"],
             "selection": "auto" if auto else "fixed",
-            "max_workgroups": args.max_workgroups or "all",
+            "max_workgroups": args.max_workgroups or "default",
             "parallelism": f"{n} simulated ranks on 1 GPU",
         },
         "us_median": round(per_call[len(per_call) // 2] * 1e3, 2),

@@ -152,7 +152,7 @@ ar_status ar_allgather(ar_comm_t comm, const void* const* sendbufs, void* const*
 
 /* Workgroup budget of the communicator's calls (NCCL's channel count): each
  * call's kernel runs at most `max_workgroups` workgroups of 256 threads
- * (0 = as many as fit on the GPU, the default), leaving the remaining CUs to
+ * (0, the default: up to 3 per CU, which measured fastest), leaving CUs to
  * kernels running concurrently on other streams ([H] "Protocols", the
  * paragraph on channels: each channel runs as one block, so communication
  * occupies SMs that compute could use; "Common environment variables and
