@@ -22,6 +22,19 @@ here as follows.
   sum therefore starts at rank j+1 and ends at rank j, the rank that keeps it
   ("reduce-scatter: each keeps only its slice of the sum").  The wire carries
   the payload type, so a bf16 partial is rounded after every hop.
+* Tree all-reduce (same section, tree: a double binary tree that reduces
+  up the tree and then broadcasts down it, in O(log n) steps).  The page
+  gives neither the tree shapes nor how the data is split between the two
+  trees.  Reading taken: the buffer is cut in two halves like an N=2 block
+  split; half 0 runs on tree 0, half 1 on tree 1.  Both trees are complete
+  binary trees in heap layout (position p has children 2p+1 and 2p+2 and
+  parent (p-1)/2); tree 0 holds rank p at position p, tree 1 holds rank
+  N-1-p, so a rank that is an inner node of one tree is a leaf of the other
+  (for even N).  Going up, the node at position p adds, in this order, its
+  own input, then the partial of child 2p+1, then that of child 2p+2; it
+  sends its partial up rounded to the payload type (the wire carries bf16,
+  as on the ring).  The root's sum is the result, and going down every node
+  copies its parent's result.
 * Reduce-scatter and all-gather ("NCCL collectives...", section "Direct
   answer"): "direct" reads the slices straight from every rank (the
   one-shot / two-shot schedule has a single exchange for these); "ring" runs
@@ -146,10 +159,35 @@ def allreduce_ring(inputs, dt, chunk_bytes=DEFAULT_CHUNK_BYTES):
     return _ring_gather(owned, blocks, size, dt, chunk)
 
 
+def tree_rank(n, tree, pos):
+    """Rank at heap position `pos` of tree 0 or tree 1."""
+    return pos if tree == 0 else n - 1 - pos
+
+
+def allreduce_tree(inputs, dt):
+    """Double binary tree: half h of the buffer is reduced up tree h (children
+    before parents; own input, then left child, then right child) and the
+    root's sum is broadcast down to every rank."""
+    n, size = _check(inputs, dt)
+    outs = [_empty(size, dt) for _ in range(n)]
+    for tree, (lo, hi) in enumerate(geometry.ar_blocks(size, 2, dt)):
+        sent = [None] * n  # what the node at each position sends to its parent
+        for pos in reversed(range(n)):
+            acc = dtypes.to_acc(inputs[tree_rank(n, tree, pos)][lo:hi], dt)
+            for child in (2 * pos + 1, 2 * pos + 2):
+                if child < n:
+                    acc = dtypes.add(acc, dtypes.to_acc(sent[child], dt), dt)
+            sent[pos] = dtypes.from_acc(acc, dt)
+        for r in range(n):  # down the tree: every rank ends with the root's sum
+            outs[r][lo:hi] = sent[0]
+    return outs
+
+
 ALLREDUCE = {
     "oneshot": allreduce_oneshot,
     "twoshot": allreduce_twoshot,
     "ring": allreduce_ring,
+    "tree": allreduce_tree,
 }
 
 

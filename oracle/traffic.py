@@ -24,7 +24,8 @@ than from a closed form:
 
   Flags are a few bytes per tile and are left out of both tallies.
 
-Blocks of two-shot and ring follow ``oracle.geometry``; LL / LL128 lines are
+Blocks of two-shot and ring follow ``oracle.geometry``; the tree's two halves
+are the N=2 blocks, and each node keeps its partial in its own output; LL / LL128 lines are
 cut per block, so a block's wire bytes are ``wire_bytes(block bytes)``.
 """
 
@@ -52,6 +53,10 @@ class Tally:
         return self.read + self.write
 
 
+def _tree_rank(n, tree, pos):
+    return pos if tree == 0 else n - 1 - pos
+
+
 def _blocks_bytes(op, nranks, count, dt):
     e = ESIZE[dt]
     if op == "allreduce":
@@ -67,8 +72,10 @@ def tally(op: str, algo: str, proto: str, nranks: int, count: int, dt: str,
     t = Tally(n)
     w = lambda c: protomod.wire_bytes(c, proto)  # noqa: E731
     enc = proto != "simple"
-    if algo not in ("oneshot", "twoshot", "ring"):
+    if algo not in ("oneshot", "twoshot", "ring", "tree"):
         raise ValueError(algo)
+    if algo == "tree" and (op != "allreduce" or enc):
+        raise ValueError("the tree is an all-reduce schedule, run with Simple")
     if n == 1:  # a single rank: the result is its own input
         size = count * ESIZE[dt]
         if not in_place:
@@ -94,6 +101,22 @@ def tally(op: str, algo: str, proto: str, nranks: int, count: int, dt: str,
                 else:
                     t.rd(w(size))       # peer lines (and own lines when in place)
             t.wr(size)
+        return t
+
+    if algo == "tree":
+        e = ESIZE[dt]
+        for tree, (lo, hi) in enumerate(geometry.ar_blocks(count, 2, dt)):
+            c = (hi - lo) * e
+            for pos in range(n):  # up: own input and the children's partials
+                children = [ch for ch in (2 * pos + 1, 2 * pos + 2) if ch < n]
+                t.rd(c * (1 + len(children)))
+                t.wr(c)  # the partial (the root: the sum) in the rank's own output
+                for _ in children:
+                    t.recv(_tree_rank(n, tree, pos), c)
+            for pos in range(1, n):  # down: copy the parent's sum
+                t.rd(c)
+                t.wr(c)
+                t.recv(_tree_rank(n, tree, pos), c)
         return t
 
     if op == "allreduce" and algo == "twoshot":

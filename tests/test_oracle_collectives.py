@@ -16,6 +16,7 @@ from all_reduce_reduction_rank_amd import inputs
 from oracle import bf16, collectives as C, geometry
 
 ALGOS = ("oneshot", "twoshot", "ring")
+AR_ALGOS = ALGOS + ("tree",)  # the tree is an all-reduce schedule only
 DTYPES = ("f32", "bf16", "i32")
 
 
@@ -26,7 +27,7 @@ def _as_float(x, dt):
 
 
 # ---------------------------------------------------------------- all ones
-@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("algo", AR_ALGOS)
 @pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8])
 @pytest.mark.parametrize("count", [0, 1, 7, 64, 131])
@@ -46,7 +47,7 @@ def test_page_sanity_case_128_ones():
 
 
 # ------------------------------------------------------------- int32 exact
-@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("algo", AR_ALGOS)
 @pytest.mark.parametrize("n", [2, 3, 4, 8])
 def test_int32_equals_python_integer_sum(algo, n):
     count = 1000 + 3 * n
@@ -68,7 +69,7 @@ def test_int32_wraps_twos_complement():
 
 
 # ----------------------------------------------- fp32 bound vs exact sum
-@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("algo", AR_ALGOS)
 @pytest.mark.parametrize("n", [2, 4, 8])
 def test_f32_within_bound_of_exact_sum(algo, n):
     count = 777
@@ -163,13 +164,13 @@ def test_bf16_ring_rounds_every_hop():
 def test_two_ranks_all_algorithms_bitwise_equal(dt):
     # With two terms there is one association and IEEE add commutes.
     x = inputs.rank_inputs(2, 999, dt, "normal" if dt != "i32" else "int20", seed=2)
-    outs = [C.allreduce(x, dt, a, chunk_bytes=64) for a in ALGOS]
+    outs = [C.allreduce(x, dt, a, chunk_bytes=64) for a in AR_ALGOS]
     for o in outs[1:]:
         for r in range(2):
             assert np.array_equal(o[r], outs[0][r])
 
 
-@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("algo", AR_ALGOS)
 @pytest.mark.parametrize("dt", DTYPES)
 def test_every_rank_gets_the_same_result(algo, dt):
     n = 5
@@ -270,3 +271,75 @@ def test_more_ranks_than_vectors_leaves_empty_blocks():
         for out in C.allreduce(x, "f32", algo):
             assert np.allclose(out, ref, rtol=0, atol=8 * 2.0 ** -23 * 8)
     assert geometry.ar_blocks(2, 8, "f32")[1] == (2, 2)
+
+
+# ------------------------------------------------------------------- tree
+def test_tree_association_worked_value():
+    # N=4 heap trees.  Tree 0 (half 0): position p holds rank p; node 1's
+    # child is 3, the root's children are 1 and 2, so the sum is
+    # (x0 + (x1 + x3)) + x2.  Tree 1 (half 1): position p holds rank 3-p,
+    # so the sum is (x3 + (x2 + x0)) + x1.  With x = (2**24, 2**24, -1,
+    # -2**24) both are 2**24 - 1 exactly, while a left fold in either rank
+    # order loses the -1 against 2**25 or 2**24 and gives 2**24.
+    n, a = 4, geometry.vec_elems("f32")
+    vals = [2.0 ** 24, 2.0 ** 24, -1.0, -(2.0 ** 24)]
+    x = [np.full(2 * a, v, dtype=np.float32) for v in vals]
+    for out in C.allreduce_tree(x, "f32"):
+        assert np.all(out == 2.0 ** 24 - 1)
+    for out in C.allreduce_oneshot(x, "f32"):
+        assert np.all(out == 2.0 ** 24)
+    for out in C.allreduce_oneshot(x[::-1], "f32"):
+        assert np.all(out == 2.0 ** 24)
+
+
+def test_tree_halves_are_the_two_rank_block_split():
+    # Half 0 runs on tree 0 and half 1 on tree 1, cut where an N=2 block
+    # split cuts: probe with a value that only tree 1's order keeps.
+    # N=3: tree 0 sums x0 + x1 + x2 (ascending), tree 1 sums x2 + x1 + x0.
+    # x = (1, 2**24, -2**24): ascending gives (1 + 2**24 -> 2**24) - 2**24 = 0,
+    # descending gives (-2**24 + 2**24) + 1 = 1.
+    n, count = 3, 37
+    x = [np.full(count, v, dtype=np.float32) for v in (1.0, 2.0 ** 24, -(2.0 ** 24))]
+    (lo0, hi0), (lo1, hi1) = geometry.ar_blocks(count, 2, "f32")
+    assert (lo0, hi1) == (0, count) and hi0 == lo1 == 20  # ceil(37/2) = 19, up to a 4-element vector
+    for out in C.allreduce_tree(x, "f32"):
+        assert np.all(out[lo0:hi0] == 0.0) and np.all(out[lo1:hi1] == 1.0)
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+def test_tree_three_ranks_is_oneshot_in_each_tree_order(dt):
+    # With N <= 3 every child is a leaf, so each half is a plain fold of the
+    # inputs in the tree's order: ascending for tree 0, descending for tree 1.
+    n, count = 3, 1001
+    x = inputs.rank_inputs(n, count, dt, "normal" if dt != "i32" else "int20", seed=9)
+    (lo0, hi0), (lo1, hi1) = geometry.ar_blocks(count, 2, dt)
+    tree = C.allreduce_tree(x, dt)
+    up = C.allreduce_oneshot(x, dt)
+    down = C.allreduce_oneshot(x[::-1], dt)
+    for r in range(n):
+        assert np.array_equal(tree[r][lo0:hi0], up[r][lo0:hi0])
+        assert np.array_equal(tree[r][lo1:hi1], down[r][lo1:hi1])
+
+
+def test_bf16_tree_rounds_each_partial_it_sends():
+    # N=4, tree 0: node 1 sends bf16(x1 + x3) up.  x1 = 256, x3 = 1: 257 is a
+    # bf16 tie between 256 and 258 and rounds to even, 256.  The root then
+    # adds x0 = 1 and x2 = 1: 1 + 256 + 1 = 258, exact in bf16.  Rounding only
+    # once would round 259, a tie between 258 and 260, to even: 260.
+    n, a = 4, geometry.vec_elems("bf16")
+    one, b256 = 0x3F80, 0x4380
+    x = [np.full(2 * a, one, dtype=np.uint16) for _ in range(n)]
+    x[1][:] = b256
+    out = C.allreduce_tree(x, "bf16")
+    (lo0, hi0), _ = geometry.ar_blocks(2 * a, 2, "bf16")
+    assert np.all(bf16.widen(out[0][lo0:hi0]) == 258.0)
+    assert np.all(bf16.widen(C.allreduce_oneshot(x, "bf16")[0][lo0:hi0]) == 260.0)
+
+
+@pytest.mark.parametrize("n", [2, 5, 8])
+def test_tree_is_not_defined_for_reduce_scatter_or_all_gather(n):
+    x = [np.zeros(16, dtype=np.float32) for _ in range(n)]
+    with pytest.raises(ValueError):
+        C.reduce_scatter(x, "f32", "tree")
+    with pytest.raises(ValueError):
+        C.allgather(x, "f32", "tree")

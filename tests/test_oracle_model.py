@@ -232,3 +232,20 @@ def test_oneshot_has_nothing_to_wait_on_out_of_place():
     assert sim.blocked("allreduce", "oneshot", 8, withheld=(3, 0))[0] == []
     stuck, first = sim.blocked("allreduce", "oneshot", 8, withheld=(3, 0), in_place=True)
     assert len(stuck) == 8 and first == (0, 1)
+
+
+@pytest.mark.parametrize("n", [2, 3, 5, 8])
+def test_tree_bytes(n):
+    # Per half of c bytes: going up, every node reads its input and each
+    # child's partial (N + (N-1) reads of c) and writes its partial (N);
+    # going down, N-1 nodes read their parent's sum and write it: (5N-3) c in
+    # all, so (5N-3) S for the two halves.  Each rank-to-rank transfer (N-1
+    # up, N-1 down per half) moves c: 2(N-1)/N S per rank on average, the
+    # ring's figure ("Algorithms": the tree's bandwidth is close to optimal).
+    count = 8 * 1000
+    s = count * 4
+    t = traffic.tally("allreduce", "tree", "simple", n, count, "f32")
+    assert t.hbm == (5 * n - 3) * s
+    assert sum(t.link) == 2 * (n - 1) * s
+    with pytest.raises(ValueError):
+        traffic.tally("allreduce", "tree", "ll", n, count, "f32")
