@@ -24,9 +24,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("AR_LIBRARY") or os.path.join(HERE, "libar.so")
 
 OPS = {"allreduce": 0, "reduce_scatter": 1, "allgather": 2}
-ALGOS = {"oneshot": 0, "twoshot": 1, "ring": 2}
+ALGOS = {"oneshot": 0, "twoshot": 1, "ring": 2, "tree": 3}
 PROTOS = {"simple": 0, "ll": 1, "ll128": 2}
-AUTO = 3  # AR_ALGO_AUTO / AR_PROTO_AUTO: the library picks (ar_select)
+ALGO_AUTO, PROTO_AUTO = 4, 3  # AR_ALGO_AUTO / AR_PROTO_AUTO: the library picks (ar_select)
 DTYPES = {"f32": 0, "bf16": 1, "i32": 2}
 ESIZE = {"f32": 4, "bf16": 2, "i32": 4}
 
@@ -99,11 +99,11 @@ def _check(status, what):
 
 
 def _algo(name):
-    return AUTO if name == "auto" else ALGOS[name]
+    return ALGO_AUTO if name == "auto" else ALGOS[name]
 
 
 def _proto(name):
-    return AUTO if name == "auto" else PROTOS[name]
+    return PROTO_AUTO if name == "auto" else PROTOS[name]
 
 
 def _dtype_name(t):

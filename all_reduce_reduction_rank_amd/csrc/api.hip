@@ -256,6 +256,7 @@ static ar_status run(ar_comm_t c, int op, const void* const* send, void* const* 
     if (!select_schedule(op, n, dtype, rank_bytes, algo, proto, line_ok, &algo, &proto, nullptr))
       return AR_ERR_INVALID;
   }
+  if (algo == ALGO_TREE && n > 1 && (op != OP_ALLREDUCE || proto != PROTO_SIMPLE)) return AR_ERR_UNSUPPORTED;
   if (proto != PROTO_SIMPLE && n > 1 && rank_bytes > c->max_line_bytes) return AR_ERR_TOO_LARGE;
 
   int in_place = 0, same = 0;

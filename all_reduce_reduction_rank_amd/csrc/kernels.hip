@@ -35,12 +35,14 @@ constexpr int U_LL128 = 4;   // LL128 line groups (8 lines of a wave) per pass
 // =============================================================== Simple path
 // dst = fold(term(0), ..., term(n-1)) over `nbytes` (whole elements, at most
 // 64 KiB: one tile).  One term = raw copy (bit-exact for every type).
-// COH_FIRST: term(0) was written by another rank program during this call
-// (read at device scope).  COH_DST: dst will be read by another rank program
-// during this call (written at device scope).  Other terms are inputs.
+// COH_TERMS: bit i set = term(i) was written by another rank program during
+// this call (read at device scope); a plain `true` marks term(0) only.
+// COH_DST: dst will be read by another rank program during this call
+// (written at device scope).  Other terms are inputs.
 // NT_IN: inputs are read once per call; NT_OUT: a plain dst is final output.
-template <int DT, bool COH_FIRST, bool COH_DST, bool NT_IN = true, bool NT_OUT = true, class Term>
+template <int DT, unsigned COH_TERMS, bool COH_DST, bool NT_IN = true, bool NT_OUT = true, class Term>
 __device__ __forceinline__ void simple_stream(Term term, int nterms, char* dst, uint64_t nbytes) {
+  constexpr bool COH_FIRST = (COH_TERMS & 1u) != 0;
   const int es = Elem<DT>::size;
   const char* t0 = term(0);
   const Rsrc r0 = make_rsrc(t0, (uint32_t)nbytes);
@@ -72,10 +74,19 @@ __device__ __forceinline__ void simple_stream(Term term, int nterms, char* dst, 
     for (int u = 0; u < U_SIMPLE; ++u) acc[u] = Vec<DT>::widen(x[u]);
     for (int i = 1; i < nterms; ++i) {
       const char* p = term(i);
+      if ((COH_TERMS >> i) & 1u) {
+        const Rsrc rp = make_rsrc(p, (uint32_t)nbytes);
 #pragma unroll
-      for (int u = 0; u < U_SIMPLE; ++u) {
-        const uint32_t v = base + u * WG_THREADS;
-        x[u] = (v < nfull) ? ld16_hint<NT_IN>(p + (uint64_t)v * 16) : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < U_SIMPLE; ++u) {
+          const uint32_t v = base + u * WG_THREADS;
+          x[u] = (v < nfull) ? cld16(rp, v * 16) : make_uint4(0, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U_SIMPLE; ++u) {
+          const uint32_t v = base + u * WG_THREADS;
+          x[u] = (v < nfull) ? ld16_hint<NT_IN>(p + (uint64_t)v * 16) : make_uint4(0, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int u = 0; u < U_SIMPLE; ++u) acc[u].add(Vec<DT>::widen(x[u]));
@@ -98,7 +109,11 @@ __device__ __forceinline__ void simple_stream(Term term, int nterms, char* dst, 
     uint4 x = COH_FIRST ? cld_partial(r0, off, nb, es) : ld_any(t0 + off, nb, es);
     if (nterms > 1) {
       Vec<DT> acc = Vec<DT>::widen(x);
-      for (int i = 1; i < nterms; ++i) acc.add(Vec<DT>::widen(ld_any(term(i) + off, nb, es)));
+      for (int i = 1; i < nterms; ++i) {
+        const uint4 y = ((COH_TERMS >> i) & 1u) ? cld_partial(make_rsrc(term(i), (uint32_t)nbytes), off, nb, es)
+                                                 : ld_any(term(i) + off, nb, es);
+        acc.add(Vec<DT>::widen(y));
+      }
       x = acc.narrow();
     }
     if (COH_DST) cst_partial(rd, off, x, nb, es);
@@ -534,6 +549,41 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
     }
   }
 
+  if constexpr (KIND == K_TREE) {
+    // Half `tree` of the buffer on tree `tree`; this task is the node at heap
+    // position p.  A node keeps its partial, and later the sum, in its own
+    // output.  Flags per (tree, tile, position): tag+1 = partial ready,
+    // tag+2 = sum ready (the root's up task, every other node's down task).
+    const uint64_t tree = k.block;
+    const int p = k.peer;
+    const uint64_t off = (block_lo(g, tree) + k.lo) * es;
+    uint64_t* fl = a.flags + (tree * g.tiles + k.tile) * (uint64_t)n;
+    const int c1 = 2 * p + 1, c2 = 2 * p + 2;
+    char* mine = a.out[k.rank] + off;
+    if (k.phase == PH_TREE_UP) {
+      if (c1 < n && !wg_wait(a, fl + c1, tag + 1, 0, k.rank)) return;
+      if (c2 < n && !wg_wait(a, fl + c2, tag + 1, 0, k.rank)) return;
+      const char* own = a.in[k.rank] + off;
+      const char* left = c1 < n ? (const char*)a.out[tree_rank(n, tree, c1)] + off : nullptr;
+      const char* right = c2 < n ? (const char*)a.out[tree_rank(n, tree, c2)] + off : nullptr;
+      // own input, then the left and the right child's partial (device scope)
+      auto terms = [&](int i) { return i == 0 ? own : (i == 1 ? left : right); };
+      const int nt = 1 + (c1 < n) + (c2 < n);
+      simple_stream<DT, 6u, true>(terms, nt, mine, nbytes);
+      wg_signal(a, fl + p, tag + (p == 0 ? 2 : 1), 0, k.rank);
+    } else {
+      const int parent = (p - 1) / 2;
+      if (!wg_wait(a, fl + parent, tag + 2, 1, k.rank)) return;
+      const char* up = a.out[tree_rank(n, tree, parent)] + off;
+      if (c1 < n) {  // this node's children copy the sum from here
+        simple_stream<DT, 1u, true>([&](int) { return up; }, 1, mine, nbytes);
+        wg_signal(a, fl + p, tag + 2, 1, k.rank);
+      } else {
+        simple_stream<DT, 1u, false>([&](int) { return up; }, 1, mine, nbytes);
+      }
+    }
+  }
+
   if constexpr (KIND == K_RING) {
     const int j = (int)k.block;
     const int s = k.step, q = k.rank;
@@ -688,6 +738,9 @@ static KernelFn pick_kind(int kind) {
     case K_RS_DIRECT: return collective_kernel<DT, PROTO, K_RS_DIRECT>;
     case K_AG_DIRECT: return collective_kernel<DT, PROTO, K_AG_DIRECT>;
     case K_RING: return collective_kernel<DT, PROTO, K_RING>;
+    case K_TREE:
+      if constexpr (PROTO == PROTO_SIMPLE) return collective_kernel<DT, PROTO, K_TREE>;
+      return nullptr;
     default: return nullptr;
   }
 }

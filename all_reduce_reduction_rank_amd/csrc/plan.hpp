@@ -32,7 +32,7 @@ constexpr uint64_t LL128_ALIGN = 240;       // 2 lines: a multiple of 16 bytes a
 inline int esize_of(int dtype) { return dtype == DT_BF16 ? 2 : 4; }
 
 // AR_ALGO_AUTO / AR_PROTO_AUTO in the C ABI.
-constexpr int ALGO_AUTO = 3;
+constexpr int ALGO_AUTO = 4;
 constexpr int PROTO_AUTO = 3;
 constexpr uint64_t MALL_BYTES = 256ull << 20;
 
@@ -71,8 +71,8 @@ inline double predict_us(int op, int nranks, int esize, int algo, int proto, uin
 // time (fixed choices are kept).  LL and LL128 are candidates only when
 // `line_ok` (the message fits the communicator's line staging).  On ties, or
 // with no fit at all, the earlier candidate wins: Simple before LL before
-// LL128, one-shot before two-shot before ring.  Returns false on a bad
-// argument.
+// LL128, one-shot before two-shot before ring before tree.  Returns false on
+// a bad argument.
 inline bool select_schedule(int op, int nranks, int dtype, uint64_t rank_bytes, int algo, int proto,
                             bool line_ok, int* out_algo, int* out_proto, double* out_us) {
   if (op < 0 || op > 2 || dtype < 0 || dtype > 2 || nranks < 1 || nranks > MAX_RANKS) return false;
@@ -80,13 +80,15 @@ inline bool select_schedule(int op, int nranks, int dtype, uint64_t rank_bytes, 
   int best_a = algo == ALGO_AUTO ? ALGO_ONESHOT : algo;
   int best_p = proto == PROTO_AUTO ? PROTO_SIMPLE : proto;
   double best_t = -1.0;
-  for (int a = 0; a < 3; ++a) {
+  for (int a = 0; a < 4; ++a) {
     if (algo != ALGO_AUTO && a != algo) continue;
-    // reduce-scatter / all-gather: two-shot names the same direct schedule
-    if (algo == ALGO_AUTO && op != OP_ALLREDUCE && a == ALGO_TWOSHOT) continue;
+    // reduce-scatter / all-gather: two-shot names the same direct schedule,
+    // and the tree is an all-reduce schedule
+    if (algo == ALGO_AUTO && op != OP_ALLREDUCE && (a == ALGO_TWOSHOT || a == ALGO_TREE)) continue;
     for (int p = 0; p < 3; ++p) {
       if (proto != PROTO_AUTO && p != proto) continue;
       if (proto == PROTO_AUTO && p != PROTO_SIMPLE && !line_ok) continue;
+      if (a == ALGO_TREE && p != PROTO_SIMPLE) continue;  // the tree runs with Simple only
       const double t = predict_us(op, nranks, esize_of(dtype), a, p, rank_bytes);
       if (t < 0) continue;
       if (best_t < 0 || t < best_t) { best_t = t; best_a = a; best_p = p; }
@@ -118,7 +120,7 @@ inline uint64_t pick_tile_bytes(int proto, uint64_t rank_bytes, int kind, bool i
   const uint64_t want = floor_pow2(rank_bytes / 128 + 1);
   if (proto == PROTO_SIMPLE) {
     uint64_t hi = 131072;
-    if (kind == K_RING || kind == K_TWOSHOT) hi = 32768;
+    if (kind == K_RING || kind == K_TWOSHOT || kind == K_TREE) hi = 32768;
     if (kind == K_ONESHOT && in_place) hi = 16384;
     return clampu(want, 4096, hi);
   }
@@ -145,7 +147,7 @@ inline uint32_t pick_batch(const Geometry& g, uint64_t resident, uint32_t max_ba
 inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, uint64_t count,
                           uint64_t chunk_bytes, int in_place, Geometry* out, const Tuning& tune = Tuning()) {
   if (nranks < 1 || nranks > MAX_RANKS) return false;
-  if (op < 0 || op > 2 || algo < 0 || algo > 2 || proto < 0 || proto > 2 || dtype < 0 || dtype > 2)
+  if (op < 0 || op > 2 || algo < 0 || algo > 3 || proto < 0 || proto > 2 || dtype < 0 || dtype > 2)
     return false;
   Geometry g = {};
   g.op = op; g.algo = algo; g.proto = proto; g.dtype = dtype;
@@ -178,7 +180,11 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
     return true;
   }
 
-  if (op == OP_ALLREDUCE) g.kind = algo == ALGO_ONESHOT ? K_ONESHOT : (algo == ALGO_TWOSHOT ? K_TWOSHOT : K_RING);
+  if (algo == ALGO_TREE && (op != OP_ALLREDUCE || proto != PROTO_SIMPLE)) return false;  // all-reduce, Simple
+  if (op == OP_ALLREDUCE)
+    g.kind = algo == ALGO_ONESHOT ? K_ONESHOT
+             : algo == ALGO_TWOSHOT ? K_TWOSHOT
+             : algo == ALGO_TREE ? K_TREE : K_RING;
   else if (op == OP_REDUCE_SCATTER) g.kind = algo == ALGO_RING ? K_RING : K_RS_DIRECT;
   else g.kind = algo == ALGO_RING ? K_RING : K_AG_DIRECT;
 
@@ -218,6 +224,17 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
     g.tile_lines = lines ? lines_for(g, tile_b) : 0;
     g.slot_lines = g.loops * g.tiles * g.tile_lines;
     g.nslots = lines ? n * (uint64_t)(g.steps - 1) : 0;
+    *out = g;
+    return true;
+  }
+
+  if (g.kind == K_TREE) {  // two halves: the N=2 block split
+    g.block = cdiv(cdiv(count, 2), vec) * vec;
+    g.tile = tile_b / es;
+    g.tiles = cdiv(g.block, g.tile);
+    g.per_group = 4ull * n - 2;
+    g.ntasks = g.tiles * g.per_group;
+    g.nflags = 2ull * g.tiles * n;
     *out = g;
     return true;
   }
@@ -356,6 +373,15 @@ inline Bytes account(const Geometry& g) {
           if (keeps) b.wr += len;
           if (s < last) b.wr += w;
           if (g.op == OP_REDUCE_SCATTER && s == last) {}  // last step: output only
+        }
+        break;
+      }
+      case K_TREE: {
+        if (k.phase == PH_TREE_UP) {  // own input + each child's partial -> own output
+          const uint64_t kids = (2 * k.peer + 1 < n) + (2 * k.peer + 2 < n);
+          b.rd += (1 + kids) * len; b.wr += len; b.link[r] += kids * len;
+        } else {                      // the parent's sum -> own output
+          b.rd += len; b.wr += len; b.link[r] += len;
         }
         break;
       }

@@ -24,6 +24,12 @@
 //   K_RING      chain per (block, chunk loop, tile): N-1 reduce steps and/or
 //               N-1 copy steps, each run by the receiving rank; tickets go
 //               window by window, step by step inside a window.
+//   K_TREE      double binary tree (all-reduce, Simple): half h of the
+//               buffer goes up tree h (heap layout; tree 0 holds rank p at
+//               position p, tree 1 rank N-1-p), every node adding its own
+//               input and its children's partials, then the root's sum goes
+//               back down; per tile, tickets run the up tasks leaves first
+//               and the down tasks root first.
 //   K_COPY      a single rank: output = input.
 //
 // With LL / LL128 a transfer is lines written by the sender into staging
@@ -43,10 +49,10 @@
 namespace ar {
 
 enum Op { OP_ALLREDUCE = 0, OP_REDUCE_SCATTER = 1, OP_ALLGATHER = 2 };
-enum Algo { ALGO_ONESHOT = 0, ALGO_TWOSHOT = 1, ALGO_RING = 2 };
+enum Algo { ALGO_ONESHOT = 0, ALGO_TWOSHOT = 1, ALGO_RING = 2, ALGO_TREE = 3 };
 enum Proto { PROTO_SIMPLE = 0, PROTO_LL = 1, PROTO_LL128 = 2 };
 enum DType { DT_F32 = 0, DT_BF16 = 1, DT_I32 = 2 };
-enum Kind { K_COPY = 0, K_ONESHOT = 1, K_TWOSHOT = 2, K_RS_DIRECT = 3, K_AG_DIRECT = 4, K_RING = 5 };
+enum Kind { K_COPY = 0, K_ONESHOT = 1, K_TWOSHOT = 2, K_RS_DIRECT = 3, K_AG_DIRECT = 4, K_RING = 5, K_TREE = 6 };
 
 constexpr int MAX_RANKS = 8;
 constexpr int WG_THREADS = 256;
@@ -62,7 +68,9 @@ enum Phase {
   PH_SEND,        // LL/LL128: encode the rank's own input slice as lines
   PH_RECV_FOLD,   // LL/LL128: own input + N-1 peers' lines -> output (+ publish)
   PH_RECV_COPY,   // LL/LL128: lines -> output
-  PH_RING         // one step of a ring chain
+  PH_RING,        // one step of a ring chain
+  PH_TREE_UP,     // tree: own input + children's partials -> own output
+  PH_TREE_DOWN    // tree: parent's sum -> own output
 };
 
 struct Geometry {
@@ -160,6 +168,9 @@ AR_HD int32_t rank_mod(int64_t x, int32_t n) { return (int32_t)(((x % n) + n) % 
 // Rank r' in [0, n-1) mapped onto [0, n) skipping `skip`.
 AR_HD int32_t skip_rank(int32_t rp, int32_t skip) { return rp + (rp >= skip ? 1 : 0); }
 
+// Rank at heap position `pos` of tree 0 or tree 1.
+AR_HD int32_t tree_rank(int32_t n, uint64_t tree, int32_t pos) { return tree == 0 ? pos : n - 1 - pos; }
+
 // Decode ticket t of geometry g.
 AR_HD Task decode(const Geometry& g, uint64_t t) {
   Task k;
@@ -173,6 +184,32 @@ AR_HD Task decode(const Geometry& g, uint64_t t) {
     k.phase = PH_COPY;
     k.tile = t;
     tile_range(g, g.total, t, &k.lo, &k.hi);
+    return k;
+  }
+
+  if (g.kind == K_TREE) {
+    // per tile: up tree 0 (positions N-1..0), up tree 1, down tree 0
+    // (positions 1..N-1), down tree 1
+    const uint64_t per_tile = 4ull * n - 2;
+    const uint64_t tile = t / per_tile, r = t % per_tile;
+    uint64_t tree;
+    int32_t pos;
+    if (r < 2ull * n) {
+      tree = r / n;
+      pos = n - 1 - (int32_t)(r % n);
+      k.phase = PH_TREE_UP;
+    } else {
+      const uint64_t d = r - 2ull * n;
+      tree = d / (n - 1);
+      pos = 1 + (int32_t)(d % (n - 1));
+      k.phase = PH_TREE_DOWN;
+    }
+    k.block = tree;
+    k.peer = pos;
+    k.rank = tree_rank(n, tree, pos);
+    k.tile = tile;
+    tile_range(g, block_len(g, tree), tile, &k.lo, &k.hi);
+    if (k.hi <= k.lo) k.phase = PH_NONE;
     return k;
   }
 

@@ -22,8 +22,17 @@ import sys
 import time
 
 SIZES = [8 * 4 ** k for k in range(14)] + [1 << 30]
-ALGOS = ("oneshot", "twoshot", "ring")
+ALGOS = ("oneshot", "twoshot", "ring", "tree")
 PROTOS = ("simple", "ll", "ll128")
+
+
+def combos(op):
+    """(algorithm, protocol) pairs a sweep of `op` times.  For reduce-scatter
+    and all-gather one-shot and two-shot name the same direct schedule; the
+    tree is an all-reduce schedule with Simple only."""
+    if op != "allreduce":
+        return [(a, p) for a in ("oneshot", "ring") for p in PROTOS]
+    return [(a, p) for a in ("oneshot", "twoshot", "ring") for p in PROTOS] + [("tree", "simple")]
 ESIZE = {"f32": 4, "bf16": 2, "i32": 4}
 MALL_BYTES = 256 << 20
 
@@ -80,7 +89,6 @@ def run(out_path, ns, dtypes, sizes=SIZES, graphs=True, op="allreduce"):
     from . import Comm, inputs
 
     torch.cuda.set_device(0)
-    algos = ALGOS if op == "allreduce" else ("oneshot", "ring")
     with open(out_path, "a") as out:
         for n in ns:
             for dt in dtypes:
@@ -102,22 +110,21 @@ def run(out_path, ns, dtypes, sizes=SIZES, graphs=True, op="allreduce"):
                     else:
                         count, s_in, s_out = shard, [t[:shard] for t in send], [t[:n * shard] for t in recv]
                     fn = getattr(comm, op)
-                    for algo in algos:
-                        for proto in PROTOS:
-                            def call():
-                                fn(s_in, s_out, algo=algo, proto=proto, stream=side)
+                    for algo, proto in combos(op):
+                        def call():
+                            fn(s_in, s_out, algo=algo, proto=proto, stream=side)
 
-                            with torch.cuda.stream(side):
-                                rec = _time_calls(call, side)
-                                if graphs and nbytes < (1 << 20):
-                                    rec["us_graph"] = _time_graph(call, side)
-                            st = comm.check(side)
-                            if st[0] != "AR_OK":
-                                raise SystemExit(f"device error at {op} N={n} {dt} {nbytes} B {algo}/{proto}: {st}")
-                            rec.update(op=op, n=n, dtype=dt, bytes=nbytes, algo=algo, proto=proto,
-                                       cache_resident=2 * n * nbytes < 2 * MALL_BYTES)
-                            out.write(json.dumps(rec) + "\n")
-                            out.flush()
+                        with torch.cuda.stream(side):
+                            rec = _time_calls(call, side)
+                            if graphs and nbytes < (1 << 20):
+                                rec["us_graph"] = _time_graph(call, side)
+                        st = comm.check(side)
+                        if st[0] != "AR_OK":
+                            raise SystemExit(f"device error at {op} N={n} {dt} {nbytes} B {algo}/{proto}: {st}")
+                        rec.update(op=op, n=n, dtype=dt, bytes=nbytes, algo=algo, proto=proto,
+                                   cache_resident=2 * n * nbytes < 2 * MALL_BYTES)
+                        out.write(json.dumps(rec) + "\n")
+                        out.flush()
                     print(f"[sweep] {op} N={n} {dt} {nbytes} B done", file=sys.stderr, flush=True)
                 comm.close()
                 del send, recv, s_in, s_out
@@ -143,17 +150,17 @@ def summary(recs, table_ranks=None):
     for op, n, dt in keys:
         rows = [r for r in recs if r.get("op", "allreduce") == op and r["n"] == n and r["dtype"] == dt]
         sizes = sorted({r["bytes"] for r in rows})
-        algos = [a for a in ALGOS if any(r["algo"] == a for r in rows)]
+        cols = [c for c in combos(op) if any((r["algo"], r["proto"]) == c for r in rows)]
         lines.append(f"\n### {op}, N={n}, {dt} (µs per call)\n")
         if table_ranks is None or n in table_ranks:
-            lines.append("| bytes/rank | " + " | ".join(f"{a}/{p}" for a in algos for p in PROTOS) + " | fastest |")
-            lines.append("|---:|" + "---:|" * (len(algos) * len(PROTOS)) + "---|")
+            lines.append("| bytes/rank | " + " | ".join(f"{a}/{p}" for a, p in cols) + " | fastest |")
+            lines.append("|---:|" + "---:|" * len(cols) + "---|")
         for s in sizes:
             if table_ranks is not None and n not in table_ranks:
                 break
             t = {(r["algo"], r["proto"]): best_time(r) for r in rows if r["bytes"] == s}
             fast = min(t, key=t.get)
-            cells = [f"{t[(a, p)]:.1f}" if (a, p) in t else "" for a in algos for p in PROTOS]
+            cells = [f"{t[c]:.1f}" if c in t else "" for c in cols]
             lines.append(f"| {s} | " + " | ".join(cells) + f" | {fast[0]}/{fast[1]} |")
         lines.append("")
         t_all = {}

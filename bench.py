@@ -127,7 +127,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
-    ap.add_argument("--algo", choices=("oneshot", "twoshot", "ring", "auto"))
+    ap.add_argument("--algo", choices=("oneshot", "twoshot", "ring", "tree", "auto"))
     ap.add_argument("--proto", choices=("simple", "ll", "ll128", "auto"))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample length; 0 skips it")
     ap.add_argument("--max-workgroups", type=int, default=0,

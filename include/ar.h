@@ -68,8 +68,14 @@ typedef enum { AR_F32 = 0, AR_BF16 = 1, AR_I32 = 2 } ar_dtype;
 
 /* [H] "Algorithms".  For reduce-scatter and all-gather, ONESHOT and TWOSHOT
  * both name the direct schedule (one exchange: every rank reads its slices
- * straight from every rank).  AR_ALGO_AUTO: the library picks (ar_select). */
-typedef enum { AR_ONESHOT = 0, AR_TWOSHOT = 1, AR_RING = 2, AR_ALGO_AUTO = 3 } ar_algo;
+ * straight from every rank).  AR_TREE: the double binary tree, all-reduce
+ * with AR_SIMPLE only (other combinations return AR_ERR_UNSUPPORTED): half h
+ * of the buffer (the N=2 block split) is reduced up tree h and its sum sent
+ * back down; both trees are complete binary trees in heap layout, tree 0
+ * holding rank p at position p and tree 1 rank N-1-p; a node adds its own
+ * input, then its left and right children's partials, and sends its partial
+ * up in the payload type.  AR_ALGO_AUTO: the library picks (ar_select). */
+typedef enum { AR_ONESHOT = 0, AR_TWOSHOT = 1, AR_RING = 2, AR_TREE = 3, AR_ALGO_AUTO = 4 } ar_algo;
 
 /* [H] "Protocols".  AR_PROTO_AUTO: the library picks (ar_select). */
 typedef enum { AR_SIMPLE = 0, AR_LL = 1, AR_LL128 = 2, AR_PROTO_AUTO = 3 } ar_proto;

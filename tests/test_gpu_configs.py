@@ -223,3 +223,30 @@ def test_in_place_at_8mib(algo):
         assert_same(to_host(send[r], dt), want[r], f"in place {algo} rank {r}")
     assert c.check()[0] == "AR_OK"
     c.close()
+
+
+# ------------------------------------------- tree at the gradient-bucket size
+def test_tree_gradient_bucket_256mib_sampled():
+    # The tree's order depends only on the half an element is in, so a
+    # reduced problem made of `per` samples of each half (in order) keeps it.
+    n, count, dt = 8, 64 << 20, "f32"
+    _say("tree-full", n, count)
+    send = inputs.device_rank_inputs(n, count, dt, "normal_1e-3", seed=1, cfg=51)
+    recv = [torch.empty_like(t) for t in send]
+    c = Comm(n, count * 4, 0)
+    c.allreduce(send, recv, algo="tree", proto="simple")
+    torch.cuda.synchronize()
+    assert c.check()[0] == "AR_OK"
+    c.close()
+    rng = np.random.default_rng(1)
+    per = 2048
+    halves = geometry.ar_blocks(count, 2, dt)
+    idx = np.concatenate([_samples(lo, hi, per, rng) for lo, hi in halves])
+    red_in = _gather(send, idx, dt)
+    assert geometry.ar_blocks(len(idx), 2, dt) == [(0, per), (per, 2 * per)]
+    want = C.allreduce(red_in, dt, "tree")
+    got = _gather(recv, idx, dt)
+    for r in range(n):
+        assert_same(got[r], want[r], f"tree 256 MiB rank {r}")
+    del send, recv
+    torch.cuda.empty_cache()

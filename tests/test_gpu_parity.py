@@ -364,3 +364,58 @@ def test_workgroup_budget_keeps_results(budget):
         assert_same(to_host(inplace[r], dt), want[r], f"budget {budget} in-place rank {r}")
     assert c.check()[0] == "AR_OK"
     c.close()
+
+
+# ------------------------------------------------------ double binary tree
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 7, 8])
+def test_tree_allreduce(n, dt):
+    # 1 element (half 1 empty), ragged halves, several 32 KiB tiles per half.
+    for count in (1, 7, 1000, 70001, 300003):
+        run_allreduce(n, count, dt, "tree", "simple", seed=count)
+
+
+def test_tree_in_place_ones_and_single_rank():
+    for dt in DTYPES:
+        for n, count in ((2, 4096), (5, 33333), (8, 100001)):
+            run_allreduce(n, count, dt, "tree", "simple", seed=3, in_place=True)
+        run_allreduce(8, 128, dt, "tree", "simple", dist="ones")
+    run_allreduce(1, 999, "f32", "tree", "simple")
+
+
+def test_tree_graph_replays():
+    n, count, dt = 6, 50001, "f32"
+    c = comm(n)
+    send = [empty(count, dt) for _ in range(n)]
+    recv = [empty(count, dt) for _ in range(n)]
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        c.allreduce(send, recv, algo="tree", proto="simple")
+    torch.cuda.synchronize()
+    for it in range(3):
+        host = inputs.rank_inputs(n, count, dt, "normal", seed=3000 + it)
+        for t, x in zip(send, host):
+            t.copy_(to_dev(x, dt))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = C.allreduce(host, dt, "tree")
+        for r in range(n):
+            assert_same(to_host(recv[r], dt), want[r], f"tree replay {it} rank {r}")
+        c.allreduce(send, [empty(count, dt) for _ in range(n)], algo="ring")  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_tree_with_line_protocols_or_rs_ag_is_unsupported():
+    n = 4
+    c = comm(n)
+    x = [empty(64, "f32") for _ in range(n)]
+    y = [empty(64, "f32") for _ in range(n)]
+    for proto in ("ll", "ll128"):
+        with pytest.raises(ARError) as e:
+            c.allreduce(x, y, algo="tree", proto=proto)
+        assert e.value.status == 2
+    with pytest.raises(ARError):
+        c.reduce_scatter(x, [empty(16, "f32") for _ in range(n)], algo="tree")
+    assert c.check()[0] == "AR_OK"

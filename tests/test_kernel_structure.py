@@ -35,8 +35,8 @@ def _kernels(text):
 
 
 def test_every_kernel_compiled(asm):
-    # 3 payload types x (3 protocols x 5 schedules + 1 copy kernel)
-    assert len(_kernels(asm)) == 48
+    # 3 payload types x (3 protocols x 5 schedules + the Simple tree + 1 copy kernel)
+    assert len(_kernels(asm)) == 51
 
 
 def _label_of(line):

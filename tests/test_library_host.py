@@ -74,3 +74,20 @@ def test_headline_plan_bytes():
     p = binding.plan_bytes(8, "allreduce", s // 4, "f32", "ring", "simple", chunk_bytes=512 << 10)
     assert p["hbm"] == 35 * s
     assert p["link"] == [2 * 7 * s // 8] * 8
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("count", [0, 1, 7, 999, 70001])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_tree_plan_bytes_match_oracle_tally(n, count, dt):
+    got = binding.plan_bytes(n, "allreduce", count, dt, "tree", "simple")
+    want = traffic.tally("allreduce", "tree", "simple", n, count, dt)
+    assert (got["read"], got["write"]) == (want.read, want.write)
+    assert got["link"] == want.link[:n] or n == 1
+
+
+def test_tree_is_all_reduce_with_simple_only():
+    for op, proto in (("allreduce", "ll"), ("allreduce", "ll128"), ("reduce_scatter", "simple"),
+                      ("allgather", "simple")):
+        with pytest.raises(binding.ARError):
+            binding.plan_bytes(4, op, 1000, "f32", "tree", proto)
