@@ -22,6 +22,9 @@ constexpr uint64_t DEFAULT_CHUNK_BYTES = 512 * 1024;
 // Workgroups an MI355X keeps resident for these kernels (256 CUs x up to 8):
 // the tickets between a task and its predecessor should exceed it.
 constexpr uint64_t RESIDENT_HINT = 2048;
+// Tasks between the levels of one tree tile: about the default grid (3
+// workgroups on each of 256 CUs) plus a third.
+constexpr uint64_t TREE_RESIDENT_HINT = 1024;
 // Bytes that one step of a ring window moves over all ranks: a quarter of
 // the 256 MB last-level cache (MALL), so a step's staged chunks are still
 // there when the next step reads them.
@@ -233,7 +236,16 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
     g.tile = tile_b / es;
     g.tiles = cdiv(g.block, g.tile);
     g.per_group = 4ull * n - 2;
-    g.ntasks = g.tiles * g.per_group;
+    // Levels of a tile `lag` groups apart, about one resident grid of tasks,
+    // so a task's inputs are mostly ready when it starts.  When every task
+    // fits in one grid there is no lag: the levels of a tile follow each
+    // other directly (a lag would only stretch the chain of a small call).
+    const uint64_t deepest = tree_depth(n - 1);
+    g.lag = g.tiles * g.per_group <= TREE_RESIDENT_HINT
+                ? 0
+                : (int32_t)umax(1, umin(g.tiles, cdiv(TREE_RESIDENT_HINT, g.per_group)));
+    g.groups = g.tiles + 2 * deepest * (uint64_t)g.lag;
+    g.ntasks = g.groups * g.per_group;
     g.nflags = 2ull * g.tiles * n;
     *out = g;
     return true;

@@ -28,8 +28,8 @@
 //               buffer goes up tree h (heap layout; tree 0 holds rank p at
 //               position p, tree 1 rank N-1-p), every node adding its own
 //               input and its children's partials, then the root's sum goes
-//               back down; per tile, tickets run the up tasks leaves first
-//               and the down tasks root first.
+//               back down; each tile's up tasks run leaves first and its
+//               down tasks root first, the levels `lag` ticket groups apart.
 //   K_COPY      a single rank: output = input.
 //
 // With LL / LL128 a transfer is lines written by the sender into staging
@@ -168,6 +168,13 @@ AR_HD int32_t rank_mod(int64_t x, int32_t n) { return (int32_t)(((x % n) + n) % 
 // Rank r' in [0, n-1) mapped onto [0, n) skipping `skip`.
 AR_HD int32_t skip_rank(int32_t rp, int32_t skip) { return rp + (rp >= skip ? 1 : 0); }
 
+// Depth of heap position `pos` (the root is 0).
+AR_HD uint64_t tree_depth(int32_t pos) {
+  uint64_t d = 0;
+  for (uint32_t x = (uint32_t)pos + 1; x > 1; x >>= 1) ++d;
+  return d;
+}
+
 // Rank at heap position `pos` of tree 0 or tree 1.
 AR_HD int32_t tree_rank(int32_t n, uint64_t tree, int32_t pos) { return tree == 0 ? pos : n - 1 - pos; }
 
@@ -188,27 +195,37 @@ AR_HD Task decode(const Geometry& g, uint64_t t) {
   }
 
   if (g.kind == K_TREE) {
-    // per tile: up tree 0 (positions N-1..0), up tree 1, down tree 0
-    // (positions 1..N-1), down tree 1
-    const uint64_t per_tile = 4ull * n - 2;
-    const uint64_t tile = t / per_tile, r = t % per_tile;
+    // A group holds one of each of the 4N-2 tasks of a tile: up on tree 0
+    // (positions N-1..0), up on tree 1, down on tree 0 (positions 1..N-1),
+    // down on tree 1.  With lag 0 group g is tile g.  Otherwise each task
+    // belongs to a stage (up: D - depth, leaves first; down: D + depth) and
+    // group g holds, for every stage st, the tasks of tile g - st*lag: a
+    // task's inputs then come from about `lag` groups earlier.
+    const uint64_t per_group = 4ull * n - 2;
+    const uint64_t group = t / per_group, r = t % per_group;
     uint64_t tree;
     int32_t pos;
+    bool up;
     if (r < 2ull * n) {
       tree = r / n;
       pos = n - 1 - (int32_t)(r % n);
-      k.phase = PH_TREE_UP;
+      up = true;
     } else {
       const uint64_t d = r - 2ull * n;
       tree = d / (n - 1);
       pos = 1 + (int32_t)(d % (n - 1));
-      k.phase = PH_TREE_DOWN;
+      up = false;
     }
+    const uint64_t depth = tree_depth(pos), deepest = tree_depth(n - 1);
+    const uint64_t stage = up ? deepest - depth : deepest + depth;
+    const uint64_t shift = stage * (uint64_t)g.lag;
+    if (group < shift || group - shift >= g.tiles) return k;  // no tile in this slot
+    k.phase = up ? PH_TREE_UP : PH_TREE_DOWN;
     k.block = tree;
     k.peer = pos;
     k.rank = tree_rank(n, tree, pos);
-    k.tile = tile;
-    tile_range(g, block_len(g, tree), tile, &k.lo, &k.hi);
+    k.tile = group - shift;
+    tile_range(g, block_len(g, tree), k.tile, &k.lo, &k.hi);
     if (k.hi <= k.lo) k.phase = PH_NONE;
     return k;
   }
