@@ -45,3 +45,20 @@ def ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
         return np.where(v & 0x8000, -mag, mag)
 
     return np.abs(key(a_bits) - key(b_bits))
+
+
+def narrow_rne_f64(x) -> np.ndarray:
+    """fp64 -> bf16 bit patterns, rounded once to nearest even (no detour
+    through fp32, whose own rounding could move a value onto a bf16 tie).
+    bf16 keeps 8 significant bits over fp32's exponent range: a value
+    m * 2**e (0.5 <= |m| < 1) is rounded to a multiple of 2**(e-8), or of
+    2**-133 (the smallest bf16 subnormal) below the normal range."""
+    x = np.asarray(x, dtype=np.float64)
+    finite = np.isfinite(x)
+    _, e = np.frexp(np.where(finite, x, 0.0))
+    q = np.maximum(e - 8, -133)
+    val = np.ldexp(np.rint(np.ldexp(np.where(finite, x, 0.0), -q)), q)  # rint: half to even
+    val = np.where(finite, val, x)
+    with np.errstate(over="ignore"):
+        f32 = val.astype(np.float32)  # exact, or +-inf past the largest bf16
+    return (f32.view(np.uint32) >> 16).astype(np.uint16)
