@@ -38,7 +38,7 @@ STATUS = {
 # Every symbol include/ar.h declares.
 SYMBOLS = (
     "ar_comm_create", "ar_comm_destroy", "ar_comm_check", "ar_comm_reset",
-    "ar_comm_workspace_bytes", "ar_comm_set_max_workgroups", "ar_allreduce", "ar_reduce_scatter", "ar_allgather",
+    "ar_comm_workspace_bytes", "ar_comm_set_max_workgroups", "ar_allreduce", "ar_allreduce_rmsnorm", "ar_reduce_scatter", "ar_allgather",
     "ar_plan_bytes", "ar_select", "ar_debug_inject", "ar_debug_state", "ar_status_string",
 )
 
@@ -62,6 +62,7 @@ def _declare(lib):
     lib.ar_comm_workspace_bytes.argtypes = [P]
     lib.ar_comm_workspace_bytes.restype = S
     lib.ar_comm_set_max_workgroups.argtypes = [P, ctypes.c_uint]
+    lib.ar_allreduce_rmsnorm.argtypes = [P, PP, PP, PP, P, S, S, ctypes.c_float, I, P]
     for name in ("ar_allreduce", "ar_reduce_scatter", "ar_allgather"):
         getattr(lib, name).argtypes = [P, PP, PP, S, I, I, I, S, P]
     lib.ar_plan_bytes.argtypes = [I, I, S, I, I, I, S, I, ctypes.POINTER(U64), ctypes.POINTER(U64),
@@ -174,6 +175,27 @@ class Comm:
         status = getattr(_lib(), name)(self._h, s, r, count, DTYPES[dt], _algo(algo), _proto(proto),
                                        chunk_bytes, _stream_handle(stream))
         _check(status, name)
+
+    def allreduce_rmsnorm(self, send, out, weight, eps=1e-6, residual=None, stream=None):
+        """out[r] = RMSNorm(sum of send[0..N-1] (+ residual[r])) * weight, row by row.
+
+        send / out / residual: N contiguous [rows, hidden] device tensors
+        (residual updated in place, or None); weight: [hidden]."""
+        dt = _dtype_name(send[0])
+        for t in list(send) + list(out) + list(residual or []) + [weight]:
+            if _dtype_name(t) != dt:
+                raise TypeError("all buffers must share one dtype")
+        if send[0].dim() != 2:
+            raise ValueError("rank buffers must be [rows, hidden]")
+        rows, hidden = send[0].shape
+        if weight.numel() != hidden or not weight.is_contiguous() or not weight.is_cuda:
+            raise ValueError("weight must be a contiguous device vector of `hidden` elements")
+        s, o = _ptrs(send, self.nranks, self.device), _ptrs(out, self.nranks, self.device)
+        res = _ptrs(residual, self.nranks, self.device) if residual is not None else None
+        status = _lib().ar_allreduce_rmsnorm(self._h, s, o, res, ctypes.c_void_p(weight.data_ptr()), rows, hidden,
+                                             float(eps), DTYPES[dt], _stream_handle(stream))
+        _check(status, "ar_allreduce_rmsnorm")
+        return out
 
     def allreduce(self, send, recv=None, algo="ring", proto="simple", chunk_bytes=0, stream=None):
         """recv[r] = sum of send[0..N-1]; recv=None runs in place."""

@@ -18,6 +18,7 @@
 #include "../../include/ar.h"
 #include "device.hpp"
 #include "plan.hpp"
+#include "rmsnorm.hpp"
 
 namespace ar {
 hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uint32_t max_workgroups);
@@ -305,6 +306,60 @@ extern "C" {
 ar_status ar_allreduce(ar_comm_t c, const void* const* send, void* const* recv, size_t count, ar_dtype dtype,
                        ar_algo algo, ar_proto proto, size_t chunk_bytes, ar_stream_t stream) {
   return run(c, OP_ALLREDUCE, send, recv, count, dtype, algo, proto, chunk_bytes, stream);
+}
+
+ar_status ar_allreduce_rmsnorm(ar_comm_t c, const void* const* send, void* const* out, void* const* residual,
+                               const void* weight, size_t rows, size_t hidden, float eps, ar_dtype dtype,
+                               ar_stream_t stream) {
+  if (!c || !send || !out) return AR_ERR_INVALID;
+  if (c->broken) return AR_ERR_BROKEN;
+  if ((int)dtype < 0 || (int)dtype > 2) return AR_ERR_INVALID;
+  if (dtype == AR_I32) return AR_ERR_UNSUPPORTED;  // a norm of integers is not defined
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return AR_ERR_INVALID;
+  if (rows == 0 || hidden == 0) return AR_OK;
+  const uint64_t es = (uint64_t)esize_of((int)dtype);
+  if ((hidden * es) % 16) return AR_ERR_INVALID;  // rows of whole 16-byte vectors
+  if (hidden > RMS_MAX_HIDDEN) return AR_ERR_UNSUPPORTED;
+  if (rows > (1ull << 40) / hidden) return AR_ERR_TOO_LARGE;
+  const uint64_t bytes = (uint64_t)rows * hidden * es;
+  if (bytes > c->max_bytes) return AR_ERR_TOO_LARGE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != c->device) return AR_ERR_INVALID;
+  if (!weight || ((uintptr_t)weight & 15)) return AR_ERR_INVALID;
+  const int n = c->nranks;
+  for (int r = 0; r < n; ++r) {
+    if (!send[r] || !out[r] || ((uintptr_t)send[r] & 15) || ((uintptr_t)out[r] & 15)) return AR_ERR_INVALID;
+    if (residual && (!residual[r] || ((uintptr_t)residual[r] & 15))) return AR_ERR_INVALID;
+  }
+  // Outputs and residuals are written: none may overlap another buffer.
+  for (int r = 0; r < n; ++r) {
+    if (overlap(out[r], bytes, weight, hidden * es)) return AR_ERR_INVALID;
+    if (residual && overlap(residual[r], bytes, weight, hidden * es)) return AR_ERR_INVALID;
+    for (int q = 0; q < n; ++q) {
+      if (overlap(out[r], bytes, send[q], bytes)) return AR_ERR_INVALID;
+      if (q != r && overlap(out[r], bytes, out[q], bytes)) return AR_ERR_INVALID;
+      if (residual) {
+        if (overlap(residual[r], bytes, send[q], bytes) || overlap(residual[r], bytes, out[q], bytes))
+          return AR_ERR_INVALID;
+        if (q != r && overlap(residual[r], bytes, residual[q], bytes)) return AR_ERR_INVALID;
+      }
+    }
+  }
+  RmsArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int r = 0; r < n; ++r) {
+    a.in[r] = (const char*)send[r];
+    a.out[r] = (char*)out[r];
+    a.res[r] = residual ? (char*)residual[r] : nullptr;
+  }
+  a.weight = (const char*)weight;
+  a.rows = rows;
+  a.hidden = hidden;
+  a.nranks = n;
+  a.eps = eps;
+  return ar::launch_rmsnorm(a, (int)dtype, c->device, (hipStream_t)stream, c->max_workgroups) == hipSuccess
+             ? AR_OK
+             : AR_ERR_HIP;
 }
 
 ar_status ar_reduce_scatter(ar_comm_t c, const void* const* send, void* const* recv, size_t recvcount,

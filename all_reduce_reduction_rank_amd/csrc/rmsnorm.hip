@@ -1,0 +1,123 @@
+// rmsnorm.hip -- all-reduce with a fused RMSNorm epilogue (one-shot, Simple).
+//
+// "Collective communication: NCCL's algorithms and protocols, and custom
+// all-reduce", section "Source code", names the fused all-reduce + RMSNorm
+// kernel (FlashInfer, integrated by SGLang) as the operation that follows
+// tensor parallelism's all-reduce; fusing it saves writing the sum and
+// reading it back.  For every rank r and row i of a [rows, hidden] buffer:
+//
+//   a = sum of row i over the N ranks, ascending rank order, fp32
+//       accumulate, rounded to the payload type (the one-shot all-reduce)
+//   h = a + residual[r][i]  (fp32 add; h = a without a residual)
+//   residual[r][i] <- h rounded to the payload type
+//   out[r][i] = h * (1 / sqrt(mean(h^2) + eps)) * weight, rounded once
+//
+// One workgroup runs one (row, rank) item at a time: the one-shot sum needs
+// no flags (every input is ready when the kernel starts), and the row's h
+// values wait in LDS between the two passes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.hpp"
+#include "rmsnorm.hpp"
+
+namespace ar {
+
+// The E = 16/esize elements of a 16-byte payload vector as floats.
+template <int DT>
+struct VecF {
+  static constexpr int E = DT == DT_BF16 ? 8 : 4;
+  float v[E];
+  __device__ __forceinline__ static VecF load(const uint4& x) {
+    VecF r;
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == DT_BF16) {
+        r.v[2 * i] = __uint_as_float(w[i] << 16);
+        r.v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      } else {
+        r.v[i] = __uint_as_float(w[i]);
+      }
+    }
+    return r;
+  }
+  __device__ __forceinline__ uint4 store() const {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == DT_BF16) w[i] = bf16_round(v[2 * i]) | (bf16_round(v[2 * i + 1]) << 16);
+      else w[i] = __float_as_uint(v[i]);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+template <int DT>
+__global__ __launch_bounds__(WG_THREADS) void rmsnorm_kernel(RmsArgs a) {
+  extern __shared__ float h_lds[];  // hidden floats: this item's h
+  __shared__ float s_part[WG_THREADS / 64];
+  constexpr int E = VecF<DT>::E;
+  constexpr uint64_t es = DT == DT_BF16 ? 2 : 4;
+  const uint64_t nvec = a.hidden / E;
+  const uint64_t items = a.rows * (uint64_t)a.nranks;
+  const int n = a.nranks;
+  for (uint64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const uint64_t row = item / (uint64_t)n;
+    const int r = (int)(item % (uint64_t)n);
+    const uint64_t base = row * a.hidden * es;
+    float ss = 0.0f;
+    for (uint64_t v = threadIdx.x; v < nvec; v += WG_THREADS) {
+      const uint64_t off = base + v * 16;
+      // one-shot sum in ascending rank order; the N rank programs of a row
+      // re-read the same inputs, so these loads stay cached
+      Vec<DT> acc = Vec<DT>::widen(ld16(a.in[0] + off));
+      for (int j = 1; j < n; ++j) acc.add(Vec<DT>::widen(ld16(a.in[j] + off)));
+      VecF<DT> h = VecF<DT>::load(acc.narrow());  // the all-reduce result, rounded
+      if (a.res[r]) {
+        const VecF<DT> q = VecF<DT>::load(ld16(a.res[r] + off));
+#pragma unroll
+        for (int e = 0; e < E; ++e) h.v[e] = h.v[e] + q.v[e];
+        st16(a.res[r] + off, h.store());
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        h_lds[v * E + e] = h.v[e];
+        ss = ss + h.v[e] * h.v[e];
+      }
+    }
+    // sum of squares over the workgroup: within each wave, then across waves
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = s_part[0];
+#pragma unroll
+    for (int w = 1; w < WG_THREADS / 64; ++w) tot += s_part[w];
+    const float inv = 1.0f / sqrtf(tot / (float)a.hidden + a.eps);
+    for (uint64_t v = threadIdx.x; v < nvec; v += WG_THREADS) {
+      const VecF<DT> w = VecF<DT>::load(ld16(a.weight + v * 16));
+      VecF<DT> o;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o.v[e] = (h_lds[v * E + e] * inv) * w.v[e];
+      st16_hint<true>(a.out[r] + base + v * 16, o.store());
+    }
+    __syncthreads();  // s_part and h_lds are reused by the next item
+  }
+}
+
+hipError_t launch_rmsnorm(const RmsArgs& a, int dtype, int device, hipStream_t stream, uint32_t max_workgroups) {
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) cus = 1;
+  const uint64_t items = a.rows * (uint64_t)a.nranks;
+  uint64_t grid = umin(items, 3ull * (uint64_t)cus);
+  if (max_workgroups) grid = umin(grid, (uint64_t)max_workgroups);
+  if (grid < 1) grid = 1;
+  const size_t lds = (size_t)a.hidden * sizeof(float);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(rmsnorm_kernel<DT_BF16>, dim3((unsigned)grid), dim3(WG_THREADS), lds, stream, a);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<DT_F32>, dim3((unsigned)grid), dim3(WG_THREADS), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace ar

@@ -139,6 +139,30 @@ ar_status ar_allreduce(ar_comm_t comm, const void* const* sendbufs, void* const*
                        size_t count, ar_dtype dtype, ar_algo algo, ar_proto proto,
                        size_t chunk_bytes, ar_stream_t stream);
 
+/* All-reduce with a fused RMSNorm epilogue ([H] "Source code": the fused
+ * all-reduce + RMSNorm kernel that follows tensor parallelism's all-reduce).
+ * Each rank buffer is a row-major [rows, hidden] matrix of `dtype` (AR_F32
+ * or AR_BF16; AR_I32 returns AR_ERR_UNSUPPORTED).  For every rank r, row i:
+ *   a = the one-shot all-reduce of row i (ascending rank order, fp32
+ *       accumulate, rounded to dtype once: the same bits ar_allreduce gives);
+ *   h = a + residualbufs[r][i] in fp32 (h = a when residualbufs is NULL);
+ *   residualbufs[r][i] <- h rounded to dtype (in place);
+ *   outbufs[r][i] = h * (1 / sqrt(mean(h*h) + eps)) * weight, in fp32,
+ *       rounded once to dtype.
+ * `weight`: one DEVICE vector of `hidden` dtype elements shared by all ranks.
+ * `residualbufs`: NULL, or a HOST array of N DEVICE pointers (rows*hidden
+ * each).  hidden*esize must be a multiple of 16 and hidden <= 12288; every
+ * pointer 16-byte aligned; outputs and residuals must not overlap any other
+ * buffer of the call (out of place only).  rows*hidden*esize must fit the
+ * communicator's max_bytes_per_rank.  No device waits: one kernel, each
+ * workgroup normalizing one (row, rank) at a time.  rows or hidden 0:
+ * AR_OK, nothing done.
+ * Errors: AR_ERR_INVALID, AR_ERR_UNSUPPORTED, AR_ERR_TOO_LARGE,
+ * AR_ERR_BROKEN, AR_ERR_HIP. */
+ar_status ar_allreduce_rmsnorm(ar_comm_t comm, const void* const* sendbufs, void* const* outbufs,
+                               void* const* residualbufs, const void* weight, size_t rows, size_t hidden,
+                               float eps, ar_dtype dtype, ar_stream_t stream);
+
 /* Reduce-scatter (SUM): sendbufs[i] holds N*recvcount elements; recvbufs[r]
  * (recvcount elements) receives sum_i sendbufs[i][r*recvcount ...]
  * ([Q] "Direct answer").  ONESHOT/TWOSHOT: direct, rank r sums in rank order;
