@@ -44,6 +44,12 @@ WORKLOADS = {
     # integer path: N=8 int32, 64 MiB per rank
     "int32-64MiB-ring": dict(op="allreduce", nranks=8, bytes=64 << 20, dtype="i32", dist="int20",
                              algo="ring", proto="simple", chunk=512 << 10),
+    # the same TP activations with the fused RMSNorm epilogue (residual add,
+    # weight [5120]); one-shot sum
+    "tp-decode-t1-rmsnorm": dict(op="allreduce_rmsnorm", nranks=8, bytes=1 * 5120 * 2, rows=1, hidden=5120,
+                                 dtype="bf16", dist="normal", algo="oneshot", proto="simple", chunk=0),
+    "tp-prefill-t512-rmsnorm": dict(op="allreduce_rmsnorm", nranks=8, bytes=512 * 5120 * 2, rows=512, hidden=5120,
+                                    dtype="bf16", dist="normal", algo="oneshot", proto="simple", chunk=0),
     # calibration: one rank, whose all-reduce is a copy of 256 MiB (read S,
     # write S); its counter readings scale the others' to bytes
     "copy-256MiB": dict(op="allreduce", nranks=1, bytes=256 << 20, dtype="f32", dist="normal",
@@ -56,14 +62,24 @@ from all_reduce_reduction_rank_amd.profiling import kernel_hash  # noqa: E402
 
 
 def busbw_factor(op, n):
-    return 2 * (n - 1) / n if op == "allreduce" else (n - 1) / n
+    return 2 * (n - 1) / n if op in ("allreduce", "allreduce_rmsnorm") else (n - 1) / n
+
+
+def fused_hbm_bytes(w):
+    """Algorithmic HBM bytes of one fused all-reduce + RMSNorm call.  Each of
+    the N rank programs, for each row, reads the row of the N inputs, its
+    residual and the weight, and writes its residual and its output: N (N + 4) S
+    with S = rows * hidden * esize per rank."""
+    n, s = w["nranks"], w["bytes"]
+    return n * (n + 4) * s
 
 
 def counts(w):
+    """(count argument of the call, input elements, output elements) per rank."""
     es = {"f32": 4, "bf16": 2, "i32": 4}[w["dtype"]]
     n = w["nranks"]
-    if w["op"] == "allreduce":
-        return w["bytes"] // es, w["bytes"] // es, w["bytes"] // es   # count, in elems, out elems
+    if w["op"] in ("allreduce", "allreduce_rmsnorm"):
+        return w["bytes"] // es, w["bytes"] // es, w["bytes"] // es
     per = w["bytes"] // es // n
     if w["op"] == "reduce_scatter":
         return per, n * per, per
@@ -95,15 +111,27 @@ def cpu_baseline(w, min_seconds):
     from oracle import collectives
 
     es = {"f32": 4, "bf16": 2, "i32": 4}[w["dtype"]]
-    sample_bytes = min(w["bytes"], 32 << 20)
     n = w["nranks"]
-    per = sample_bytes // es
-    if w["op"] != "allreduce":
-        per //= n
-    host = inputs.rank_inputs(n, per if w["op"] != "reduce_scatter" else n * per, w["dtype"], w["dist"],
-                              seed=1, cfg=9)
-    fn = {"allreduce": collectives.allreduce, "reduce_scatter": collectives.reduce_scatter,
-          "allgather": collectives.allgather}[w["op"]]
+    if w["op"] == "allreduce_rmsnorm":
+        from oracle import fused
+
+        rows = max(1, min(w["rows"], 64))  # a bounded sample of the rows
+        sample_bytes = rows * w["hidden"] * es
+        host = inputs.rank_inputs(n, rows * w["hidden"], w["dtype"], w["dist"], seed=1, cfg=9)
+        res = inputs.rank_inputs(n, rows * w["hidden"], w["dtype"], w["dist"], seed=2, cfg=9)
+        weight = inputs.rank_inputs(1, w["hidden"], w["dtype"], w["dist"], seed=3, cfg=9)[0]
+
+        def fn(x, dt, algo, chunk_bytes=0):
+            fused.allreduce_rmsnorm(x, res, weight, rows, w["hidden"], 1e-5, dt)
+    else:
+        sample_bytes = min(w["bytes"], 32 << 20)
+        per = sample_bytes // es
+        if w["op"] != "allreduce":
+            per //= n
+        host = inputs.rank_inputs(n, per if w["op"] != "reduce_scatter" else n * per, w["dtype"], w["dist"],
+                                  seed=1, cfg=9)
+        fn = {"allreduce": collectives.allreduce, "reduce_scatter": collectives.reduce_scatter,
+              "allgather": collectives.allgather}[w["op"]]
     reps, t0 = 0, time.perf_counter()
     while True:
         fn(host, w["dtype"], w["algo"], chunk_bytes=w["chunk"] or collectives.DEFAULT_CHUNK_BYTES)
@@ -116,7 +144,7 @@ def cpu_baseline(w, min_seconds):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{w['op']} {w['algo']} N={n} {w['dtype']} {w['dist']}, {sample_bytes >> 20} MiB per rank, "
+        "sample": f"{w['op']} {w['algo']} N={n} {w['dtype']} {w['dist']}, {sample_bytes / 2**20:.3g} MiB per rank, "
                   f"{reps} calls in {el:.1f} s (NumPy, single thread)",
     }
 
@@ -158,11 +186,21 @@ def main():
         w["algo"], w["proto"], _ = select(n, op, count, dt, w["algo"], w["proto"], line_cap)
     send = inputs.device_rank_inputs(n, n_in, dt, w["dist"], seed=0, cfg=4)
     recv = [torch.empty(n_out, dtype=send[0].dtype, device="cuda") for _ in range(n)]
-    comm = Comm(n, w["bytes"], line_cap)
+    comm = Comm(n, w["bytes"], line_cap if op != "allreduce_rmsnorm" else 0)
     if args.max_workgroups:
         comm.set_max_workgroups(args.max_workgroups)
-    call = getattr(comm, op)
     stream = torch.cuda.current_stream()
+    if op == "allreduce_rmsnorm":
+        rows, hidden = w["rows"], w["hidden"]
+        send = [t.view(rows, hidden) for t in send]
+        recv = [t.view(rows, hidden) for t in recv]
+        residual = [t.view(rows, hidden) for t in inputs.device_rank_inputs(n, n_in, dt, w["dist"], seed=1, cfg=4)]
+        weight = inputs.device_rank_inputs(1, hidden, dt, w["dist"], seed=2, cfg=4)[0]
+
+        def call(s_, r_, algo=None, proto=None, chunk_bytes=0, stream=None):
+            comm.allreduce_rmsnorm(s_, r_, weight, eps=1e-5, residual=residual, stream=stream)
+    else:
+        call = getattr(comm, op)
 
     def step():
         call(send, recv, algo=req_algo, proto=req_proto, chunk_bytes=w["chunk"], stream=stream)
@@ -215,7 +253,10 @@ def main():
 
     s = w["bytes"]
     t = ms / 1e3
-    plan = plan_bytes(n, op, count, dt, w["algo"], w["proto"], chunk_bytes=w["chunk"])
+    if op == "allreduce_rmsnorm":
+        plan = {"hbm": fused_hbm_bytes(w)}
+    else:
+        plan = plan_bytes(n, op, count, dt, w["algo"], w["proto"], chunk_bytes=w["chunk"])
     algbw = s / t / 1e9
     achieved = plan["hbm"] / t / 1e9
     traffic = traffic_from_profile(traffic_name(args.workload, w))

@@ -1,0 +1,43 @@
+"""Host logic of bench.py (no GPU): workload sizes, byte models and the
+one-GPU contract."""
+
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_counts_per_operation():
+    w = dict(op="allreduce", nranks=8, bytes=1 << 20, dtype="f32")
+    assert bench.counts(w) == (1 << 18, 1 << 18, 1 << 18)
+    w = dict(op="reduce_scatter", nranks=8, bytes=1 << 20, dtype="bf16")
+    assert bench.counts(w) == (1 << 16, 1 << 19, 1 << 16)
+    w = dict(op="allgather", nranks=4, bytes=1 << 20, dtype="i32")
+    assert bench.counts(w) == (1 << 16, 1 << 16, 1 << 18)
+
+
+def test_every_workload_is_well_formed():
+    for name, w in bench.WORKLOADS.items():
+        count, n_in, n_out = bench.counts(w)
+        assert count > 0 and n_in > 0 and n_out > 0, name
+        if w["op"] == "allreduce_rmsnorm":
+            assert w["rows"] * w["hidden"] * 2 == w["bytes"], name
+            assert bench.fused_hbm_bytes(w) == w["nranks"] * (w["nranks"] + 4) * w["bytes"]
+
+
+def test_busbw_factors():
+    assert bench.busbw_factor("allreduce", 8) == 2 * 7 / 8
+    assert bench.busbw_factor("allgather", 8) == 7 / 8
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2 and "one GPU" in res.stderr
+
+
+def test_kernel_hash_is_stable():
+    assert bench.kernel_hash() == bench.kernel_hash() and len(bench.kernel_hash()) == 16
