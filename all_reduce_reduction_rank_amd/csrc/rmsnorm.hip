@@ -14,7 +14,7 @@
 //
 // One workgroup runs one (row, rank) item at a time: the one-shot sum needs
 // no flags (every input is ready when the kernel starts), and the row's h
-// values wait in LDS between the two passes.
+// values wait in registers between the two passes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,10 +55,12 @@ struct VecF {
 
 template <int DT>
 __global__ __launch_bounds__(WG_THREADS) void rmsnorm_kernel(RmsArgs a) {
-  extern __shared__ float h_lds[];  // hidden floats: this item's h
-  __shared__ float s_part[WG_THREADS / 64];
   constexpr int E = VecF<DT>::E;
+  // vectors of a row each thread holds at most: the row's h stays in
+  // registers (48 floats per thread at the largest hidden size)
+  constexpr int VPT = (int)(RMS_MAX_HIDDEN / E / WG_THREADS);
   constexpr uint64_t es = DT == DT_BF16 ? 2 : 4;
+  __shared__ float s_part[WG_THREADS / 64];
   const uint64_t nvec = a.hidden / E;
   const uint64_t items = a.rows * (uint64_t)a.nranks;
   const int n = a.nranks;
@@ -66,24 +68,33 @@ __global__ __launch_bounds__(WG_THREADS) void rmsnorm_kernel(RmsArgs a) {
     const uint64_t row = item / (uint64_t)n;
     const int r = (int)(item % (uint64_t)n);
     const uint64_t base = row * a.hidden * es;
+    char* res = a.res[r];
+    VecF<DT> h[VPT];
     float ss = 0.0f;
-    for (uint64_t v = threadIdx.x; v < nvec; v += WG_THREADS) {
-      const uint64_t off = base + v * 16;
-      // one-shot sum in ascending rank order; the N rank programs of a row
-      // re-read the same inputs, so these loads stay cached
-      Vec<DT> acc = Vec<DT>::widen(ld16(a.in[0] + off));
-      for (int j = 1; j < n; ++j) acc.add(Vec<DT>::widen(ld16(a.in[j] + off)));
-      VecF<DT> h = VecF<DT>::load(acc.narrow());  // the all-reduce result, rounded
-      if (a.res[r]) {
-        const VecF<DT> q = VecF<DT>::load(ld16(a.res[r] + off));
 #pragma unroll
-        for (int e = 0; e < E; ++e) h.v[e] = h.v[e] + q.v[e];
-        st16(a.res[r] + off, h.store());
-      }
+    for (int i = 0; i < VPT; ++i) {
+      const uint64_t v = threadIdx.x + (uint64_t)i * WG_THREADS;
+      if (v < nvec) {
+        const uint64_t off = base + v * 16;
+        // all N loads in flight, then the sum in ascending rank order; the N
+        // rank programs of a row re-read the same inputs, so these stay cached
+        uint4 x[MAX_RANKS];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        h_lds[v * E + e] = h.v[e];
-        ss = ss + h.v[e] * h.v[e];
+        for (int j = 0; j < MAX_RANKS; ++j)
+          if (j < n) x[j] = ld16(a.in[j] + off);
+        Vec<DT> acc = Vec<DT>::widen(x[0]);
+#pragma unroll
+        for (int j = 1; j < MAX_RANKS; ++j)
+          if (j < n) acc.add(Vec<DT>::widen(x[j]));
+        h[i] = VecF<DT>::load(acc.narrow());  // the all-reduce result, rounded
+        if (res) {
+          const VecF<DT> q = VecF<DT>::load(ld16(res + off));
+#pragma unroll
+          for (int e = 0; e < E; ++e) h[i].v[e] = h[i].v[e] + q.v[e];
+          st16(res + off, h[i].store());
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) ss = ss + h[i].v[e] * h[i].v[e];
       }
     }
     // sum of squares over the workgroup: within each wave, then across waves
@@ -94,14 +105,18 @@ __global__ __launch_bounds__(WG_THREADS) void rmsnorm_kernel(RmsArgs a) {
 #pragma unroll
     for (int w = 1; w < WG_THREADS / 64; ++w) tot += s_part[w];
     const float inv = 1.0f / sqrtf(tot / (float)a.hidden + a.eps);
-    for (uint64_t v = threadIdx.x; v < nvec; v += WG_THREADS) {
-      const VecF<DT> w = VecF<DT>::load(ld16(a.weight + v * 16));
-      VecF<DT> o;
 #pragma unroll
-      for (int e = 0; e < E; ++e) o.v[e] = (h_lds[v * E + e] * inv) * w.v[e];
-      st16_hint<true>(a.out[r] + base + v * 16, o.store());
+    for (int i = 0; i < VPT; ++i) {
+      const uint64_t v = threadIdx.x + (uint64_t)i * WG_THREADS;
+      if (v < nvec) {
+        const VecF<DT> w = VecF<DT>::load(ld16(a.weight + v * 16));
+        VecF<DT> o;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o.v[e] = (h[i].v[e] * inv) * w.v[e];
+        st16_hint<true>(a.out[r] + base + v * 16, o.store());
+      }
     }
-    __syncthreads();  // s_part and h_lds are reused by the next item
+    __syncthreads();  // s_part is reused by the next item
   }
 }
 
@@ -112,11 +127,10 @@ hipError_t launch_rmsnorm(const RmsArgs& a, int dtype, int device, hipStream_t s
   uint64_t grid = umin(items, 3ull * (uint64_t)cus);
   if (max_workgroups) grid = umin(grid, (uint64_t)max_workgroups);
   if (grid < 1) grid = 1;
-  const size_t lds = (size_t)a.hidden * sizeof(float);
   if (dtype == DT_BF16)
-    hipLaunchKernelGGL(rmsnorm_kernel<DT_BF16>, dim3((unsigned)grid), dim3(WG_THREADS), lds, stream, a);
+    hipLaunchKernelGGL(rmsnorm_kernel<DT_BF16>, dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<DT_F32>, dim3((unsigned)grid), dim3(WG_THREADS), lds, stream, a);
+    hipLaunchKernelGGL(rmsnorm_kernel<DT_F32>, dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -9,7 +9,7 @@
 
 namespace ar {
 
-constexpr uint64_t RMS_MAX_HIDDEN = 12288;  // fp32 h of one row in LDS: 48 KiB
+constexpr uint64_t RMS_MAX_HIDDEN = 12288;  // a row's fp32 h in registers: 48 floats per thread
 
 struct RmsArgs {
   const char* in[MAX_RANKS];

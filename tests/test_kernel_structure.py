@@ -117,3 +117,16 @@ def test_no_spills_to_memory(asm):
     spills = re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm)
     assert spills and all(int(x) == 0 for x in spills)
     assert not re.search(r"^\s+scratch_(load|store)", asm, re.M)
+
+
+def test_fused_rmsnorm_kernel_keeps_its_row_in_registers(tmp_path):
+    out = tmp_path / "rmsnorm.s"
+    src = os.path.join(ROOT, "all_reduce_reduction_rank_amd", "csrc", "rmsnorm.hip")
+    cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-S", "--cuda-device-only",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", str(out), src]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    text = out.read_text()
+    spills = re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)
+    assert len(spills) == 2 and all(int(x) == 0 for x in spills)
+    assert not re.search(r"^\s+scratch_(load|store)", text, re.M)
