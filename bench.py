@@ -103,7 +103,39 @@ def traffic_from_profile(name):
     return rec.get("hbm_bytes_per_call")
 
 
-def cpu_baseline(w, min_seconds):
+def cpu_threads():
+    """Host threads the threaded oracle run uses: the cores this process may
+    run on, at most 16 (a GPU machine's CPU share)."""
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return max(1, min(16, os.cpu_count() or 1))
+
+
+def cpu_baseline_threaded(w, min_seconds, threads):
+    """T copies of the single-thread sample run side by side on T host
+    threads (NumPy releases the GIL in its loops), each on its own inputs:
+    the throughput the oracle reaches when every core runs it."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(_):
+        return cpu_baseline(w, min_seconds, seed=1 + _)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as pool:
+        runs = list(pool.map(one, range(threads)))
+    el = time.perf_counter() - t0
+    total = sum(r["_bytes"] for r in runs)
+    return {
+        "value": round(total / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{threads} threads, each: " + runs[0]["sample"],
+    }
+
+
+def cpu_baseline(w, min_seconds, seed=1):
     """The oracle as it stands, on a bounded sample: the same collective on
     the same N and distribution, 32 MiB per rank (or the workload's size if
     smaller), repeated until `min_seconds` have passed."""
@@ -117,8 +149,8 @@ def cpu_baseline(w, min_seconds):
 
         rows = max(1, min(w["rows"], 64))  # a bounded sample of the rows
         sample_bytes = rows * w["hidden"] * es
-        host = inputs.rank_inputs(n, rows * w["hidden"], w["dtype"], w["dist"], seed=1, cfg=9)
-        res = inputs.rank_inputs(n, rows * w["hidden"], w["dtype"], w["dist"], seed=2, cfg=9)
+        host = inputs.rank_inputs(n, rows * w["hidden"], w["dtype"], w["dist"], seed=seed, cfg=9)
+        res = inputs.rank_inputs(n, rows * w["hidden"], w["dtype"], w["dist"], seed=seed + 1000, cfg=9)
         weight = inputs.rank_inputs(1, w["hidden"], w["dtype"], w["dist"], seed=3, cfg=9)[0]
 
         def fn(x, dt, algo, chunk_bytes=0):
@@ -129,7 +161,7 @@ def cpu_baseline(w, min_seconds):
         if w["op"] != "allreduce":
             per //= n
         host = inputs.rank_inputs(n, per if w["op"] != "reduce_scatter" else n * per, w["dtype"], w["dist"],
-                                  seed=1, cfg=9)
+                                  seed=seed, cfg=9)
         fn = {"allreduce": collectives.allreduce, "reduce_scatter": collectives.reduce_scatter,
               "allgather": collectives.allgather}[w["op"]]
     reps, t0 = 0, time.perf_counter()
@@ -140,6 +172,7 @@ def cpu_baseline(w, min_seconds):
         if el >= min_seconds:
             break
     return {
+        "_bytes": sample_bytes * reps,
         "value": round(sample_bytes * reps / el / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
@@ -301,7 +334,12 @@ def main():
         out["hbm_measured_GBps"] = round(traffic / t / 1e9, 1)
         out["hbm_measured_frac"] = round(traffic / t / 1e9 / HBM_PEAK_GBPS, 4)
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        # the oracle as it stands (one thread), then T copies side by side
+        base = cpu_baseline(w, args.cpu_seconds / 2)
+        base.pop("_bytes")
+        out["cpu_baseline"] = base
+        threaded = cpu_baseline_threaded(w, args.cpu_seconds / 2, cpu_threads())
+        out["cpu_baseline_threads"] = threaded
     comm.close()
     print(json.dumps(out))
 
