@@ -664,9 +664,20 @@ template <int DT, int PROTO, int KIND>
 __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
   __shared__ uint64_t s_epoch;
   __shared__ uint32_t s_ticket;
-  if (threadIdx.x == 0) s_epoch = __hip_atomic_load(&a.ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // A call that starts with the abort word set (an earlier call's latched
+  // error) runs nothing.  An abort raised during the call is seen by the
+  // waits, so the fetches below need not read it: the first fetch then goes
+  // out together with these two loads, one round trip for all three.
+  uint32_t aborted = 0;
+  if (threadIdx.x == 0) {
+    s_epoch = __hip_atomic_load(&a.ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    aborted = ld_u32(&a.ctl->abort);
+  }
   const uint32_t ntasks = (uint32_t)a.g.ntasks;
   const uint32_t batch = a.batch;
+  // When the grid's first fetches cover every ticket, each workgroup
+  // fetches once: a second fetch could only come back empty.
+  const bool one_fetch = (uint64_t)gridDim.x * batch >= (uint64_t)ntasks;
   uint32_t finished = 0;  // tasks this workgroup ran (diagnostics)
   bool more = true;
   while (more) {
@@ -677,10 +688,8 @@ __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
     // take every later ticket and wait on tickets held by workgroups that
     // cannot be dispatched until one of them exits.
     if (threadIdx.x == 0) {
-      uint32_t t = 0xffffffffu;
-      if (!ld_u32(&a.ctl->abort))
-        t = __hip_atomic_fetch_add(&a.ctl->ticket, batch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_ticket = t;
+      const uint32_t t = __hip_atomic_fetch_add(&a.ctl->ticket, batch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_ticket = aborted ? 0xffffffffu : t;
     }
     __syncthreads();
     // Broadcast through readfirstlane so every branch below is a scalar
@@ -703,7 +712,7 @@ __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
     }
     // Tickets are handed out in increasing order: once a batch reaches the
     // end, every later fetch would come back empty.
-    if (first >= ntasks || ntasks - first <= batch) more = false;
+    if (one_fetch || first >= ntasks || ntasks - first <= batch) more = false;
   }
   if (threadIdx.x == 0) {
     // Relaxed is enough: every ticket fetch and the epoch load of this
