@@ -15,6 +15,8 @@
 // follow the former page's section "Protocols" (see device.hpp).
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "device.hpp"
 #include "plan.hpp"
 
@@ -786,16 +788,22 @@ KernelFn pick_kernel(int dtype, int proto, int kind) {
 // More resident workgroups than this only add polling and contention.
 constexpr int DEFAULT_WG_PER_CU = 3;
 
-// Workgroups of kernel f a call may run at once on `device`: those that fit
-// (occupancy x CUs), at most DEFAULT_WG_PER_CU per CU (cached per kernel).
+// Workgroups of kernel f a call may run at once on `device` (the current
+// device): those that fit (occupancy x CUs), at most DEFAULT_WG_PER_CU per
+// CU.  Cached per (kernel, device); safe to call from several host threads.
 int resident_workgroups(KernelFn f, int device) {
-  static KernelFn seen[64];
-  static int count[64];
+  struct Entry {
+    KernelFn f;
+    int device, count;
+  };
+  static std::mutex mu;
+  static Entry seen[256];
   static int used = 0;
-  static int dev_seen = -1;
-  if (dev_seen != device) { used = 0; dev_seen = device; }
-  for (int i = 0; i < used; ++i)
-    if (seen[i] == f) return count[i];
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (seen[i].f == f && seen[i].device == device) return seen[i].count;
+  }
   int per_cu = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)f, WG_THREADS, 0) != hipSuccess)
     per_cu = 1;
@@ -803,7 +811,8 @@ int resident_workgroups(KernelFn f, int device) {
   if (per_cu < 1) per_cu = 1;
   if (per_cu > DEFAULT_WG_PER_CU) per_cu = DEFAULT_WG_PER_CU;
   const int total = per_cu * cus;
-  if (used < 64) { seen[used] = f; count[used] = total; ++used; }
+  std::lock_guard<std::mutex> lock(mu);
+  if (used < 256) seen[used++] = {f, device, total};
   return total;
 }
 
