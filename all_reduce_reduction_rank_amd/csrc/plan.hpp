@@ -113,17 +113,23 @@ struct Tuning {
 
 // Tile size in bytes for a per-rank buffer of `rank_bytes`: aim for >= 128
 // tiles per rank so a call spreads over the 256 CUs, within per-schedule
-// bounds.  Simple: 32 KiB on the ring and two-shot (measured at 256 MiB,
-// N=8 fp32: ring 0.87 of HBM peak at 32 KiB against 0.79 at 64 KiB and 0.72
-// at 128 KiB; two-shot equal at 32 and 128 KiB, and 23% faster at 25 MiB
-// with 32 KiB), 128 KiB for one-shot (each task reads N tiles) and the
-// direct reduce-scatter / all-gather, 16 KiB for the in-place one-shot (its
-// tile lives in registers).  LL up to 16 KiB; LL128 whole wave passes.
+// bounds measured at N=8 fp32 (fractions of HBM peak, default grid):
+//   ring, tree    32 KiB  (ring 256 MiB: 0.87 at 32 KiB, 0.79 at 64, 0.72 at 128)
+//   two-shot      64 KiB from 64 MiB per rank (256 MiB: 0.91 against 0.86 at
+//                 32 KiB), else 32 KiB (25 MiB: 0.59 against 0.56 at 64 KiB)
+//   one-shot      128 KiB (each task reads N tiles; 256 MiB: 1.59 ms against
+//                 1.63 at 64 KiB and 1.96 at 32 KiB); 16 KiB in place (the
+//                 tile lives in registers)
+//   RS direct     16 KiB (256 MiB: 0.72 against 0.62 at 128 KiB)
+//   AG direct     16 KiB (256 MiB: 409 us against 467 at 128 KiB)
+// LL up to 16 KiB; LL128 whole wave passes.
 inline uint64_t pick_tile_bytes(int proto, uint64_t rank_bytes, int kind, bool in_place) {
   const uint64_t want = floor_pow2(rank_bytes / 128 + 1);
   if (proto == PROTO_SIMPLE) {
     uint64_t hi = 131072;
-    if (kind == K_RING || kind == K_TWOSHOT || kind == K_TREE) hi = 32768;
+    if (kind == K_RING || kind == K_TREE) hi = 32768;
+    if (kind == K_TWOSHOT) hi = rank_bytes >= (64ull << 20) ? 65536 : 32768;
+    if (kind == K_RS_DIRECT || kind == K_AG_DIRECT) hi = 16384;
     if (kind == K_ONESHOT && in_place) hi = 16384;
     return clampu(want, 4096, hi);
   }

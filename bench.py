@@ -44,6 +44,12 @@ WORKLOADS = {
     # integer path: N=8 int32, 64 MiB per rank
     "int32-64MiB-ring": dict(op="allreduce", nranks=8, bytes=64 << 20, dtype="i32", dist="int20",
                              algo="ring", proto="simple", chunk=512 << 10),
+    # reduce-scatter and all-gather of 256 MiB per rank (the full per-rank
+    # buffer: RS sends it and keeps 1/N, AG receives it), N=8 fp32, direct
+    "rs-256MiB": dict(op="reduce_scatter", nranks=8, bytes=256 << 20, dtype="f32", dist="normal",
+                      algo="oneshot", proto="simple", chunk=512 << 10),
+    "ag-256MiB": dict(op="allgather", nranks=8, bytes=256 << 20, dtype="f32", dist="normal",
+                      algo="oneshot", proto="simple", chunk=512 << 10),
     # the same TP activations with the fused RMSNorm epilogue (residual add,
     # weight [5120]); one-shot sum
     "tp-decode-t1-rmsnorm": dict(op="allreduce_rmsnorm", nranks=8, bytes=1 * 5120 * 2, rows=1, hidden=5120,
