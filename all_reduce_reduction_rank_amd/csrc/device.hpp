@@ -279,6 +279,8 @@ struct KArgs {
   uint64_t timeout;     // wall-clock ticks (100 MHz) a wait may last
   int32_t inj_rank, inj_step;
   uint32_t batch;       // tickets a workgroup takes per fetch
+  uint32_t fixed;       // 1: workgroup b runs tickets [b*batch, (b+1)*batch) and
+                        //    touches no counter (tasks that never wait, one pass)
 };
 
 __device__ __forceinline__ void note_blocked(Ctl* c, int step, int rank) {

@@ -53,7 +53,13 @@ struct VecF {
   }
 };
 
-template <int DT>
+// EARLY_W: the weights' loads go out with the inputs' (the weights do not
+// depend on the sum), so a row costs one round trip to memory, not two.
+// Chosen when every workgroup runs one row at most (decode): there latency
+// is all.  With several rows per workgroup (prefill) the extra registers and
+// loads in flight measured 3 % slower, and at fp32 (twice the vectors per
+// row) they would cut residency from 3 to 2 workgroups per CU.
+template <int DT, bool EARLY_W>
 __global__ __launch_bounds__(WG_THREADS) void rmsnorm_kernel(RmsArgs a) {
   constexpr int E = VecF<DT>::E;
   // vectors of a row each thread holds at most: the row's h stays in
@@ -70,12 +76,14 @@ __global__ __launch_bounds__(WG_THREADS) void rmsnorm_kernel(RmsArgs a) {
     const uint64_t base = row * a.hidden * es;
     char* res = a.res[r];
     VecF<DT> h[VPT];
+    uint4 wv[EARLY_W ? VPT : 1];
     float ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const uint64_t v = threadIdx.x + (uint64_t)i * WG_THREADS;
       if (v < nvec) {
         const uint64_t off = base + v * 16;
+        if constexpr (EARLY_W) wv[i] = ld16(a.weight + v * 16);
         // all N loads in flight, then the sum in ascending rank order; the N
         // rank programs of a row re-read the same inputs, so these stay cached
         uint4 x[MAX_RANKS];
@@ -109,7 +117,7 @@ __global__ __launch_bounds__(WG_THREADS) void rmsnorm_kernel(RmsArgs a) {
     for (int i = 0; i < VPT; ++i) {
       const uint64_t v = threadIdx.x + (uint64_t)i * WG_THREADS;
       if (v < nvec) {
-        const VecF<DT> w = VecF<DT>::load(ld16(a.weight + v * 16));
+        const VecF<DT> w = VecF<DT>::load(EARLY_W ? wv[EARLY_W ? i : 0] : ld16(a.weight + v * 16));
         VecF<DT> o;
 #pragma unroll
         for (int e = 0; e < E; ++e) o.v[e] = (h[i].v[e] * inv) * w.v[e];
@@ -127,10 +135,13 @@ hipError_t launch_rmsnorm(const RmsArgs& a, int dtype, int device, hipStream_t s
   uint64_t grid = umin(items, 3ull * (uint64_t)cus);
   if (max_workgroups) grid = umin(grid, (uint64_t)max_workgroups);
   if (grid < 1) grid = 1;
-  if (dtype == DT_BF16)
-    hipLaunchKernelGGL(rmsnorm_kernel<DT_BF16>, dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL(rmsnorm_kernel<DT_F32>, dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, a);
+  const bool one_row = items <= grid;
+  if (dtype == DT_BF16) {
+    if (one_row) hipLaunchKernelGGL((rmsnorm_kernel<DT_BF16, true>), dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, a);
+    else hipLaunchKernelGGL((rmsnorm_kernel<DT_BF16, false>), dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((rmsnorm_kernel<DT_F32, false>), dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

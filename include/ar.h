@@ -36,7 +36,11 @@
  *   - Errors: argument errors return at once and launch nothing.  A device
  *     wait that exceeds the communicator's time limit stops the call, latches
  *     AR_ERR_TIMEOUT in device memory and makes later calls no-ops until
- *     ar_comm_reset; ar_comm_check reports it.  Nothing is printed.
+ *     ar_comm_reset; ar_comm_check reports it.  The exception: a call that
+ *     cannot wait (Simple one-shot out of place, direct reduce-scatter or
+ *     all-gather, small enough that one grid covers all its tiles) still
+ *     runs in full.  Once ar_comm_check has seen the error, every call
+ *     returns AR_ERR_BROKEN until ar_comm_reset.  Nothing is printed.
  */
 #ifndef AR_H
 #define AR_H
@@ -237,7 +241,9 @@ ar_status ar_debug_inject(ar_comm_t comm, int rank, int step, uint64_t timeout_u
  * communicator's device control block into out: [0] timed-out waits,
  * [1] flag index, [2] value seen and [3] value awaited by the first of them,
  * [4] the call counter then, [5] tasks finished (all calls), [6] calls
- * completed, [7] ticket counter, [8] finished workgroups, [9] abort word. */
+ * completed, [7] ticket counter, [8] finished workgroups, [9] abort word.
+ * Calls that cannot wait and run without the ticket counter (see Errors
+ * above) add to neither [5] nor [6]. */
 ar_status ar_debug_state(ar_comm_t comm, ar_stream_t stream, uint64_t* out, int n);
 
 /* Static description of a status code. */

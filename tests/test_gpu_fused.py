@@ -69,7 +69,9 @@ def run_fused(n, rows, hidden, dt, with_residual, eps=1e-6, seed=0, comm=None, z
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("n", [1, 2, 4, 8])
 def test_fused_matches_oracle(n, dt):
-    for rows, hidden in ((1, 5120), (7, 640), (64, 5120), (3, 12288), (5, 8)):
+    # (160, 1024): at N=8, 1280 (row, rank) items, more than one per
+    # workgroup of the grid -- the kernel then loads the weights after the sum
+    for rows, hidden in ((1, 5120), (7, 640), (64, 5120), (3, 12288), (5, 8), (160, 1024)):
         if hidden * (2 if dt == "bf16" else 4) % 16:
             continue
         run_fused(n, rows, hidden, dt, with_residual=False, seed=rows)

@@ -266,6 +266,60 @@ def test_argument_errors_are_reported():
     assert c.check()[0] == "AR_OK"
 
 
+
+def test_calls_that_never_wait_touch_no_counter():
+    # One-shot (out of place), direct reduce-scatter and all-gather with
+    # Simple never wait; when the grid covers every task they run without
+    # the ticket counter and leave the call counter where it was.  Calls
+    # that do wait still advance it by one.
+    n, dt = 8, "bf16"
+    c = Comm(n, 1 << 20, 0)
+    host = inputs.rank_inputs(n, 4096, dt, "normal", seed=7)
+    send = [to_dev(x, dt) for x in host]
+    recv = [empty(4096, dt) for _ in range(n)]
+    _say("never-wait counters")
+    before = c.debug_state()
+    c.allreduce(send, recv, algo="oneshot")
+    c.reduce_scatter(send, [empty(4096 // n, dt) for _ in range(n)], algo="oneshot")
+    c.allgather([t[:512] for t in send], [empty(512 * n, dt) for _ in range(n)], algo="oneshot")
+    mid = c.debug_state()
+    assert (mid["calls"], mid["ticket"], mid["done"], mid["tasks_done"]) == \
+        (before["calls"], 0, 0, before["tasks_done"])
+    want = C.allreduce(host, dt, "oneshot")
+    for r in range(n):
+        assert_same(to_host(recv[r], dt), want[r], f"oneshot rank {r}")
+    c.allreduce(send, recv, algo="ring")
+    after = c.debug_state()
+    assert after["calls"] == before["calls"] + 1 and after["ticket"] == 0 and after["done"] == 0
+    c.close()
+
+
+def test_a_call_that_never_waits_completes_while_an_error_is_latched():
+    # Forced from the host as in the timeout test below: the ring call times
+    # out after 50 ms and latches the abort word.  A one-shot call that
+    # follows before anyone checks cannot block, so it still runs in full;
+    # the error stays latched for check().
+    n = 4
+    c = Comm(n, 1 << 20, 0)
+    count = 64 * n
+    host = inputs.rank_inputs(n, count, "f32", "normal", seed=5)
+    send = [to_dev(x, "f32") for x in host]
+    c.inject(1, 2, timeout_us=50_000)
+    _say("latched abort, then oneshot")
+    c.allreduce(send, [empty(count, "f32") for _ in range(n)], algo="ring")
+    c.inject(-1, -1)
+    recv = [empty(count, "f32") for _ in range(n)]
+    c.allreduce(send, recv, algo="oneshot")
+    torch.cuda.synchronize()
+    want = C.allreduce(host, "f32", "oneshot")
+    for r in range(n):
+        assert_same(to_host(recv[r], "f32"), want[r], f"oneshot after abort, rank {r}")
+    assert c.check()[0] == "AR_ERR_TIMEOUT"
+    c.reset()
+    assert c.check()[0] == "AR_OK"
+    c.close()
+
+
 @pytest.mark.parametrize("algo,n,rank,step", [("ring", 4, 1, 2), ("ring", 8, 5, 9), ("twoshot", 4, 2, 0)])
 def test_withheld_signal_times_out_and_names_the_blocked_rank(algo, n, rank, step):
     # Forced from the host: one rank program skips one signal and waits are
