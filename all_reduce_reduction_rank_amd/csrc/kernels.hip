@@ -472,6 +472,136 @@ __device__ __forceinline__ void ll128_pass(const KArgs& a, Terms terms, int nter
   }
 }
 
+// LL128 receive of a pass over many terms (one-shot and direct
+// reduce-scatter receive, the two-shot fold: the own input and N-1 peers'
+// lines).  Checking one term after another costs two round trips per peer
+// (flag, then payload).  Here the flags of every line term come first, in one
+// round trip: lane L checks line l0 + L%32 of terms 2k + L/32 (k = 0..3), so
+// the wave covers all (term, line) pairs of its 32 lines.  Once the whole
+// wave has seen them, each line group's payload of every term is loaded in
+// one round trip and summed in term order.
+template <int DT, class Terms>
+__device__ __forceinline__ void ll128_gather(const KArgs& a, Terms terms, int nterms, char* out_plain,
+                                             char* out_lines, uint64_t nbytes, uint64_t flag, int step,
+                                             int rank) {
+  const int es = Elem<DT>::size;
+  const uint64_t nlines = cdiv(nbytes, LL128_DATA);
+  const int wave = uniform((int)(threadIdx.x / 64)), lane = threadIdx.x % 64;
+  const int q = lane % 8, grp = lane / 8;
+  const uint32_t lane_cap = (q < 7) ? 16u : 8u;
+  constexpr int FLAG_LOADS = (MAX_RANKS * 32 + 63) / 64;
+  const int pi = plain_term(terms, nterms);
+  for (uint64_t l0 = (uint64_t)wave * U_LL128 * 8; l0 < nlines; l0 += 4ull * U_LL128 * 8) {
+    {
+      // Terms 2k and 2k+1 are evaluated for the wave (uniform), each lane
+      // picks its own; lanes with nothing to check load a harmless word, so
+      // all loads go out back to back.
+      const uint64_t fl = l0 + lane % 32;
+      const uint64_t* fp[FLAG_LOADS];
+      bool ready[FLAG_LOADS];
+#pragma unroll
+      for (int k = 0; k < FLAG_LOADS; ++k) {
+        const LTerm t0 = 2 * k < nterms ? terms(2 * k) : LTerm{nullptr, nullptr};
+        const LTerm t1 = 2 * k + 1 < nterms ? terms(2 * k + 1) : LTerm{nullptr, nullptr};
+        const char* ln = lane < 32 ? t0.lines : t1.lines;
+        const bool check = ln != nullptr && fl < nlines;
+        ready[k] = !check;
+        fp[k] = check ? (const uint64_t*)(ln + fl * LL128_LINE + LL128_DATA) : &a.ctl->epoch;
+      }
+      uint64_t fv[FLAG_LOADS];
+#pragma unroll
+      for (int k = 0; k < FLAG_LOADS; ++k) fv[k] = ld_flag(fp[k]);
+      bool all = true;
+#pragma unroll
+      for (int k = 0; k < FLAG_LOADS; ++k) {
+        ready[k] = ready[k] || fv[k] == flag;
+        all = all && ready[k];
+      }
+      if (!all) {
+        PollClock clock;
+        uint32_t level = 0;
+        while (true) {
+          poll_sleep(level);
+          all = true;
+#pragma unroll
+          for (int k = 0; k < FLAG_LOADS; ++k) {
+            if (!ready[k]) ready[k] = ld_flag(fp[k]) == flag;
+            all = all && ready[k];
+          }
+          if (all) break;
+          const int st = clock.tick(a);
+          if (st == POLL_ABORTED) { note_blocked(a.ctl, step, rank); break; }
+          if (st == POLL_TIMED_OUT) { raise_timeout(a.ctl, step, rank); break; }
+        }
+      }
+    }
+    // Every lane of the wave is past its polls: all flags of the pass are
+    // seen.  Per line group, every term's piece in one round trip.
+#pragma unroll
+    for (int u = 0; u < U_LL128; ++u) {
+      const uint32_t line = (uint32_t)(l0 + (uint64_t)u * 8 + grp);
+      const uint64_t off = (uint64_t)line * LL128_DATA + 16ull * q;
+      const uint32_t nb = (line < nlines && off < nbytes) ? (uint32_t)umin(lane_cap, nbytes - off) : 0u;
+      // Every line term's piece with no branch between the loads, then the
+      // plain term's piece, so they all go out before the first wait (a lane
+      // past the tile's last line reads outside the buffer resource and gets
+      // zeros; the plain term's slot reads through an empty one).
+      uint4 x[MAX_RANKS];
+      bool is_line[MAX_RANKS];
+#pragma unroll
+      for (int i = 0; i < MAX_RANKS; ++i) {  // no early exit: terms past nterms read nothing
+        const LTerm tm = terms(i);             // address arithmetic only
+        is_line[i] = i < nterms && tm.lines != nullptr;
+        const Rsrc rl = make_rsrc(is_line[i] ? tm.lines : a.lines, is_line[i] ? (uint32_t)(nlines * LL128_LINE) : 0u);
+        x[i] = cld16(rl, line * LL128_LINE + 16u * q);
+      }
+      uint4 xp = make_uint4(0, 0, 0, 0);
+      if (pi >= 0 && nb) xp = ld_piece(terms(pi).plain + off, nb, es);
+      // Nothing may use a loaded value before the last load is issued: the
+      // scheduler would otherwise wait out each load before the next.
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < MAX_RANKS; ++i) {
+        const uint4 lv = q < 7 ? x[i] : make_uint4(x[i].x, x[i].y, 0, 0);
+        x[i] = !nb ? make_uint4(0, 0, 0, 0) : (is_line[i] ? lv : xp);
+      }
+      Vec<DT> acc = Vec<DT>::widen(x[0]);
+#pragma unroll
+      for (int i = 1; i < MAX_RANKS; ++i)
+        if (i < nterms) acc.add(Vec<DT>::widen(x[i]));
+      const uint4 res = nterms > 1 ? acc.narrow() : x[0];
+      if (out_plain && nb) st_piece(out_plain + off, res, nb, es);
+      if (out_lines && line < nlines) {
+        const Rsrc rl = make_rsrc(out_lines, (uint32_t)(nlines * LL128_LINE));
+        cst16(rl, line * LL128_LINE + 16u * q, q < 7 ? res : make_uint4(res.x, res.y, 0, 0));
+      }
+    }
+    if (out_lines) {
+      wait_mem();
+#pragma unroll
+      for (int u = 0; u < U_LL128; ++u) {
+        const uint32_t line = (uint32_t)(l0 + (uint64_t)u * 8 + grp);
+        if (q == 7 && line < nlines)
+          st_flag((uint64_t*)(out_lines + (uint64_t)line * LL128_LINE + LL128_DATA), flag);
+      }
+    }
+  }
+}
+
+// A line-protocol pass over many terms (see ll128_gather); LL's own pass
+// already loads every term at once.
+template <int DT, int PROTO, class Terms>
+__device__ __forceinline__ void line_gather(const KArgs& a, Terms terms, int nterms, char* out_plain,
+                                            char* out_lines, uint64_t nbytes, uint64_t epoch, int step,
+                                            int rank) {
+  if constexpr (PROTO == PROTO_LL) {
+    const uint32_t flag = (uint32_t)(epoch % 0xffffffffull) + 1u;
+    ll_pass<DT>(a, terms, nterms, out_plain, out_lines, nbytes, flag, step, rank);
+  } else {
+    ll128_gather<DT>(a, terms, nterms, out_plain, out_lines, nbytes, epoch + 1, step, rank);
+  }
+}
+
 // One line-protocol pass, dispatched on the protocol.
 template <int DT, int PROTO, class Terms>
 __device__ __forceinline__ void line_pass(const KArgs& a, Terms terms, int nterms, char* out_plain,
@@ -544,7 +674,7 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
         line_pass<DT, PROTO>(a, [&](int) { return LTerm{a.in[r] + off, nullptr}; }, 1, nullptr,
                              slot_tile(a, r, k.tile), nbytes, epoch, 0, r);
       } else {  // rank r sums all N in rank order: own input, peers' lines
-        line_pass<DT, PROTO>(
+        line_gather<DT, PROTO>(
             a,
             [&](int i) {
               if (i == r && !g.in_place) return LTerm{a.in[r] + off, nullptr};
@@ -576,7 +706,7 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
         line_pass<DT, PROTO>(a, [&](int) { return LTerm{a.in[r] + off, nullptr}; }, 1, nullptr,
                              slot_tile(a, (uint64_t)r * n + j, k.tile), nbytes, epoch, 0, r);
       } else if (k.phase == PH_RECV_FOLD) {  // owner j sums, keeps and publishes block j
-        line_pass<DT, PROTO>(
+        line_gather<DT, PROTO>(
             a,
             [&](int i) {
               if ((uint64_t)i == j) return LTerm{a.in[j] + off, nullptr};
@@ -601,7 +731,7 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
         line_pass<DT, PROTO>(a, [&](int) { return LTerm{a.in[r] + in_off, nullptr}; }, 1, nullptr,
                              slot_tile(a, (uint64_t)r * n + j, k.tile), nbytes, epoch, 0, r);
       } else {
-        line_pass<DT, PROTO>(
+        line_gather<DT, PROTO>(
             a,
             [&](int i) {
               if ((uint64_t)i == j) return LTerm{a.in[j] + in_off, nullptr};
