@@ -32,7 +32,8 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
 
 constexpr int U_SIMPLE = 4;  // 16-byte vectors in flight per thread per source
 constexpr int U_LL = 4;      // LL words per thread per pass
-constexpr int U_LL128 = 4;   // LL128 line groups (8 lines of a wave) per pass
+constexpr int U_LL128 = 4;   // LL128 line groups (8 lines of a wave) per pass of the N-term gather
+constexpr int U_LL128_PASS = 4;  // ... and per pass of a one- or two-term pass (ring, send, copy)
 
 // =============================================================== Simple path
 // dst = fold(term(0), ..., term(n-1)) over `nbytes` (whole elements, at most
@@ -229,10 +230,18 @@ __device__ __forceinline__ void ll_pass(const KArgs& a, Terms terms, int nterms,
     uint32_t pre[U_LL];
     if (pi >= 0) {
       const char* src = terms(pi).plain;
+      // A pass of whole words (every pass but a tile's last) loads with no
+      // branch, so the loads go out together.
+      const uint64_t pass_end = (base - threadIdx.x + (uint64_t)U_LL * WG_THREADS) * 4;
+      if (((uintptr_t)src & 3) == 0 && pass_end <= nbytes) {
 #pragma unroll
-      for (int u = 0; u < U_LL; ++u) {
-        const uint64_t w = base + (uint64_t)u * WG_THREADS;
-        pre[u] = (w < nwords) ? ld_word(src + 4 * w, (uint32_t)umin(4, nbytes - 4 * w), es) : 0u;
+        for (int u = 0; u < U_LL; ++u) pre[u] = *(const uint32_t*)(src + 4 * (base + (uint64_t)u * WG_THREADS));
+      } else {
+#pragma unroll
+        for (int u = 0; u < U_LL; ++u) {
+          const uint64_t w = base + (uint64_t)u * WG_THREADS;
+          pre[u] = (w < nwords) ? ld_word(src + 4 * w, (uint32_t)umin(4, nbytes - 4 * w), es) : 0u;
+        }
       }
     }
     uint64_t got[MAX_RANKS][U_LL];
@@ -335,21 +344,24 @@ __device__ __forceinline__ void st_piece(char* p, const uint4& v, uint32_t nb, i
 // LL128: 128-byte lines {120 payload bytes, 8-byte flag}.  Lane q (0..7) of
 // an 8-lane group owns bytes [16q, 16q+16) of its line: lanes 0..6 carry 16
 // payload bytes, lane 7 carries 8 payload bytes and the flag.  Line L of a
-// tile carries payload bytes [120L, 120L+120).  Each wave handles U_LL128
-// groups of 8 consecutive lines per pass (1 KiB per store instruction).
+// tile carries payload bytes [120L, 120L+120).  This pass takes one or two
+// terms -- at most one plain buffer and one staging slot: a send, a ring
+// step, a copy -- and each wave handles U_LL128_PASS groups of 8 consecutive
+// lines per pass (1 KiB per store instruction).
 //
-// The plain term's loads and the first line term's flag loads go out
-// together; a line term then costs one more round trip for its payload.
-// Payload moves a whole line per instruction: a line's bytes land as one
-// full-line write instead of three partial ones (measured at 256 MiB fp32,
-// N=8 ring: 4.91 -> 3.30 ms, HBM writes 30.4 S -> 26.7 S against 22.9 S of
-// payload).  Holding each pass's flag stores back until the wave's next wait
-// was tried as well: no faster at 256 MiB and slower at 2-32 MiB, where
-// consumers then wait longer for every line.
+// One round trip brings the plain term's pieces and the line term's flags;
+// once every flag is seen, one more brings the line term's payload, all
+// groups at once.  Payload moves a whole line per instruction: a line's
+// bytes land as one full-line write instead of three partial ones (measured
+// at 256 MiB fp32, N=8 ring: 4.91 -> 3.30 ms, HBM writes 30.4 S -> 26.7 S
+// against 22.9 S of payload).  Holding each pass's flag stores back until
+// the wave's next wait was tried as well: no faster at 256 MiB and slower at
+// 2-32 MiB, where consumers then wait longer for every line.
 template <int DT, class Terms>
 __device__ __forceinline__ void ll128_pass(const KArgs& a, Terms terms, int nterms, char* out_plain,
                                            char* out_lines, uint64_t nbytes, uint64_t flag, int step,
                                            int rank) {
+  constexpr int U = U_LL128_PASS;
   const int es = Elem<DT>::size;
   const uint64_t nlines = cdiv(nbytes, LL128_DATA);
   const int wave = uniform((int)(threadIdx.x / 64)), lane = threadIdx.x % 64;
@@ -357,117 +369,125 @@ __device__ __forceinline__ void ll128_pass(const KArgs& a, Terms terms, int nter
   const uint32_t lane_cap = (q < 7) ? 16u : 8u;
   const int pi = plain_term(terms, nterms);
   const int li = line_term(terms, nterms);
-  for (uint64_t l0 = (uint64_t)wave * U_LL128 * 8; l0 < nlines; l0 += 4ull * U_LL128 * 8) {
-    uint32_t line[U_LL128];
-    uint32_t nb[U_LL128];  // payload bytes this lane owns in each of its lines
+  const char* src_plain = pi >= 0 ? terms(pi).plain : nullptr;
+  const char* src_lines = li >= 0 ? terms(li).lines : nullptr;
+  const Rsrc rin = make_rsrc(src_lines ? src_lines : a.lines, src_lines ? (uint32_t)(nlines * LL128_LINE) : 0u);
+  for (uint64_t l0 = (uint64_t)wave * U * 8; l0 < nlines; l0 += 4ull * U * 8) {
+    uint32_t nb[U];  // payload bytes this lane owns in each of its lines
 #pragma unroll
-    for (int u = 0; u < U_LL128; ++u) {
-      line[u] = (uint32_t)(l0 + (uint64_t)u * 8 + grp);
-      const uint64_t off = (uint64_t)line[u] * LL128_DATA + 16ull * q;
-      nb[u] = (line[u] < nlines && off < nbytes) ? (uint32_t)umin(lane_cap, nbytes - off) : 0u;
+    for (int u = 0; u < U; ++u) {
+      const uint32_t line = (uint32_t)(l0 + (uint64_t)u * 8 + grp);
+      const uint64_t off = (uint64_t)line * LL128_DATA + 16ull * q;
+      nb[u] = (line < nlines && off < nbytes) ? (uint32_t)umin(lane_cap, nbytes - off) : 0u;
     }
-    // Loads that wait on nothing: the plain term, and the first line term's
-    // flags (every lane polls its own line's flag word).
-    uint4 pre[U_LL128];
-    if (pi >= 0) {
-      const char* src = terms(pi).plain;
+    // Loads that wait on nothing: the plain term, and the line term's flags
+    // (every lane polls its own line's flag word; past the last line, a
+    // harmless word).
+    // A pass of whole lines (every pass but a short tile's last) loads the
+    // plain pieces as two 8-byte halves per lane with no branch; lane 7,
+    // which owns 8 bytes, loads its half twice and drops the copy.
+    const bool whole = src_plain && ((uintptr_t)src_plain & 7) == 0 &&
+                       (l0 + (uint64_t)U * 8) * LL128_DATA <= nbytes;
+    uint4 pre[U];
+    uint2 plo[U], phi[U];
+    if (whole) {
 #pragma unroll
-      for (int u = 0; u < U_LL128; ++u)
-        pre[u] = nb[u] ? ld_piece(src + (uint64_t)line[u] * LL128_DATA + 16ull * q, nb[u], es)
-                       : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < U; ++u) {
+        const char* p = src_plain + (l0 + (uint64_t)u * 8 + grp) * LL128_DATA + 16ull * q;
+        plo[u] = *(const uint2*)p;
+        phi[u] = *(const uint2*)(q < 7 ? p + 8 : p);
+      }
+    } else if (src_plain) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t off = (l0 + (uint64_t)u * 8 + grp) * LL128_DATA + 16ull * q;
+        pre[u] = nb[u] ? ld_piece(src_plain + off, nb[u], es) : make_uint4(0, 0, 0, 0);
+      }
     }
-    uint64_t f0[U_LL128];
-    if (li >= 0) {
-      const char* ln = terms(li).lines;
+    // The flag word of group u's line (past the last line: line 0's, which
+    // this pass reads anyway; one shared word for every idle lane of the GPU
+    // would queue them all in one memory channel).
+    auto flag_at = [&](int u) -> const uint64_t* {
+      const uint64_t line = l0 + (uint64_t)u * 8 + grp;
+      return (const uint64_t*)(src_lines + (line >= nlines ? 0 : line * LL128_LINE) + LL128_DATA);
+    };
+    bool ready[U];
+    uint64_t fv[U];
+    if (src_lines) {
 #pragma unroll
-      for (int u = 0; u < U_LL128; ++u)
-        f0[u] = line[u] < nlines ? ld_flag((const uint64_t*)(ln + (uint64_t)line[u] * LL128_LINE + LL128_DATA))
-                                 : flag;
+      for (int u = 0; u < U; ++u) fv[u] = ld_flag(flag_at(u));
     }
-    uint4 val[U_LL128];
-    Vec<DT> acc[U_LL128];
-    for (int i = 0; i < nterms; ++i) {
-      const LTerm tm = terms(i);
-      if (i == pi) {
+    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any is used
+    if (whole) {
 #pragma unroll
-        for (int u = 0; u < U_LL128; ++u) val[u] = pre[u];
-      } else if (tm.plain) {
+      for (int u = 0; u < U; ++u)
+        pre[u] = q < 7 ? make_uint4(plo[u].x, plo[u].y, phi[u].x, phi[u].y) : make_uint4(plo[u].x, plo[u].y, 0, 0);
+    }
+    if (src_lines) {
+      bool all = true;
 #pragma unroll
-        for (int u = 0; u < U_LL128; ++u)
-          val[u] = nb[u] ? ld_piece(tm.plain + (uint64_t)line[u] * LL128_DATA + 16ull * q, nb[u], es)
-                         : make_uint4(0, 0, 0, 0);
-      } else {
-        bool ready = true;
+      for (int u = 0; u < U; ++u) {
+        ready[u] = l0 + (uint64_t)u * 8 + grp >= nlines || fv[u] == flag;
+        all = all && ready[u];
+      }
+      if (!all) {
+        PollClock clock;
+        uint32_t level = 0;
+        while (true) {
+          poll_sleep(level);
+          all = true;
 #pragma unroll
-        for (int u = 0; u < U_LL128; ++u) {
-          if (line[u] < nlines) {
-            const uint64_t fv = (i == li) ? f0[u]
-                                          : ld_flag((const uint64_t*)(tm.lines + (uint64_t)line[u] * LL128_LINE +
-                                                                      LL128_DATA));
-            ready = ready && fv == flag;
+          for (int u = 0; u < U; ++u) {
+            if (!ready[u]) ready[u] = ld_flag(flag_at(u)) == flag;
+            all = all && ready[u];
           }
-        }
-        if (!ready) {
-          PollClock clock;
-          uint32_t level = 0;
-          while (true) {
-            poll_sleep(level);
-            ready = true;
-#pragma unroll
-            for (int u = 0; u < U_LL128; ++u) {
-              if (line[u] < nlines)
-                ready = ready && ld_flag((const uint64_t*)(tm.lines + (uint64_t)line[u] * LL128_LINE +
-                                                           LL128_DATA)) == flag;
-            }
-            if (ready) break;
-            const int st = clock.tick(a);
-            if (st == POLL_ABORTED) { note_blocked(a.ctl, step, rank); break; }
-            if (st == POLL_TIMED_OUT) { raise_timeout(a.ctl, step, rank); break; }
-          }
-        }
-        // Flags seen: read the payload at device scope, the whole line in
-        // one instruction (lane 7's upper half is the flag word: dropped).
-        const Rsrc rl = make_rsrc(tm.lines, (uint32_t)(nlines * LL128_LINE));
-#pragma unroll
-        for (int u = 0; u < U_LL128; ++u) {
-          const uint32_t off = line[u] * LL128_LINE + 16u * q;
-          val[u] = nb[u] ? cld16(rl, off) : make_uint4(0, 0, 0, 0);
-          if (q == 7) val[u].z = val[u].w = 0;
+          if (all) break;
+          const int st = clock.tick(a);
+          if (st == POLL_ABORTED) { note_blocked(a.ctl, step, rank); break; }
+          if (st == POLL_TIMED_OUT) { raise_timeout(a.ctl, step, rank); break; }
         }
       }
+    }
+    // Flags seen: the payload of every group at device scope, whole lines,
+    // no branch between the loads (past the last line: zeros, nothing read).
+    uint4 val[U];
+    if (src_lines) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        val[u] = cld16(rin, (uint32_t)((l0 + (uint64_t)u * 8 + grp) * LL128_LINE) + 16u * q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Sum in term order (term 0, then term 1), one group at a time.
+    const Rsrc rout = make_rsrc(out_lines ? out_lines : a.lines, out_lines ? (uint32_t)(nlines * LL128_LINE) : 0u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t line = l0 + (uint64_t)u * 8 + grp;
+      const uint64_t off = line * LL128_DATA + 16ull * q;
+      uint4 lv = make_uint4(0, 0, 0, 0);
+      if (src_lines && nb[u]) lv = q < 7 ? val[u] : make_uint4(val[u].x, val[u].y, 0, 0);
+      const uint4 x0 = pi == 0 ? pre[u] : lv;
+      uint4 res = x0;
       if (nterms > 1) {
-#pragma unroll
-        for (int u = 0; u < U_LL128; ++u) {
-          const Vec<DT> x = Vec<DT>::widen(val[u]);
-          if (i == 0) acc[u] = x; else acc[u].add(x);
-        }
+        const uint4 x1 = pi == 1 ? pre[u] : lv;
+        Vec<DT> acc = Vec<DT>::widen(x0);
+        acc.add(Vec<DT>::widen(x1));
+        res = acc.narrow();
       }
-    }
-    uint4 res[U_LL128];
-#pragma unroll
-    for (int u = 0; u < U_LL128; ++u) res[u] = (nterms > 1) ? acc[u].narrow() : val[u];
-    if (out_plain) {
-#pragma unroll
-      for (int u = 0; u < U_LL128; ++u)
-        if (nb[u]) st_piece(out_plain + (uint64_t)line[u] * LL128_DATA + 16ull * q, res[u], nb[u], es);
+      if (out_plain && nb[u]) st_piece(out_plain + off, res, nb[u], es);
+      // Whole line, flag word still 0 (never a valid flag); a partial lane
+      // stores zero padding.
+      if (out_lines && line < nlines)
+        cst16(rout, (uint32_t)(line * LL128_LINE) + 16u * q, q < 7 ? res : make_uint4(res.x, res.y, 0, 0));
     }
     if (out_lines) {
-      // Payload of every line at device scope, each line whole in one
-      // instruction with its flag word still 0 (never a valid flag; a
-      // partial lane stores zero padding) ...
-      const Rsrc rl = make_rsrc(out_lines, (uint32_t)(nlines * LL128_LINE));
-#pragma unroll
-      for (int u = 0; u < U_LL128; ++u) {
-        if (line[u] >= nlines) continue;
-        const uint32_t off = line[u] * LL128_LINE + 16u * q;
-        cst16(rl, off, q < 7 ? res[u] : make_uint4(res[u].x, res[u].y, 0, 0));
-      }
       // ... complete (visible device-wide), then the flags.
       wait_mem();
 #pragma unroll
-      for (int u = 0; u < U_LL128; ++u)
-        if (q == 7 && line[u] < nlines)
-          st_flag((uint64_t*)(out_lines + (uint64_t)line[u] * LL128_LINE + LL128_DATA), flag);
+      for (int u = 0; u < U; ++u) {
+        const uint64_t line = l0 + (uint64_t)u * 8 + grp;
+        if (q == 7 && line < nlines)
+          st_flag((uint64_t*)(out_lines + line * LL128_LINE + LL128_DATA), flag);
+      }
     }
   }
 }
@@ -491,12 +511,15 @@ __device__ __forceinline__ void ll128_gather(const KArgs& a, Terms terms, int nt
   const uint32_t lane_cap = (q < 7) ? 16u : 8u;
   constexpr int FLAG_LOADS = (MAX_RANKS * 32 + 63) / 64;
   const int pi = plain_term(terms, nterms);
+  const int li = line_term(terms, nterms);
   for (uint64_t l0 = (uint64_t)wave * U_LL128 * 8; l0 < nlines; l0 += 4ull * U_LL128 * 8) {
     {
       // Terms 2k and 2k+1 are evaluated for the wave (uniform), each lane
-      // picks its own; lanes with nothing to check load a harmless word, so
-      // all loads go out back to back.
+      // picks its own; lanes with nothing to check load a harmless word (the
+      // first line term's line 0 flag, read anyway), so all loads go out
+      // back to back.
       const uint64_t fl = l0 + lane % 32;
+      const uint64_t* idle = li >= 0 ? (const uint64_t*)(terms(li).lines + LL128_DATA) : &a.ctl->epoch;
       const uint64_t* fp[FLAG_LOADS];
       bool ready[FLAG_LOADS];
 #pragma unroll
@@ -506,7 +529,7 @@ __device__ __forceinline__ void ll128_gather(const KArgs& a, Terms terms, int nt
         const char* ln = lane < 32 ? t0.lines : t1.lines;
         const bool check = ln != nullptr && fl < nlines;
         ready[k] = !check;
-        fp[k] = check ? (const uint64_t*)(ln + fl * LL128_LINE + LL128_DATA) : &a.ctl->epoch;
+        fp[k] = check ? (const uint64_t*)(ln + fl * LL128_LINE + LL128_DATA) : idle;
       }
       uint64_t fv[FLAG_LOADS];
 #pragma unroll
