@@ -8,9 +8,16 @@
 // they can be captured in HIP graphs, and the workspace caps the message size.
 //
 // Workspace layout (one hipMalloc, 256-byte aligned regions):
-//   [Ctl][flags: u64 x nflags][LL/LL128 lines][ring reduce-scatter partials]
+//   [Ctl][flags: u64 x nflags][LL lines][LL128 lines][ring reduce-scatter partials]
 // Ctl, flags and lines are zeroed at creation; flags and lines are tagged
 // with the device call counter, so they are never cleared again.
+// LL and LL128 stage in separate regions, as NCCL keeps a buffer per
+// protocol.  An LL reader takes bytes 4-7 of every 8-byte slot as a flag;
+// in a shared region those bytes can hold an earlier LL128 call's payload,
+// and a payload word that equals the current LL flag would pass a stale line
+// as fresh.  In its own region an LL flag slot only ever holds an LL flag of
+// this or an earlier call; LL128 flag words (bytes 120-127 of each line)
+// likewise only ever hold LL128 flags.
 #include <hip/hip_runtime.h>
 #include <stdlib.h>
 #include <string.h>
@@ -36,8 +43,8 @@ struct ar_comm {
   Ctl* ctl = nullptr;
   uint64_t* flags = nullptr;
   uint64_t nflags = 0;
-  char* lines = nullptr;
-  uint64_t lines_bytes = 0;
+  char* lines[2] = {nullptr, nullptr};  // LL, LL128 staging
+  uint64_t lines_bytes[2] = {0, 0};
   char* stage = nullptr;
   uint64_t stage_stride = 0;
   uint64_t ticks_per_us = 100;
@@ -62,20 +69,20 @@ static const Tuning& tuning() {
   return t;
 }
 
-// Largest staging any LL / LL128 call on payloads of up to `line_bytes` per
-// rank can need (the ring all-reduce dominates; checked again per call).
-static uint64_t line_capacity(int n, uint64_t line_bytes) {
+// Largest staging any call of protocol `proto` (LL or LL128) on payloads of
+// up to `line_bytes` per rank can need (the ring all-reduce dominates;
+// checked again per call).
+static uint64_t line_capacity(int n, uint64_t line_bytes, int proto) {
   if (!line_bytes) return 0;
   uint64_t best = 0;
   for (int op = 0; op < 3; ++op)
     for (int algo = 0; algo < 3; ++algo)
-      for (int proto = PROTO_LL; proto <= PROTO_LL128; ++proto)
-        for (int dt = 0; dt < 3; dt += 1) {
-          const uint64_t es = (uint64_t)esize_of(dt);
-          const uint64_t cnt = op == OP_ALLREDUCE ? line_bytes / es : line_bytes / es / n;
-          Geometry g;
-          if (make_geometry(op, algo, proto, dt, n, cnt, 0, 0, &g)) best = umax(best, staging_bytes(g));
-        }
+      for (int dt = 0; dt < 3; dt += 1) {
+        const uint64_t es = (uint64_t)esize_of(dt);
+        const uint64_t cnt = op == OP_ALLREDUCE ? line_bytes / es : line_bytes / es / n;
+        Geometry g;
+        if (make_geometry(op, algo, proto, dt, n, cnt, 0, 0, &g)) best = umax(best, staging_bytes(g));
+      }
   return best + best / 8 + (1u << 20);
 }
 
@@ -111,11 +118,13 @@ ar_status ar_comm_create(int nranks, size_t max_bytes_per_rank, size_t max_line_
 
   const uint64_t n = (uint64_t)nranks;
   c->nflags = umax(65536, 2 * n * (max_bytes_per_rank / 4096 + 8));
-  c->lines_bytes = line_capacity(nranks, max_line_bytes_per_rank);
+  c->lines_bytes[0] = line_capacity(nranks, max_line_bytes_per_rank, PROTO_LL);
+  c->lines_bytes[1] = line_capacity(nranks, max_line_bytes_per_rank, PROTO_LL128);
   c->stage_stride = align256(max_bytes_per_rank);
   const uint64_t off_flags = align256(sizeof(Ctl));
-  const uint64_t off_lines = off_flags + align256(c->nflags * 8);
-  const uint64_t off_stage = off_lines + align256(c->lines_bytes);
+  const uint64_t off_ll = off_flags + align256(c->nflags * 8);
+  const uint64_t off_ll128 = off_ll + align256(c->lines_bytes[0]);
+  const uint64_t off_stage = off_ll128 + align256(c->lines_bytes[1]);
   c->ws_bytes = off_stage + (nranks > 1 ? n * c->stage_stride : 0);
   if (hipMalloc((void**)&c->ws, c->ws_bytes) != hipSuccess) {
     (void)hipGetLastError();
@@ -124,7 +133,8 @@ ar_status ar_comm_create(int nranks, size_t max_bytes_per_rank, size_t max_line_
   }
   c->ctl = (Ctl*)c->ws;
   c->flags = (uint64_t*)(c->ws + off_flags);
-  c->lines = c->ws + off_lines;
+  c->lines[0] = c->ws + off_ll;
+  c->lines[1] = c->ws + off_ll128;
   c->stage = c->ws + off_stage;
   Ctl init = {};
   init.err_key = 0xffffffffu;
@@ -280,7 +290,8 @@ static ar_status run(ar_comm_t c, int op, const void* const* send, void* const* 
   if (!make_geometry(op, algo, proto, dtype, n, count, chunk_bytes, in_place, &g, tuning())) return AR_ERR_INVALID;
   if (g.ntasks == 0) return AR_OK;
   if (g.ntasks >= (1ull << 31)) return AR_ERR_TOO_LARGE;
-  if (g.nflags > c->nflags || staging_bytes(g) > c->lines_bytes) return AR_ERR_TOO_LARGE;
+  const int li = g.proto == PROTO_LL128 ? 1 : 0;
+  if (g.nflags > c->nflags || staging_bytes(g) > c->lines_bytes[li]) return AR_ERR_TOO_LARGE;
 
   KArgs a;
   memset(&a, 0, sizeof(a));
@@ -291,7 +302,7 @@ static ar_status run(ar_comm_t c, int op, const void* const* send, void* const* 
   a.g = g;
   a.ctl = c->ctl;
   a.flags = c->flags;
-  a.lines = c->lines;
+  a.lines = c->lines[li];
   a.stage = c->stage;
   a.stage_stride = c->stage_stride;
   a.timeout = c->timeout_ticks;

@@ -93,8 +93,10 @@ typedef void* ar_stream_t; /* a hipStream_t */
  * device ([P] overview; [H] exercise 3).  It allocates, once, the workspace
  * every later call uses: flags, a device call counter, an error record,
  * staging for ring reduce-scatter partials sized for buffers of up to
- * `max_bytes_per_rank`, and LL / LL128 line staging sized for payloads of up
- * to `max_line_bytes_per_rank` per rank (0: LL / LL128 calls are refused).
+ * `max_bytes_per_rank`, and LL and LL128 line staging (one region per
+ * protocol, so that no line slot ever holds another protocol's bytes where
+ * its flag goes) sized for payloads of up to `max_line_bytes_per_rank` per
+ * rank (0: LL / LL128 calls are refused).
  * The per-rank cap applies to the largest buffer of a call: count*esize for
  * all-reduce, nranks*recvcount*esize (input) for reduce-scatter,
  * nranks*sendcount*esize (output) for all-gather.
