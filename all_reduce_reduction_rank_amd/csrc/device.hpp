@@ -281,6 +281,7 @@ struct KArgs {
   uint32_t batch;       // tickets a workgroup takes per fetch
   uint32_t fixed;       // 1: workgroup b runs tickets [b*batch, (b+1)*batch) and
                         //    touches no counter (tasks that never wait, one pass)
+  uint32_t fold;        // 1: one-shot tasks load every term of a pass at once
 };
 
 __device__ __forceinline__ void note_blocked(Ctl* c, int step, int rank) {

@@ -124,6 +124,116 @@ __device__ __forceinline__ void simple_stream(Term term, int nterms, char* dst, 
   }
 }
 
+// Raw-buffer 16-byte accesses with a non-temporal hint (cache policy nt):
+// the buffer forms let one pass load every term with no per-lane bounds
+// branch (an access past the resource's end reads zeros, a store there is
+// dropped), and a scheduling barrier then keeps every load in flight before
+// the first add.
+constexpr int CPOL_NT = 2;
+template <bool NT>
+__device__ __forceinline__ uint4 bld16(Rsrc r, uint32_t off) {
+  const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? CPOL_NT : 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <bool NT>
+__device__ __forceinline__ void bst16(Rsrc r, uint32_t off, const uint4& x) {
+  const v4u32 v = {x.x, x.y, x.z, x.w};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, NT ? CPOL_NT : 0);
+}
+
+// Vectors per thread per term of a fold pass, for about VECS loads in flight
+// per thread whatever the term count (at most 8 per term).  Loading one term
+// after another keeps only 4 vectors per thread in flight; with ~768 resident
+// workgroups that is about 12 MiB GPU-wide, too little to cover HBM latency
+// under load.  Measured at N=8, 256 MiB fp32: the two-shot (fold tasks
+// interleaved with the gather tasks) runs 852 us with one term at a time, 824
+// with 16 loads in flight and 791 with 32.  More in flight costs registers:
+// the one-shot kernel with 32 needs 173 VGPRs, which leaves room for only two
+// workgroups per CU, so its fold keeps 16.
+template <int NTERMS, int VECS>
+constexpr int fold_unroll() {
+  return VECS / NTERMS >= 8 ? 8 : (VECS / NTERMS >= 1 ? VECS / NTERMS : 1);
+}
+
+// One payload element at byte offset `off` of a buffer resource, as a word
+// whose low element is the payload (bf16 in the low half-word).
+template <int DT>
+__device__ __forceinline__ uint32_t bld_elem(Rsrc r, uint32_t off) {
+  if constexpr (DT == DT_BF16) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// dst = term(0) + term(1) + ... + term(NTERMS-1), element by element in
+// that order, over `nbytes` of one tile, for terms that are all inputs of the
+// call (ready at launch: one-shot, the two-shot fold, direct reduce-scatter).
+// Every term's vectors of a pass are loaded before the first add.  The tail
+// (and every element of a range that is not 16-byte aligned, which only odd
+// reduce-scatter slices produce) takes one element per thread through the
+// same buffer resources.
+// NT_IN: inputs are read once per call; NT_OUT: dst is final output;
+// COH_DST: dst is read by another rank program during this call.
+template <int DT, int NTERMS, int VECS, bool NT_IN, bool NT_OUT, bool COH_DST, class Term>
+__device__ __forceinline__ void fold_inputs(Term term, char* dst, uint64_t nbytes) {
+  constexpr int UF = fold_unroll<NTERMS, VECS>();
+  constexpr uint32_t ES = Elem<DT>::size;
+  bool aligned = ((uintptr_t)dst & 15) == 0;
+#pragma unroll
+  for (int i = 0; i < NTERMS; ++i) aligned = aligned && (((uintptr_t)term(i) & 15) == 0);
+  const uint32_t nfull = aligned ? (uint32_t)(nbytes / 16) : 0u;
+  Rsrc rt[NTERMS];
+#pragma unroll
+  for (int i = 0; i < NTERMS; ++i) rt[i] = make_rsrc(term(i), (uint32_t)nbytes);
+  const Rsrc rd = make_rsrc(dst, (uint32_t)nbytes);
+  for (uint32_t base = threadIdx.x; base < nfull; base += UF * WG_THREADS) {
+    uint4 x[UF][NTERMS];
+#pragma unroll
+    for (int u = 0; u < UF; ++u)
+#pragma unroll
+      for (int i = 0; i < NTERMS; ++i) {
+        // vectors past the last whole one read as zeros and are not stored
+        const uint32_t v = base + u * WG_THREADS;
+        x[u][i] = bld16<NT_IN>(rt[i], v < nfull ? v * 16 : 0xfffffff0u);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < UF; ++u) {
+      Vec<DT> acc = Vec<DT>::widen(x[u][0]);
+#pragma unroll
+      for (int i = 1; i < NTERMS; ++i) acc.add(Vec<DT>::widen(x[u][i]));
+      const uint32_t v = base + u * WG_THREADS;
+      const uint32_t off = v < nfull ? v * 16 : 0xfffffff0u;
+      if (COH_DST) cst16(rd, off, acc.narrow());
+      else bst16<NT_OUT>(rd, off, acc.narrow());
+    }
+  }
+  const uint32_t done = nfull * 16;
+  const uint32_t nelem = ((uint32_t)nbytes - done) / ES;
+  for (uint32_t e = threadIdx.x; e < nelem; e += WG_THREADS) {
+    const uint32_t off = done + e * ES;
+    Word<DT> acc = Word<DT>::widen(bld_elem<DT>(rt[0], off));
+#pragma unroll
+    for (int i = 1; i < NTERMS; ++i) acc.add(Word<DT>::widen(bld_elem<DT>(rt[i], off)));
+    const uint32_t w = acc.narrow();
+    if constexpr (DT == DT_BF16) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)w, rd, off, 0, COH_DST ? CPOL_SC1 : 0);
+    else __builtin_amdgcn_raw_buffer_store_b32(w, rd, off, 0, COH_DST ? CPOL_SC1 : 0);
+  }
+}
+
+// fold_inputs over n terms (2..MAX_RANKS), n uniform.
+template <int DT, int VECS, bool NT_IN, bool NT_OUT, bool COH_DST, class Term>
+__device__ __forceinline__ void fold_n(Term term, int n, char* dst, uint64_t nbytes) {
+  switch (n) {
+    case 2: fold_inputs<DT, 2, VECS, NT_IN, NT_OUT, COH_DST>(term, dst, nbytes); break;
+    case 3: fold_inputs<DT, 3, VECS, NT_IN, NT_OUT, COH_DST>(term, dst, nbytes); break;
+    case 4: fold_inputs<DT, 4, VECS, NT_IN, NT_OUT, COH_DST>(term, dst, nbytes); break;
+    case 5: fold_inputs<DT, 5, VECS, NT_IN, NT_OUT, COH_DST>(term, dst, nbytes); break;
+    case 6: fold_inputs<DT, 6, VECS, NT_IN, NT_OUT, COH_DST>(term, dst, nbytes); break;
+    case 7: fold_inputs<DT, 7, VECS, NT_IN, NT_OUT, COH_DST>(term, dst, nbytes); break;
+    case 8: fold_inputs<DT, 8, VECS, NT_IN, NT_OUT, COH_DST>(term, dst, nbytes); break;
+    default: simple_stream<DT, 0u, COH_DST, NT_IN, NT_OUT>(term, n, dst, nbytes); break;
+  }
+}
+
 // simple_stream with the coherence choices made at run time (uniform values).
 template <int DT, class Term>
 __device__ __forceinline__ void stream(bool coh_first, bool coh_dst, Term term, int nterms, char* dst,
@@ -663,7 +773,8 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
     if constexpr (PROTO == PROTO_SIMPLE) {
       if (!g.in_place) {
         // every rank program of this tile re-reads the same inputs: keep them cached
-        simple_stream<DT, false, false, false>([&](int i) { return a.in[i] + off; }, n, a.out[r] + off, nbytes);
+        if (a.fold) fold_n<DT, 16, false, true, false>([&](int i) { return a.in[i] + off; }, n, a.out[r] + off, nbytes);
+        else simple_stream<DT, false, false, false>([&](int i) { return a.in[i] + off; }, n, a.out[r] + off, nbytes);
         return;
       }
       // In place: every rank program of this tile reads all N inputs into
@@ -716,7 +827,7 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
       uint64_t* fl = a.flags + j * g.tiles + k.tile;
       if (k.phase == PH_FOLD) {  // shot 1: rank j sums block j of every rank
         // block j's sum is read back by the other ranks: device scope
-        simple_stream<DT, false, true>([&](int i) { return a.in[i] + off; }, n, a.out[j] + off, nbytes);
+        fold_n<DT, 32, true, true, true>([&](int i) { return a.in[i] + off; }, n, a.out[j] + off, nbytes);
         wg_signal(a, fl, tag + 1, 0, r);
       } else {  // shot 2: rank r reads block j's sum back
         if (!wg_wait(a, fl, tag + 1, 1, r)) return;
@@ -748,7 +859,12 @@ __device__ __forceinline__ void run_task(const KArgs& a, const Task& k, uint64_t
     const uint64_t in_off = (block_lo(g, j) + k.lo) * es, out_off = k.lo * es;
     const int r = k.rank;
     if constexpr (PROTO == PROTO_SIMPLE) {
-      simple_stream<DT, false, false>([&](int i) { return a.in[i] + in_off; }, n, a.out[j] + out_off, nbytes);
+      // One term at a time, as for the ring: folding every term's loads at
+      // once ran slower here at every depth and tile size tried (256 MiB:
+      // 422 us against 430-490), and so did plain loads (447 us).  Plain
+      // stores of the result measured 411 us against 422 non-temporal.
+      simple_stream<DT, false, false, true, false>([&](int i) { return a.in[i] + in_off; }, n, a.out[j] + out_off,
+                                                   nbytes);
     } else {
       if (k.phase == PH_SEND) {
         line_pass<DT, PROTO>(a, [&](int) { return LTerm{a.in[r] + in_off, nullptr}; }, 1, nullptr,
@@ -1099,6 +1215,20 @@ hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uin
                           (a.g.proto == PROTO_SIMPLE && !barrier &&
                            (a.g.kind == K_ONESHOT || a.g.kind == K_RS_DIRECT || a.g.kind == K_AG_DIRECT));
   b.fixed = (waits_free && grid * b.batch >= a.g.ntasks) ? 1u : 0u;
+  // One-shot out of place folds every term of a pass at once while its N
+  // inputs are small; beyond that the same fold ran slower than one term at
+  // a time.  Measured at N=8 (us, one term at a time -> fold): bf16 4 MiB per
+  // rank 43.7 -> 38.9, 16 MiB 112.8 -> 105.3, 32 MiB 187.5 -> 221.2; fp32
+  // 4 MiB 39.4 -> 38.2, 8 MiB 59.2 -> 61.3, 32 MiB 169.5 -> 227.6.  bf16
+  // gains further (twice the widen/add/round work per byte to hide).  So:
+  // N inputs of at most 128 MiB (bf16) or 32 MiB (4-byte types).
+  static const uint64_t fold_env = [] {
+    const char* e = getenv("AR_ONESHOT_FOLD_MIB");
+    return e ? (strtoull(e, nullptr, 10) << 20) : ~0ull;
+  }();
+  const uint64_t fold_max = fold_env != ~0ull ? fold_env : (a.g.esize == 2 ? 128ull << 20 : 32ull << 20);
+  b.fold = (a.g.kind == K_ONESHOT && !a.g.in_place &&
+            (uint64_t)a.g.nranks * a.g.total * (uint64_t)a.g.esize <= fold_max) ? 1u : 0u;
   hipLaunchKernelGGL(f, dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, b);
   return hipGetLastError();
 }

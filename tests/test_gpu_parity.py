@@ -64,6 +64,16 @@ def test_allreduce_matrix(n, algo, proto, dt):
         run_allreduce(n, count, dt, algo, proto, seed=count)
 
 
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 6, 7, 8])
+def test_simple_fold_every_rank_count(n, dt):
+    # The Simple one-shot and two-shot folds are compiled per term count:
+    # every N, with a ragged tail, one pass and many passes per tile.
+    for algo in ("oneshot", "twoshot"):
+        for count in (5, 4097, 262147):
+            run_allreduce(n, count, dt, algo, "simple", seed=count + n)
+
+
 @pytest.mark.parametrize("proto", PROTOS)
 @pytest.mark.parametrize("dt", DTYPES)
 def test_ring_many_chunks(proto, dt):
@@ -95,6 +105,36 @@ def test_config_small_n2_4096_f32():
         for proto in PROTOS:
             run_allreduce(2, 4096, "f32", algo, proto, dist="uniform")
             run_allreduce(2, 4096, "f32", algo, proto, dist="ones")
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_ll_lines_never_meet_ll128_payload(algo):
+    # An LL reader takes bytes 4-7 of each 8-byte slot as the line's flag.
+    # Each protocol stages in its own region, so an earlier LL128 call's
+    # payload can never sit there: here every LL128 payload word equals the
+    # flag the next LL call writes, and that LL call must still match the
+    # oracle.
+    n = 4
+    c = Comm(n, 1 << 20, 1 << 20)
+    try:
+        for count in (4096, 30001, 65536):
+            calls = c.debug_state()["calls"]
+            # the LL128 call runs with epoch `calls`, the LL call with
+            # calls + 1, whose LL flag is calls + 2
+            bait = [torch.full((count,), calls + 2, dtype=torch.int32, device="cuda") for _ in range(n)]
+            c.allreduce(bait, [empty(count, "i32") for _ in range(n)], algo=algo, proto="ll128")
+            host = inputs.rank_inputs(n, count, "i32", "int20", seed=count, cfg=400 + n)
+            send = [to_dev(x, "i32") for x in host]
+            recv = [empty(count, "i32") for _ in range(n)]
+            _say("ll after ll128 bait", algo, n, count)
+            c.allreduce(send, recv, algo=algo, proto="ll")
+            torch.cuda.synchronize()
+            want = C.allreduce(host, "i32", algo)
+            for r in range(n):
+                assert_same(to_host(recv[r], "i32"), want[r], f"LL {algo} after LL128 bait count={count} rank {r}")
+        assert c.check()[0] == "AR_OK"
+    finally:
+        c.close()
 
 
 def test_eight_bytes_per_rank():

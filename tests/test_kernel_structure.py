@@ -71,7 +71,7 @@ def test_ticket_fetch_and_barriers_share_one_loop(asm):
             if br:
                 branches.append((header, br.group(1)))
             if fetch_loop is None and fetch_label is None and \
-                    re.search(r"global_atomic_add v\d+, v\d+, v\d+, s\[\d+:\d+\] sc0$", line):
+                    re.search(r"global_atomic_add v\d+, v(?:\d+|\[\d+:\d+\]), v\d+, (?:s\[\d+:\d+\]|off) sc0$", line):
                 fetch_loop, fetch_label = header, label
             elif (fetch_loop or fetch_label) and barrier_loop is None and "s_barrier" in line:
                 barrier_loop = header
