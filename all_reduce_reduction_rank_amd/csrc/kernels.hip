@@ -185,18 +185,25 @@ __device__ __forceinline__ void fold_inputs(Term term, char* dst, uint64_t nbyte
   for (int i = 0; i < NTERMS; ++i) rt[i] = make_rsrc(term(i), (uint32_t)nbytes);
   const Rsrc rd = make_rsrc(dst, (uint32_t)nbytes);
   for (uint32_t base = threadIdx.x; base < nfull; base += UF * WG_THREADS) {
+    // Group u of this pass starts at vector pass0 + u*WG_THREADS (the same
+    // for the whole workgroup): groups wholly past the tile are skipped, so
+    // a short tile does no work for the vectors it does not have.
+    const uint32_t pass0 = uniform(base - threadIdx.x);
     uint4 x[UF][NTERMS];
 #pragma unroll
-    for (int u = 0; u < UF; ++u)
+    for (int u = 0; u < UF; ++u) {
+      if (pass0 + u * WG_THREADS >= nfull) break;
 #pragma unroll
       for (int i = 0; i < NTERMS; ++i) {
         // vectors past the last whole one read as zeros and are not stored
         const uint32_t v = base + u * WG_THREADS;
         x[u][i] = bld16<NT_IN>(rt[i], v < nfull ? v * 16 : 0xfffffff0u);
       }
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < UF; ++u) {
+      if (pass0 + u * WG_THREADS >= nfull) break;
       Vec<DT> acc = Vec<DT>::widen(x[u][0]);
 #pragma unroll
       for (int i = 1; i < NTERMS; ++i) acc.add(Vec<DT>::widen(x[u][i]));

@@ -124,7 +124,11 @@ struct Tuning {
 //                 1.63 at 64 KiB and 1.96 at 32 KiB); 16 KiB in place (the
 //                 tile lives in registers)
 //   RS direct     16 KiB (256 MiB: 0.72 against 0.62 at 128 KiB)
-//   AG direct     16 KiB (256 MiB: 409 us against 467 at 128 KiB)
+//   AG direct     16 KiB from 64 MiB per rank (256 MiB: 409 us against 467
+//                 at 128 KiB), else 128 KiB: an all-gather has N^2 tasks per
+//                 tile row, and with 16 KiB tiles at 8-32 MiB each fetch of
+//                 the ticket counter covers one small tile (N=8 8 MiB: 65 us
+//                 against 32 at 128 KiB; N=2 32 MiB: 65 against 29)
 // LL up to 16 KiB; LL128 whole wave passes.
 inline uint64_t pick_tile_bytes(int proto, uint64_t rank_bytes, int kind, bool in_place) {
   const uint64_t want = floor_pow2(rank_bytes / 128 + 1);
@@ -132,7 +136,8 @@ inline uint64_t pick_tile_bytes(int proto, uint64_t rank_bytes, int kind, bool i
     uint64_t hi = 131072;
     if (kind == K_RING || kind == K_TREE) hi = 32768;
     if (kind == K_TWOSHOT) hi = rank_bytes >= (64ull << 20) ? 65536 : 32768;
-    if (kind == K_RS_DIRECT || kind == K_AG_DIRECT) hi = 16384;
+    if (kind == K_RS_DIRECT) hi = 16384;
+    if (kind == K_AG_DIRECT) hi = rank_bytes >= (64ull << 20) ? 16384 : 131072;
     if (kind == K_ONESHOT && in_place) hi = 16384;
     return clampu(want, 4096, hi);
   }

@@ -57,11 +57,12 @@ def test_choice_is_the_measured_fastest_at_every_swept_point():
         best = min(times.values())
         ratios.append(times[(a, p)] / best)
         worst = max(worst, ratios[-1])
-    # A two-parameter line per cache band: nearly every point picks the
-    # fastest; the worst measured miss is 1.25x (reduce-scatter, N=2, 8 MiB,
-    # where the direct and ring schedules differ by one step).
-    assert worst <= 1.30, f"auto choice up to {worst:.2f}x the fastest measured"
-    assert sum(r <= 1.05 for r in ratios) >= 0.95 * len(ratios)
+    # A two-parameter line per cache band: 99 % of the points pick the
+    # fastest and all are within 5 %; the worst measured miss is 1.03x
+    # (reduce-scatter, N=2, 2 MiB, where the direct and ring schedules
+    # differ by one step).
+    assert worst <= 1.15, f"auto choice up to {worst:.2f}x the fastest measured"
+    assert sum(r <= 1.05 for r in ratios) >= 0.97 * len(ratios)
 
 
 def test_no_line_capacity_means_simple():
