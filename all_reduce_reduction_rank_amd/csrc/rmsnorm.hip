@@ -59,14 +59,20 @@ struct VecF {
 // is all.  With several rows per workgroup (prefill) the extra registers and
 // loads in flight measured 3 % slower, and at fp32 (twice the vectors per
 // row) they would cut residency from 3 to 2 workgroups per CU.
-template <int DT, bool EARLY_W>
-__global__ __launch_bounds__(WG_THREADS) void rmsnorm_kernel(RmsArgs a) {
+// T: threads per workgroup.  A decode call has only N items (one row per
+// rank), so it runs 1024 threads per row: a row of up to 1024 vectors is
+// one pass, its loads one round trip.  With 256 threads the same row took
+// three passes, each waiting for its own loads.
+// The residual is read with the inputs and written back in the output pass,
+// so no store sits between the first pass's loads.
+template <int DT, bool EARLY_W, int T>
+__global__ __launch_bounds__(T) void rmsnorm_kernel(RmsArgs a) {
   constexpr int E = VecF<DT>::E;
   // vectors of a row each thread holds at most: the row's h stays in
-  // registers (48 floats per thread at the largest hidden size)
-  constexpr int VPT = (int)(RMS_MAX_HIDDEN / E / WG_THREADS);
+  // registers (48 floats per thread at the largest hidden size and T = 256)
+  constexpr int VPT = (int)((RMS_MAX_HIDDEN / E + T - 1) / T);
   constexpr uint64_t es = DT == DT_BF16 ? 2 : 4;
-  __shared__ float s_part[WG_THREADS / 64];
+  __shared__ float s_part[T / 64];
   const uint64_t nvec = a.hidden / E;
   const uint64_t items = a.rows * (uint64_t)a.nranks;
   const int n = a.nranks;
@@ -80,26 +86,27 @@ __global__ __launch_bounds__(WG_THREADS) void rmsnorm_kernel(RmsArgs a) {
     float ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const uint64_t v = threadIdx.x + (uint64_t)i * WG_THREADS;
+      const uint64_t v = threadIdx.x + (uint64_t)i * T;
       if (v < nvec) {
         const uint64_t off = base + v * 16;
         if constexpr (EARLY_W) wv[i] = ld16(a.weight + v * 16);
-        // all N loads in flight, then the sum in ascending rank order; the N
-        // rank programs of a row re-read the same inputs, so these stay cached
+        // all N loads in flight (and the residual's), then the sum in
+        // ascending rank order; the N rank programs of a row re-read the
+        // same inputs, so these stay cached
         uint4 x[MAX_RANKS];
 #pragma unroll
         for (int j = 0; j < MAX_RANKS; ++j)
           if (j < n) x[j] = ld16(a.in[j] + off);
+        const uint4 q = res ? ld16(res + off) : make_uint4(0, 0, 0, 0);
         Vec<DT> acc = Vec<DT>::widen(x[0]);
 #pragma unroll
         for (int j = 1; j < MAX_RANKS; ++j)
           if (j < n) acc.add(Vec<DT>::widen(x[j]));
         h[i] = VecF<DT>::load(acc.narrow());  // the all-reduce result, rounded
         if (res) {
-          const VecF<DT> q = VecF<DT>::load(ld16(res + off));
+          const VecF<DT> qf = VecF<DT>::load(q);
 #pragma unroll
-          for (int e = 0; e < E; ++e) h[i].v[e] = h[i].v[e] + q.v[e];
-          st16(res + off, h[i].store());
+          for (int e = 0; e < E; ++e) h[i].v[e] = h[i].v[e] + qf.v[e];
         }
 #pragma unroll
         for (int e = 0; e < E; ++e) ss = ss + h[i].v[e] * h[i].v[e];
@@ -111,13 +118,14 @@ __global__ __launch_bounds__(WG_THREADS) void rmsnorm_kernel(RmsArgs a) {
     __syncthreads();
     float tot = s_part[0];
 #pragma unroll
-    for (int w = 1; w < WG_THREADS / 64; ++w) tot += s_part[w];
+    for (int w = 1; w < T / 64; ++w) tot += s_part[w];
     const float inv = 1.0f / sqrtf(tot / (float)a.hidden + a.eps);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const uint64_t v = threadIdx.x + (uint64_t)i * WG_THREADS;
+      const uint64_t v = threadIdx.x + (uint64_t)i * T;
       if (v < nvec) {
         const VecF<DT> w = VecF<DT>::load(EARLY_W ? wv[EARLY_W ? i : 0] : ld16(a.weight + v * 16));
+        if (res) st16(res + base + v * 16, h[i].store());  // residual <- h, rounded
         VecF<DT> o;
 #pragma unroll
         for (int e = 0; e < E; ++e) o.v[e] = (h[i].v[e] * inv) * w.v[e];
@@ -136,11 +144,13 @@ hipError_t launch_rmsnorm(const RmsArgs& a, int dtype, int device, hipStream_t s
   if (max_workgroups) grid = umin(grid, (uint64_t)max_workgroups);
   if (grid < 1) grid = 1;
   const bool one_row = items <= grid;
+  const dim3 g((unsigned)grid);
   if (dtype == DT_BF16) {
-    if (one_row) hipLaunchKernelGGL((rmsnorm_kernel<DT_BF16, true>), dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, a);
-    else hipLaunchKernelGGL((rmsnorm_kernel<DT_BF16, false>), dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, a);
+    if (one_row) hipLaunchKernelGGL((rmsnorm_kernel<DT_BF16, true, 1024>), g, dim3(1024), 0, stream, a);
+    else hipLaunchKernelGGL((rmsnorm_kernel<DT_BF16, false, WG_THREADS>), g, dim3(WG_THREADS), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((rmsnorm_kernel<DT_F32, false>), dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, a);
+    if (one_row) hipLaunchKernelGGL((rmsnorm_kernel<DT_F32, true, 1024>), g, dim3(1024), 0, stream, a);
+    else hipLaunchKernelGGL((rmsnorm_kernel<DT_F32, false, WG_THREADS>), g, dim3(WG_THREADS), 0, stream, a);
   }
   return hipGetLastError();
 }
