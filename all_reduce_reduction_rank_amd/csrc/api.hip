@@ -57,13 +57,14 @@ struct ar_comm {
 static uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }
 
 // Tuning overrides read once from the environment (for measurements; they
-// never change results): AR_TILE_KB, AR_RING_SKEW, AR_RING_WINDOW.
+// never change results): AR_TILE_KB, AR_RING_SKEW, AR_RING_WINDOW, AR_LAG.
 static const Tuning& tuning() {
   static const Tuning t = [] {
     Tuning x;
     if (const char* e = getenv("AR_TILE_KB")) x.tile_bytes = strtoull(e, nullptr, 10) * 1024;
     if (const char* e = getenv("AR_RING_SKEW")) { x.ring_skew = strtoull(e, nullptr, 10); x.ring_skew_set = true; }
     if (const char* e = getenv("AR_RING_WINDOW")) x.ring_window = strtoull(e, nullptr, 10);
+    if (const char* e = getenv("AR_LAG")) x.lag = strtoull(e, nullptr, 10);
     return x;
   }();
   return t;

@@ -112,6 +112,7 @@ struct Tuning {
   uint64_t ring_skew = 0;   // ring order: 0 windowed, k >= 1 skewed diagonal
   uint64_t ring_window = 0; // ring window (loops) for the windowed order
   bool ring_skew_set = false;
+  uint64_t lag = 0;         // phased kinds: receiver groups behind their senders
 };
 
 // Tile size in bytes for a per-rank buffer of `rank_bytes`: aim for >= 128
@@ -270,9 +271,18 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
   const uint64_t extent = (g.kind == K_ONESHOT) ? g.total : g.block;
   g.tiles = cdiv(extent, g.tile);
   // Receivers of tile g run `lag` groups after its senders: about one
-  // resident grid of tasks in between, never more than the tiles there are.
-  const uint64_t per_group_hint = g.kind == K_TWOSHOT ? n * n : (g.kind == K_ONESHOT ? 2 * n : n * n);
-  g.lag = (int32_t)umax(1, umin(g.tiles, cdiv(RESIDENT_HINT, per_group_hint)));
+  // resident grid of tasks in between, and at most a quarter of the tiles.
+  // With the lag at the tile count, a small call's receivers all queued
+  // behind its last sender: measured at N=8 bf16 (us, that lag -> a quarter
+  // of the tiles or near it), two-shot Simple 5 MiB 56 -> 50, LL 512 KiB
+  // 85 -> 63, LL128 5 MiB 104 -> 82-86; large calls keep the grid-sized lag
+  // (two-shot LL128 32 MiB: 392 at 32 groups, 428-464 at 8-16).  One-shot
+  // with lines takes the same grid-sized lag (32 groups at N=8) although its
+  // groups hold 2N tasks, not N^2: LL 5 MiB 122 us at 128 groups, 107 at 32;
+  // 32 MiB 623 at 128, 619 at 32.
+  const uint64_t per_group_hint = n * n;
+  g.lag = (int32_t)umax(1, umin(g.tiles / 4, cdiv(RESIDENT_HINT, per_group_hint)));
+  if (tune.lag) g.lag = (int32_t)umax(1, umin(g.tiles, tune.lag));
   const uint64_t lag = (uint64_t)g.lag;
   switch (g.kind) {
     case K_ONESHOT:
