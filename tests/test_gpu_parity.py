@@ -145,6 +145,42 @@ def test_eight_bytes_per_rank():
             run_allreduce(8, 4, "bf16", algo, proto)
 
 
+@pytest.mark.parametrize("op,nbytes", [("allreduce", 512 << 10), ("allreduce", 640 << 10),
+                                       ("allgather", 512 << 10), ("allgather", 8 << 20),
+                                       ("reduce_scatter", 2 << 20)])
+def test_mid_size_calls_that_never_wait_skip_the_ticket_counter(op, nbytes):
+    # Simple one-shot and direct RS/AG calls of these sizes take tiles that
+    # fit one grid, so they launch without the ticket counter: such a call
+    # leaves the device call counter where it was.  The results still match
+    # the oracle.
+    n, dt = 8, "bf16"
+    c = Comm(n, nbytes, 0)
+    try:
+        full = nbytes // 2
+        shard = full // n
+        host = inputs.rank_inputs(n, shard if op == "allgather" else full, dt, "normal", seed=nbytes, cfg=500)
+        send = [to_dev(x, dt) for x in host]
+        recv = [empty(full if op != "reduce_scatter" else shard, dt) for _ in range(n)]
+        _say("counter-free", op, n, nbytes)
+        before = c.debug_state()["calls"]
+        if op == "allreduce":
+            c.allreduce(send, recv, algo="oneshot", proto="simple")
+            want = C.allreduce(host, dt, "oneshot")
+        elif op == "allgather":
+            c.allgather(send, recv, algo="oneshot", proto="simple")
+            want = C.allgather(host, dt, "oneshot")
+        else:
+            c.reduce_scatter(send, recv, algo="oneshot", proto="simple")
+            want = C.reduce_scatter(host, dt, "oneshot")
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_same(to_host(recv[r], dt), want[r], f"{op} {nbytes} B rank {r}")
+        assert c.debug_state()["calls"] == before, "the call went through the ticket counter"
+        assert c.check()[0] == "AR_OK"
+    finally:
+        c.close()
+
+
 def test_empty_and_single_rank():
     for algo in ALGOS:
         for proto in PROTOS:
