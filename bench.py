@@ -326,6 +326,8 @@ def main():
         "algbw_GBps": round(algbw, 3),
         "busbw_GBps": round(algbw * busbw_factor(op, n), 3),
         "hbm_bytes_per_call": plan["hbm"],
+        # HBM bytes per byte of payload (N ranks x S): the schedule's model
+        "hbm_bytes_per_payload_byte": round(plan["hbm"] / (n * s), 4),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -339,6 +341,7 @@ def main():
     if traffic:
         out["hbm_measured_GBps"] = round(traffic / t / 1e9, 1)
         out["hbm_measured_frac"] = round(traffic / t / 1e9 / HBM_PEAK_GBPS, 4)
+        out["hbm_measured_bytes_per_payload_byte"] = round(traffic / (n * s), 4)
     if args.cpu_seconds > 0:
         # the oracle as it stands (one thread), then T copies side by side
         base = cpu_baseline(w, args.cpu_seconds / 2)
