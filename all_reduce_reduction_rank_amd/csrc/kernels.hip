@@ -165,11 +165,11 @@ __device__ __forceinline__ uint32_t bld_elem(Rsrc r, uint32_t off) {
 
 // dst = term(0) + term(1) + ... + term(NTERMS-1), element by element in
 // that order, over `nbytes` of one tile, for terms that are all inputs of the
-// call (ready at launch: one-shot, the two-shot fold, direct reduce-scatter).
+// call (ready at launch: the one-shot and the two-shot's reduce half).
 // Every term's vectors of a pass are loaded before the first add.  The tail
-// (and every element of a range that is not 16-byte aligned, which only odd
-// reduce-scatter slices produce) takes one element per thread through the
-// same buffer resources.
+// of a block, and every element of a range that is not 16-byte aligned (the
+// all-reduce blocks always are; the check keeps the fold safe for any
+// caller), take one element per thread through the same buffer resources.
 // NT_IN: inputs are read once per call; NT_OUT: dst is final output;
 // COH_DST: dst is read by another rank program during this call.
 template <int DT, int NTERMS, int VECS, bool NT_IN, bool NT_OUT, bool COH_DST, class Term>

@@ -21,6 +21,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import statistics
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,13 +29,22 @@ KERNEL = "collective_kernel"
 KERNEL_SOURCES = ("csrc/kernels.hip", "csrc/device.hpp", "csrc/schedule.hpp", "csrc/plan.hpp")
 
 
+def _code_only(text):
+    """C++ source without comments and with whitespace collapsed: what the
+    compiler sees, so that editing a comment keeps a counter summary valid.
+    (The kernel sources hold no string literal with a comment marker.)"""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_hash():
-    """Hash of the sources the collective kernels are compiled from: a
-    counter summary is valid only for the kernels it was taken on."""
+    """Hash of the code the collective kernels are compiled from: a counter
+    summary is valid only for the kernels it was taken on."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(HERE, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(HERE, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -41,3 +41,12 @@ def test_more_than_one_gpu_is_refused():
 
 def test_kernel_hash_is_stable():
     assert bench.kernel_hash() == bench.kernel_hash() and len(bench.kernel_hash()) == 16
+
+
+def test_kernel_hash_ignores_comments_and_layout():
+    from all_reduce_reduction_rank_amd import profiling
+    code = "int f(int x) {\n  return x + 1;  // one more\n}\n"
+    edited = "/* a note */\nint f(int x)   {\n  return x + 1;  // one more, said again\n}\n"
+    changed = "int f(int x) {\n  return x + 2;\n}\n"
+    assert profiling._code_only(code) == profiling._code_only(edited)
+    assert profiling._code_only(code) != profiling._code_only(changed)
