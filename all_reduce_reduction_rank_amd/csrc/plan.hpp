@@ -223,17 +223,21 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
   // one grid every task costs a fetch of the shared counter, and the
   // serialized fetches set the time.  Measured at N=8 (us, before -> after):
   // all-gather 512 KiB per rank 27.9 -> 3.4, 2 MiB 30.1 -> 15.2, 8 MiB
-  // 31.7 -> 24.2 (tiles up to the schedule's bound); one-shot 512 KiB
-  // 26.5 -> 6.1.  A one-shot task reads N tiles, and past 16 KiB tiles the
-  // longer tasks cost more than the fetches save (8 MiB: 58 -> 92 with
-  // 128 KiB tiles), so one-shot tiles grow to 16 KiB at most.
+  // 31.7 -> 24.2 (tiles up to the schedule's bound); reduce-scatter 32 MiB
+  // N=2 44 -> 21, N=4 49 -> 33, N=8 68 -> 56 (64 KiB tiles); one-shot
+  // 512 KiB 26.5 -> 6.1.  A one-shot task reads N tiles, and past 16 KiB
+  // tiles the longer tasks cost more than the fetches save (8 MiB: 58 -> 92
+  // with 128 KiB tiles), so one-shot tiles grow to 16 KiB at most and
+  // reduce-scatter tiles to 64 KiB.
   if (!lines && !tune.tile_bytes &&
       ((g.kind == K_ONESHOT && !in_place) || g.kind == K_RS_DIRECT || g.kind == K_AG_DIRECT)) {
     const uint64_t per_row = g.kind == K_AG_DIRECT ? n * n : n;  // tasks per tile of every block
     const uint64_t extent_b = (g.kind == K_ONESHOT ? g.total : g.block) * es;
     const uint64_t rows = umax(1, FIXED_GRID_TASKS / per_row);
     const uint64_t need = cdiv(cdiv(extent_b, rows), 16) * 16;
-    const uint64_t bound = g.kind == K_ONESHOT ? 16384 : simple_tile_cap(rank_bytes, g.kind, in_place != 0);
+    const uint64_t bound = g.kind == K_ONESHOT     ? 16384
+                           : g.kind == K_RS_DIRECT ? 65536
+                                                   : simple_tile_cap(rank_bytes, g.kind, in_place != 0);
     if (need > tile_b && need <= bound) tile_b = need;
   }
 

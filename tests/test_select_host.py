@@ -58,10 +58,9 @@ def test_choice_is_the_measured_fastest_at_every_swept_point():
         ratios.append(times[(a, p)] / best)
         worst = max(worst, ratios[-1])
     # A two-parameter line per cache band: 99 % of the points pick the
-    # fastest; the worst measured miss is 1.23x (reduce-scatter, N=2, bf16,
-    # 32 MiB, where the direct and ring schedules differ by one step and the
-    # ring wins only inside one size band).
-    assert worst <= 1.30, f"auto choice up to {worst:.2f}x the fastest measured"
+    # fastest and all are within 5 % (worst measured miss 1.001x, at a
+    # reduce-scatter size where the direct and ring schedules tie).
+    assert worst <= 1.10, f"auto choice up to {worst:.2f}x the fastest measured"
     assert sum(r <= 1.05 for r in ratios) >= 0.97 * len(ratios)
 
 
