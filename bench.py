@@ -41,6 +41,10 @@ WORKLOADS = {
                          algo="oneshot", proto="ll", chunk=0),
     "tp-prefill-t512": dict(op="allreduce", nranks=8, bytes=512 * 5120 * 2, dtype="bf16", dist="normal",
                             algo="twoshot", proto="ll128", chunk=0),
+    # bf16 of the same size as the fp32 bucket (N=8 N(0,1), fp32 accumulate,
+    # rounded once per hop on the ring): the >= 64 MiB bandwidth target in bf16
+    "bf16-256MiB": dict(op="allreduce", nranks=8, bytes=256 << 20, dtype="bf16", dist="normal",
+                        algo="ring", proto="simple", chunk=512 << 10),
     # integer path: N=8 int32, 64 MiB per rank
     "int32-64MiB-ring": dict(op="allreduce", nranks=8, bytes=64 << 20, dtype="i32", dist="int20",
                              algo="ring", proto="simple", chunk=512 << 10),

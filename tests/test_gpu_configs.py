@@ -183,6 +183,12 @@ def test_sweep_large_sizes_sampled(algo, proto, mib):
 
 
 @pytest.mark.parametrize("algo", ALGOS)
+def test_bf16_256mib_sampled(algo):
+    # the bf16 bandwidth workload at full size, as the bench launches it
+    check_allreduce_sampled(8, (256 << 20) // 2, "bf16", algo, "simple", "normal", chunk=512 << 10, seed=16)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
 def test_sweep_one_gib(algo):
     check_allreduce_sampled(8, (1 << 30) // 4, "f32", algo, "simple", "normal", seed=30)
 
