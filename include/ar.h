@@ -41,6 +41,12 @@
  *     all-gather, small enough that one grid covers all its tiles) still
  *     runs in full.  Once ar_comm_check has seen the error, every call
  *     returns AR_ERR_BROKEN until ar_comm_reset.  Nothing is printed.
+ *   - Measurement overrides, read once per process from the environment;
+ *     they change how work is cut and ordered, never a result:
+ *     AR_TILE_KB (Simple tile), AR_BATCH (tickets per counter fetch, 1..16),
+ *     AR_LAG (receiver groups behind their senders), AR_RING_WINDOW and
+ *     AR_RING_SKEW (ring ticket order), AR_ONESHOT_FOLD_MIB (largest N*S of
+ *     a one-shot that loads every term of a pass at once).
  */
 #ifndef AR_H
 #define AR_H
