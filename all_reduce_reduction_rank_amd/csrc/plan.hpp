@@ -306,10 +306,11 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
   // of the tiles or near it), two-shot Simple 5 MiB 56 -> 50, LL 512 KiB
   // 85 -> 63, LL128 5 MiB 104 -> 82-86; large calls keep the grid-sized lag
   // (two-shot LL128 32 MiB: 392 at 32 groups, 428-464 at 8-16).  One-shot
-  // with lines takes the same grid-sized lag (32 groups at N=8) although its
-  // groups hold 2N tasks, not N^2: LL 5 MiB 122 us at 128 groups, 107 at 32;
-  // 32 MiB 623 at 128, 619 at 32.
-  const uint64_t per_group_hint = n * n;
+  // LL takes the same grid-sized lag (32 groups at N=8) although its groups
+  // hold 2N tasks, not N^2: 5 MiB 122 us at 128 groups, 107 at 32; 32 MiB
+  // 623 and 619.  One-shot LL128 keeps the 2N-task count (128 groups): at
+  // 32 groups its 8 MiB call took 380 us against 184-190 at 64-128.
+  const uint64_t per_group_hint = (g.kind == K_ONESHOT && proto == PROTO_LL128) ? 2 * n : n * n;
   g.lag = (int32_t)umax(1, umin(g.tiles / 4, cdiv(RESIDENT_HINT, per_group_hint)));
   if (tune.lag) g.lag = (int32_t)umax(1, umin(g.tiles, tune.lag));
   const uint64_t lag = (uint64_t)g.lag;
