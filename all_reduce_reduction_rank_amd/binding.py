@@ -127,6 +127,12 @@ def _ptrs(tensors, nranks, device):
     return (ctypes.c_void_p * nranks)(*[t.data_ptr() for t in tensors])
 
 
+def _sizes(tensors, want, what):
+    for i, t in enumerate(tensors):
+        if t.numel() != want:
+            raise ValueError(f"{what}[{i}] holds {t.numel()} elements; the call needs {want}")
+
+
 def _stream_handle(stream):
     import torch
 
@@ -166,11 +172,16 @@ class Comm:
         """Workgroup budget of later calls (0: the default, up to 3 per CU)."""
         _check(_lib().ar_comm_set_max_workgroups(self._h, max_workgroups), "ar_comm_set_max_workgroups")
 
-    def _call(self, name, send, recv, count, algo, proto, chunk_bytes, stream):
+    def _call(self, name, send, recv, count, algo, proto, chunk_bytes, stream, n_send, n_recv):
+        """n_send / n_recv: the elements every send / recv buffer must hold.
+        The C ABI sees only pointers, so a shorter tensor would let the kernel
+        read or write past it: sizes are checked here, before any launch."""
         dt = _dtype_name(send[0])
         for t in list(send) + list(recv):
             if _dtype_name(t) != dt:
                 raise TypeError("all rank buffers must share one dtype")
+        _sizes(send, n_send, "send")
+        _sizes(recv, n_recv, "recv")
         s, r = _ptrs(send, self.nranks, self.device), _ptrs(recv, self.nranks, self.device)
         status = getattr(_lib(), name)(self._h, s, r, count, DTYPES[dt], _algo(algo), _proto(proto),
                                        chunk_bytes, _stream_handle(stream))
@@ -188,6 +199,10 @@ class Comm:
         if send[0].dim() != 2:
             raise ValueError("rank buffers must be [rows, hidden]")
         rows, hidden = send[0].shape
+        for what, ts in (("send", send), ("out", out), ("residual", residual or [])):
+            for i, t in enumerate(ts):
+                if tuple(t.shape) != (rows, hidden):
+                    raise ValueError(f"{what}[{i}] has shape {tuple(t.shape)}; the call needs {(rows, hidden)}")
         if weight.numel() != hidden or not weight.is_contiguous() or not weight.is_cuda:
             raise ValueError("weight must be a contiguous device vector of `hidden` elements")
         s, o = _ptrs(send, self.nranks, self.device), _ptrs(out, self.nranks, self.device)
@@ -200,17 +215,22 @@ class Comm:
     def allreduce(self, send, recv=None, algo="ring", proto="simple", chunk_bytes=0, stream=None):
         """recv[r] = sum of send[0..N-1]; recv=None runs in place."""
         recv = send if recv is None else recv
-        self._call("ar_allreduce", send, recv, send[0].numel(), algo, proto, chunk_bytes, stream)
+        count = send[0].numel()
+        self._call("ar_allreduce", send, recv, count, algo, proto, chunk_bytes, stream, count, count)
         return recv
 
     def reduce_scatter(self, send, recv, algo="ring", proto="simple", chunk_bytes=0, stream=None):
         """send[i] holds N*recvcount elements; recv[r] receives slice r of the sum."""
-        self._call("ar_reduce_scatter", send, recv, recv[0].numel(), algo, proto, chunk_bytes, stream)
+        count = recv[0].numel()
+        self._call("ar_reduce_scatter", send, recv, count, algo, proto, chunk_bytes, stream, self.nranks * count,
+                   count)
         return recv
 
     def allgather(self, send, recv, algo="ring", proto="simple", chunk_bytes=0, stream=None):
         """recv[r] = send[0] | send[1] | ... | send[N-1]."""
-        self._call("ar_allgather", send, recv, send[0].numel(), algo, proto, chunk_bytes, stream)
+        count = send[0].numel()
+        self._call("ar_allgather", send, recv, count, algo, proto, chunk_bytes, stream, count,
+                   self.nranks * count)
         return recv
 
     def check(self, stream=None):

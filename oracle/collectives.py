@@ -20,7 +20,7 @@ here as follows.
   sends its partial of block (r-1-s) mod N to rank r+1, which adds its own
   input; in copy step s rank r sends block (r-s) mod N to rank r+1.  Block j's
   sum therefore starts at rank j+1 and ends at rank j, the rank that keeps it
-  ("reduce-scatter: each keeps only its slice of the sum").  The wire carries
+  (reduce-scatter leaves every rank holding just its own share of the sum).  The wire carries
   the payload type, so a bf16 partial is rounded after every hop.
 * Tree all-reduce (same section, tree: a double binary tree that reduces
   up the tree and then broadcasts down it, in O(log n) steps).  The page

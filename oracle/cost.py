@@ -11,7 +11,8 @@ all-reduce":
   S/beta; NVLS 2 alpha + S/beta.  The page evaluates these at n=8,
   alpha=1.5 us, beta=450 GB/s.
 * section "Reading nccl-tests": algbw = S/t; busbw = algbw times 2(n-1)/n for
-  all-reduce, (n-1)/n for all-gather and reduce-scatter, 1 for broadcast.
+  all-reduce, (n-1)/n for the reduce-scatter and the all-gather, and 1 for a
+  broadcast.
 * section "Exercises", exercise 2: the one-shot / two-shot crossover
   S* = 2 alpha beta / ((n-1)(1 - 2/n)); no crossover at n=2.
 """

@@ -1,13 +1,14 @@
 """LL and LL128 line codecs (test infrastructure only).
 
 "Collective communication: NCCL's algorithms and protocols, and custom
-all-reduce", section "Protocols: how do you know the data has arrived":
+all-reduce", section "Protocols" (its table of the three transports):
 
-* LL: every 8 bytes hold 4 bytes of data and 4 bytes of flag; the receiver
-  polls the flag; about 50 % bandwidth efficiency.
-* LL128: every 128 bytes hold 120 bytes of data and 8 bytes of flag; about
-  94 % efficiency.
-* Simple: a large block, a memory fence, then a flag; close to 100 %.
+* LL line: 4 payload bytes + a 4-byte flag, 8 bytes in all; the reader spins
+  on the flag; half of the bytes moved are payload.
+* LL128 line: 120 payload bytes + an 8-byte flag, 128 bytes in all; 15/16 of
+  the bytes moved are payload (the page rounds this to 94 %).
+* Simple: a whole block is written, fenced, then signalled by one flag;
+  practically every byte moved is payload.
 
 The pages give only the byte counts.  Layout taken (little-endian):
 LL line = payload bytes 0-3, flag (uint32) bytes 4-7; LL128 line = payload

@@ -7,8 +7,8 @@ than from a closed form:
   quantity the pages reason about ("Collective communication: NCCL's
   algorithms and protocols, and custom all-reduce", section "Algorithms":
   ring sends and receives 2(n-1)/n S per GPU, one-shot reads (n-1) S, two-shot
-  reads 2(n-1)/n S; section "Reading nccl-tests": (n-1)/n for all-gather and
-  reduce-scatter);
+  reads 2(n-1)/n S; section "Reading nccl-tests": the reduce-scatter and the
+  all-gather move (n-1)/n S);
 * HBM bytes per call -- what the single-GPU simulation of all N rank
   programs reads and writes in device memory.  Ranks share one HBM, so a
   "link transfer" is the receiver reading the sender's buffer (Simple) or

@@ -177,8 +177,6 @@ def test_sweep_small_sizes_full_compare(n, dt):
 @pytest.mark.parametrize("proto", PROTOS)
 @pytest.mark.parametrize("algo", ALGOS)
 def test_sweep_large_sizes_sampled(algo, proto, mib):
-    if proto == "ll" and mib > 8 and algo == "oneshot":
-        pytest.skip("LL one-shot at 128 MiB: N*2*S of staging; covered at 8 MiB")
     check_allreduce_sampled(8, mib * (1 << 20) // 4, "f32", algo, proto, "normal", seed=mib)
 
 

@@ -123,7 +123,7 @@ def _order_probe(n, per_block, dt="f32"):
 @pytest.mark.parametrize("n", [3, 4, 5, 8])
 def test_ring_sum_starts_after_owner_and_ends_at_owner(n):
     # Ring: reduce steps pass block j from rank j+1 around to rank j, which
-    # keeps it ("each keeps only its slice of the sum").  With the probe the
+    # keeps it (after a reduce-scatter a rank holds only its own share).  With the probe the
     # sum is 2**24 (+1 lost) ... (+1 lost) - 2**24 = 0 exactly.
     x, blocks = _order_probe(n, 3)
     for out in C.allreduce_ring(x, "f32", chunk_bytes=16):

@@ -2,6 +2,7 @@
 and signal graph against what the pages print and what arithmetic fixes."""
 
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -208,6 +209,59 @@ def test_hbm_bytes_ll_is_wire_expansion():
     assert ring_ll == 2 * n * s + 4 * (n - 1) * 2 * s
     ring_128 = traffic.tally("allreduce", "ring", "ll128", n, count, "f32").hbm
     assert ring_128 * 15 == (2 * n * s) * 15 + 4 * (n - 1) * 16 * s
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 8])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("proto,e", [("ll", Fraction(2)), ("ll128", Fraction(16, 15))])
+def test_hbm_bytes_line_protocols_closed_forms(n, dt, proto, e):
+    # Closed forms derived by hand from the schedules ("Algorithms": one-shot
+    # reads every rank's input, two-shot reduces a slice per rank and gathers
+    # the slice sums back, the ring does N-1 reduce hops and N-1 copy hops;
+    # "Protocols": a line-protocol transfer is the sender writing e bytes of
+    # lines per payload byte and the receiver reading them), with the staging
+    # rules of this design: a rank puts its own input on the wire once, a rank
+    # that just produced a value forwards it from registers, the own input is
+    # read directly except in place.  e = 2 (LL) and 128/120 = 16/15 (LL128);
+    # every block is a whole number of 120-byte lines, so e is exact.  S is
+    # the per-rank buffer (all-reduce: count bytes; RS/AG: N shards).
+    es = 4 if dt == "f32" else 2
+    c = 240 * 3                       # block / shard bytes: 6 LL128 lines, a multiple of 16
+    cnt = c // es
+    s = n * c
+    ar = lambda algo, **kw: traffic.tally("allreduce", algo, proto, n, n * cnt, dt, **kw).hbm  # noqa: E731
+    rs = lambda algo: traffic.tally("reduce_scatter", algo, proto, n, cnt, dt).hbm  # noqa: E731
+    ag = lambda algo: traffic.tally("allgather", algo, proto, n, cnt, dt).hbm  # noqa: E731
+    # one-shot: every rank publishes its input (S read, eS written), then each
+    # rank reads its own input and N-1 peers' lines and writes S
+    assert ar("oneshot") == n * (3 + n * e) * s
+    # ... in place: each rank reads all N ranks' lines, its own included
+    assert ar("oneshot", in_place=True) == n * (2 + (n + 1) * e) * s
+    # two-shot, per slice c = S/N: N-1 senders (c read, ec written); the owner
+    # reads c and (N-1) ec, writes c and publishes ec; N-1 readers (ec read,
+    # c written): 2N c + (3N-2) e c
+    assert ar("twoshot") == 2 * n * s + (3 * n - 2) * e * s
+    assert ar("ring") == 2 * n * s + 4 * (n - 1) * e * s
+    # reduce-scatter, per slice: N-1 senders put it on the wire; the owner
+    # reads its own slice and N-1 lines and writes c.  The ring: the first
+    # sender (c, ec), N-1 hops reading ec + c, all but the last forwarding ec,
+    # the last writing c.  Both come to (N+1) c + 2(N-1) e c.
+    assert rs("twoshot") == rs("oneshot") == (n + 1) * s + 2 * (n - 1) * e * s
+    assert rs("ring") == (n + 1) * s + 2 * (n - 1) * e * s
+    # all-gather, per shard: the owner reads it, keeps a copy and publishes it
+    # once (c read, c + ec written); N-1 receivers read ec and write c
+    assert ag("twoshot") == ag("oneshot") == (n + 1) * s + n * e * s
+    # ... ring: the owner's copy and first send, N-1 hops (ec read, c
+    # written), all but the last forwarding ec
+    assert ag("ring") == (n + 1) * s + 2 * (n - 1) * e * s
+
+
+def test_hbm_bytes_simple_in_place_one_shot():
+    # In place, each rank program still reads all N inputs and writes one
+    # output: N(N+1) S, the same as out of place.
+    n, count = 8, 8 * 4 * 100
+    s = count * 4
+    assert traffic.tally("allreduce", "oneshot", "simple", n, count, "f32", in_place=True).hbm == n * (n + 1) * s
 
 
 # --------------------------------------------------------------- signals
