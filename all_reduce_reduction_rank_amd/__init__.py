@@ -3,5 +3,5 @@ reduce-scatter and all-gather over N simulated rank buffers on one GPU, with
 Simple, LL and LL128 transports.  The work runs in hand-written HIP kernels
 (libar.so, C ABI in include/ar.h); ``binding`` marshals arguments to it."""
 
-from .binding import (ALGOS, DTYPES, OPS, PROTOS, ARError, Comm, library,  # noqa: F401
+from .binding import (ALGOS, DTYPES, OPS, PROTOS, ARError, Comm, allreduce_noalloc, library,  # noqa: F401
                       plan_bytes, select)

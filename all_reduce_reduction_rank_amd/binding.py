@@ -40,6 +40,7 @@ SYMBOLS = (
     "ar_comm_create", "ar_comm_destroy", "ar_comm_check", "ar_comm_reset",
     "ar_comm_workspace_bytes", "ar_comm_set_max_workgroups", "ar_allreduce", "ar_allreduce_rmsnorm", "ar_reduce_scatter", "ar_allgather",
     "ar_plan_bytes", "ar_select", "ar_debug_inject", "ar_debug_state", "ar_status_string",
+    "ar_allreduce_noalloc",
 )
 
 
@@ -65,6 +66,7 @@ def _declare(lib):
     lib.ar_allreduce_rmsnorm.argtypes = [P, PP, PP, PP, P, S, S, ctypes.c_float, I, P]
     for name in ("ar_allreduce", "ar_reduce_scatter", "ar_allgather"):
         getattr(lib, name).argtypes = [P, PP, PP, S, I, I, I, S, P]
+    lib.ar_allreduce_noalloc.argtypes = [I, PP, PP, S, I, I, I, S, P]
     lib.ar_plan_bytes.argtypes = [I, I, S, I, I, I, S, I, ctypes.POINTER(U64), ctypes.POINTER(U64),
                                   ctypes.POINTER(U64), ctypes.POINTER(U64)]
     lib.ar_select.argtypes = [I, I, S, I, I, I, S, ctypes.POINTER(I), ctypes.POINTER(I),
@@ -252,6 +254,28 @@ class Comm:
 
     def inject(self, rank: int, step: int, timeout_us: int = 0):
         _check(_lib().ar_debug_inject(self._h, rank, step, timeout_us), "ar_debug_inject")
+
+
+def allreduce_noalloc(send, recv=None, algo="ring", proto="simple", chunk_bytes=0, stream=None):
+    """ar_allreduce_noalloc: recv[r] = sum of send[0..N-1] with N = len(send),
+    on the current device, with no communicator and no device allocation
+    (Simple only, at most 1 GiB per rank).  recv=None runs in place."""
+    import torch
+
+    recv = send if recv is None else recv
+    n = len(send)
+    dt = _dtype_name(send[0])
+    for t in list(send) + list(recv):
+        if _dtype_name(t) != dt:
+            raise TypeError("all rank buffers must share one dtype")
+    count = send[0].numel()
+    _sizes(send, count, "send")
+    _sizes(recv, count, "recv")
+    dev = torch.cuda.current_device()
+    s, r = _ptrs(send, n, dev), _ptrs(recv, n, dev)
+    _check(_lib().ar_allreduce_noalloc(n, s, r, count, DTYPES[dt], _algo(algo), _proto(proto), chunk_bytes,
+                                       _stream_handle(stream)), "ar_allreduce_noalloc")
+    return recv
 
 
 def select(nranks, op, count, dtype, algo="auto", proto="auto", max_line_bytes_per_rank=0):

@@ -1,6 +1,6 @@
 """Build libar.so (the HIP all-reduce library) for gfx950 with hipcc.
 
-The two translation units compile in parallel; the result lands next to this
+The translation units compile in parallel; the result lands next to this
 file so it travels with the source tree.
 """
 
@@ -13,7 +13,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libar.so")
-SOURCES = ("api.hip", "kernels.hip", "rmsnorm.hip")
+SOURCES = ("api.hip", "kernels.hip", "rmsnorm.hip", "noalloc.hip")
 
 # -packed-fp32-ops: keep hipcc from fusing float adds into packed-FP32
 # instructions.  No fast-math, no denormal flushing: fp32 adds stay IEEE.

@@ -25,12 +25,8 @@
 #include "../../include/ar.h"
 #include "device.hpp"
 #include "plan.hpp"
+#include "call.hpp"
 #include "rmsnorm.hpp"
-
-namespace ar {
-hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uint32_t max_workgroups);
-hipError_t launch_reset(Ctl* c, hipStream_t stream);
-}  // namespace ar
 
 using namespace ar;
 
@@ -247,29 +243,27 @@ static bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   return na && nb && x < y + nb && y < x + na;
 }
 
-static ar_status run(ar_comm_t c, int op, const void* const* send, void* const* recv, uint64_t count,
-                     int dtype, int algo, int proto, uint64_t chunk_bytes, ar_stream_t stream) {
-  if (!c || !send || !recv) return AR_ERR_INVALID;
-  if (c->broken) return AR_ERR_BROKEN;
+ar_status ar::plan_call(int op, int n, const void* const* send, void* const* recv, uint64_t count, int dtype,
+                        int algo, int proto, uint64_t chunk_bytes, uint64_t max_bytes, uint64_t max_line_bytes,
+                        const Tuning& tune, Geometry* out) {
+  memset(out, 0, sizeof(*out));
+  if (!send || !recv) return AR_ERR_INVALID;
   if (dtype < 0 || dtype > 2 || algo < 0 || algo > ALGO_AUTO || proto < 0 || proto > PROTO_AUTO)
     return AR_ERR_INVALID;
   if (count == 0) return AR_OK;  // nothing to move; buffers may be null
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev != c->device) return AR_ERR_INVALID;
-  const int n = c->nranks;
   const uint64_t es = (uint64_t)esize_of(dtype);
   const uint64_t in_bytes = (op == OP_REDUCE_SCATTER ? (uint64_t)n * count : count) * es;
   const uint64_t out_bytes = (op == OP_ALLGATHER ? (uint64_t)n * count : count) * es;
   if (count > (1ull << 40)) return AR_ERR_TOO_LARGE;
   const uint64_t rank_bytes = umax(in_bytes, out_bytes);
-  if (rank_bytes > c->max_bytes) return AR_ERR_TOO_LARGE;
+  if (rank_bytes > max_bytes) return AR_ERR_TOO_LARGE;
   if (algo == ALGO_AUTO || proto == PROTO_AUTO) {
-    const bool line_ok = n > 1 && rank_bytes <= c->max_line_bytes;
+    const bool line_ok = n > 1 && rank_bytes <= max_line_bytes;
     if (!select_schedule(op, n, dtype, rank_bytes, algo, proto, line_ok, &algo, &proto, nullptr))
       return AR_ERR_INVALID;
   }
   if (algo == ALGO_TREE && n > 1 && (op != OP_ALLREDUCE || proto != PROTO_SIMPLE)) return AR_ERR_UNSUPPORTED;
-  if (proto != PROTO_SIMPLE && n > 1 && rank_bytes > c->max_line_bytes) return AR_ERR_TOO_LARGE;
+  if (proto != PROTO_SIMPLE && n > 1 && rank_bytes > max_line_bytes) return AR_ERR_TOO_LARGE;
 
   int in_place = 0, same = 0;
   for (int r = 0; r < n; ++r) {
@@ -286,17 +280,30 @@ static ar_status run(ar_comm_t c, int op, const void* const* send, void* const* 
       if (!in_place && overlap(recv[r], out_bytes, send[q], in_bytes)) return AR_ERR_INVALID;
     }
   }
+  if (!make_geometry(op, algo, proto, dtype, n, count, chunk_bytes, in_place, out, tune)) return AR_ERR_INVALID;
+  if (out->ntasks >= (1ull << 31)) return AR_ERR_TOO_LARGE;
+  return AR_OK;
+}
 
+static ar_status run(ar_comm_t c, int op, const void* const* send, void* const* recv, uint64_t count,
+                     int dtype, int algo, int proto, uint64_t chunk_bytes, ar_stream_t stream) {
+  if (!c || !send || !recv) return AR_ERR_INVALID;
+  if (c->broken) return AR_ERR_BROKEN;
+  if (dtype < 0 || dtype > 2 || algo < 0 || algo > ALGO_AUTO || proto < 0 || proto > PROTO_AUTO)
+    return AR_ERR_INVALID;
+  if (count == 0) return AR_OK;  // nothing to move; buffers may be null
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != c->device) return AR_ERR_INVALID;
   Geometry g;
-  if (!make_geometry(op, algo, proto, dtype, n, count, chunk_bytes, in_place, &g, tuning())) return AR_ERR_INVALID;
-  if (g.ntasks == 0) return AR_OK;
-  if (g.ntasks >= (1ull << 31)) return AR_ERR_TOO_LARGE;
+  const ar_status st = plan_call(op, c->nranks, send, recv, count, dtype, algo, proto, chunk_bytes, c->max_bytes,
+                                 c->max_line_bytes, tuning(), &g);
+  if (st != AR_OK || g.ntasks == 0) return st;
   const int li = g.proto == PROTO_LL128 ? 1 : 0;
   if (g.nflags > c->nflags || staging_bytes(g) > c->lines_bytes[li]) return AR_ERR_TOO_LARGE;
 
   KArgs a;
   memset(&a, 0, sizeof(a));
-  for (int r = 0; r < n; ++r) {
+  for (int r = 0; r < c->nranks; ++r) {
     a.in[r] = (const char*)send[r];
     a.out[r] = (char*)recv[r];
   }

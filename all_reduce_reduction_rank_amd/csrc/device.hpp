@@ -282,6 +282,8 @@ struct KArgs {
   uint32_t fixed;       // 1: workgroup b runs tickets [b*batch, (b+1)*batch) and
                         //    touches no counter (tasks that never wait, one pass)
   uint32_t fold;        // 1: one-shot tasks load every term of a pass at once
+  uint32_t rearm_errors;  // 1: the last workgroup out also clears the abort word
+                          //    and error record (workspaces no host call resets)
 };
 
 __device__ __forceinline__ void note_blocked(Ctl* c, int step, int rank) {

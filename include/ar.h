@@ -254,6 +254,35 @@ ar_status ar_debug_inject(ar_comm_t comm, int rank, int step, uint64_t timeout_u
  * above) add to neither [5] nor [6]. */
 ar_status ar_debug_state(ar_comm_t comm, ar_stream_t stream, uint64_t* out, int n);
 
+/* The all-reduce of ar_allreduce without a communicator, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It allocates nothing (no hipMalloc,
+ * no hipFree, no allocating library routine); its kernels keep their control
+ * block and flags in a fixed 8 MiB device array built into the library, one
+ * copy per GPU, held until the process ends.
+ * Arguments and results are those of ar_allreduce on a communicator of
+ * `nranks` ranks (same schedules, same kernels, the same bits), with the
+ * current HIP device as the device, these limits:
+ *   - proto AR_SIMPLE or AR_PROTO_AUTO (which then picks Simple): AR_LL and
+ *     AR_LL128 return AR_ERR_UNSUPPORTED (their line staging grows with the
+ *     message);
+ *   - count*esize at most 1 GiB per rank (AR_ERR_TOO_LARGE beyond);
+ *   - no workgroup budget, no environment overrides.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (on two streams, or a graph replay beside another call) race and must be
+ * ordered by the caller.  The first call on a device clears the array (one
+ * small kernel on `stream`, ahead of the collective); every call's kernel
+ * leaves its counters and error record cleared for the next.  A wait that
+ * passes the 5 s limit (which no correct call reaches: one kernel runs every
+ * rank program, in an order that cannot deadlock) makes that call give up
+ * with its outputs undefined; no later call reports it.
+ * Errors (returned at once, nothing launched): AR_ERR_INVALID,
+ * AR_ERR_UNSUPPORTED, AR_ERR_TOO_LARGE; AR_ERR_HIP if the device array
+ * cannot be reached or a launch fails. */
+ar_status ar_allreduce_noalloc(int nranks, const void* const* sendbufs, void* const* recvbufs,
+                               size_t count, ar_dtype dtype, ar_algo algo, ar_proto proto,
+                               size_t chunk_bytes, ar_stream_t stream);
+
 /* Static description of a status code. */
 const char* ar_status_string(ar_status status);
 

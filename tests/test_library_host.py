@@ -91,3 +91,46 @@ def test_tree_is_all_reduce_with_simple_only():
                       ("allgather", "simple")):
         with pytest.raises(binding.ARError):
             binding.plan_bytes(4, op, 1000, "f32", "tree", proto)
+
+
+def test_noalloc_argument_errors_need_no_device():
+    # Argument checks come before any HIP call: these run without a GPU.
+    import ctypes
+    lib = binding.library()
+    P = ctypes.c_void_p
+    ptrs = (P * 8)(*[0x10000 * (i + 1) for i in range(8)])
+    outs = (P * 8)(*[0x10000000 * (i + 1) for i in range(8)])
+    st = lambda n, count, dt=0, algo=2, proto=0, s=ptrs, r=outs: lib.ar_allreduce_noalloc(  # noqa: E731
+        n, s, r, count, dt, algo, proto, 0, None)
+    assert st(9, 16) == 1 and st(0, 16) == 1                  # AR_ERR_INVALID: rank count
+    assert st(8, 16, proto=1) == 2 and st(8, 16, proto=2) == 2  # LL / LL128: AR_ERR_UNSUPPORTED
+    assert st(8, (1 << 28) + 1) == 4                          # fp32 above 1 GiB per rank: AR_ERR_TOO_LARGE
+    assert st(8, (1 << 29) + 4, dt=1) == 4                    # bf16 likewise
+    assert st(8, 0) == 0                                      # count 0: nothing to do
+    assert st(8, 16, algo=5) == 1 and st(8, 16, dt=3) == 1    # bad enums
+    assert st(2, 16, s=None) == 1                             # null pointer array
+    odd = (P * 8)(*[0x10000 * (i + 1) + 4 for i in range(8)])
+    assert st(4, 16, s=odd) == 1                              # misaligned rank buffer
+
+
+def test_noalloc_device_array_holds_every_schedule_up_to_one_gib():
+    # On a host with no GPU a call that passes every argument and capacity
+    # check stops at the first HIP call (AR_ERR_HIP); one whose flags would
+    # not fit the device array stops earlier with AR_ERR_TOO_LARGE.  Every
+    # schedule, in and out of place, must fit at the 1 GiB limit.
+    import ctypes
+
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("needs a host without a GPU: the fake pointers below must never reach a kernel")
+    lib = binding.library()
+    P = ctypes.c_void_p
+    for n in range(2, 9):
+        ptrs = (P * n)(*[(1 << 40) * (i + 1) for i in range(n)])
+        outs = (P * n)(*[(1 << 40) * (i + 1) + (1 << 39) for i in range(n)])
+        for algo in range(5):
+            for dt, es in ((0, 4), (1, 2)):
+                count = (1 << 30) // es
+                for recv in (outs, ptrs):  # out of place, in place
+                    st = lib.ar_allreduce_noalloc(n, ptrs, recv, count, dt, algo, 0, 0, None)
+                    assert st == 5, (n, algo, dt, recv is ptrs, st)
