@@ -40,8 +40,17 @@ SYMBOLS = (
     "ar_comm_create", "ar_comm_destroy", "ar_comm_check", "ar_comm_reset",
     "ar_comm_workspace_bytes", "ar_comm_set_max_workgroups", "ar_allreduce", "ar_allreduce_rmsnorm", "ar_reduce_scatter", "ar_allgather",
     "ar_plan_bytes", "ar_select", "ar_debug_inject", "ar_debug_state", "ar_status_string",
-    "ar_allreduce_noalloc",
+    "ar_allreduce_noalloc", "ar_debug_calls",
 )
+
+
+class CallRecord(ctypes.Structure):
+    """ar_call_record (include/ar.h)."""
+    _fields_ = [("seq", ctypes.c_uint64), ("op", ctypes.c_int32), ("algo", ctypes.c_int32),
+                ("proto", ctypes.c_int32), ("dtype", ctypes.c_int32), ("nranks", ctypes.c_int32),
+                ("in_place", ctypes.c_int32), ("grid", ctypes.c_uint32), ("batch", ctypes.c_uint32),
+                ("counter_free", ctypes.c_uint32), ("pad", ctypes.c_uint32), ("count", ctypes.c_uint64),
+                ("ntasks", ctypes.c_uint64), ("tile_bytes", ctypes.c_uint64)]
 
 
 class ARError(RuntimeError):
@@ -67,6 +76,7 @@ def _declare(lib):
     for name in ("ar_allreduce", "ar_reduce_scatter", "ar_allgather"):
         getattr(lib, name).argtypes = [P, PP, PP, S, I, I, I, S, P]
     lib.ar_allreduce_noalloc.argtypes = [I, PP, PP, S, I, I, I, S, P]
+    lib.ar_debug_calls.argtypes = [P, ctypes.POINTER(CallRecord), I, ctypes.POINTER(I)]
     lib.ar_plan_bytes.argtypes = [I, I, S, I, I, I, S, I, ctypes.POINTER(U64), ctypes.POINTER(U64),
                                   ctypes.POINTER(U64), ctypes.POINTER(U64)]
     lib.ar_select.argtypes = [I, I, S, I, I, I, S, ctypes.POINTER(I), ctypes.POINTER(I),
@@ -251,6 +261,21 @@ class Comm:
         keys = ("timeouts", "flag_index", "seen", "awaited", "epoch_then", "tasks_done", "calls", "ticket",
                 "done", "abort")
         return dict(zip(keys, list(out)))
+
+    def debug_calls(self, max_calls=16):
+        """The communicator's most recent calls (ar_debug_calls), oldest first."""
+        recs = (CallRecord * max_calls)()
+        n = ctypes.c_int()
+        _check(_lib().ar_debug_calls(self._h, recs, max_calls, ctypes.byref(n)), "ar_debug_calls")
+        names = ({v: k for k, v in OPS.items()}, {v: k for k, v in ALGOS.items()}, {v: k for k, v in PROTOS.items()},
+                 {v: k for k, v in DTYPES.items()})
+        out = []
+        for r in recs[:n.value]:
+            d = {f: getattr(r, f) for f, _ in CallRecord._fields_ if f != "pad"}
+            d["op"], d["algo"], d["proto"], d["dtype"] = (names[0][r.op], names[1][r.algo], names[2][r.proto],
+                                                          names[3][r.dtype])
+            out.append(d)
+        return out
 
     def inject(self, rank: int, step: int, timeout_us: int = 0):
         _check(_lib().ar_debug_inject(self._h, rank, step, timeout_us), "ar_debug_inject")

@@ -19,6 +19,7 @@
 // this or an earlier call; LL128 flag words (bytes 120-127 of each line)
 // likewise only ever hold LL128 flags.
 #include <hip/hip_runtime.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -26,6 +27,7 @@
 #include "device.hpp"
 #include "plan.hpp"
 #include "call.hpp"
+#include "calllog.hpp"
 #include "rmsnorm.hpp"
 
 using namespace ar;
@@ -48,16 +50,19 @@ struct ar_comm {
   int inj_rank = -1, inj_step = -1;
   uint32_t max_workgroups = 0;  // 0: as many as fit on the GPU
   bool broken = false;
+  CallLog log;                  // the most recent calls launched
 };
 
 static uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }
 
 // Tuning overrides read once from the environment (for measurements; they
-// never change results): AR_TILE_KB, AR_RING_SKEW, AR_RING_WINDOW, AR_LAG.
+// never change results): AR_TILE_KB, AR_LINE_TILE_KB, AR_RING_SKEW,
+// AR_RING_WINDOW, AR_LAG.
 static const Tuning& tuning() {
   static const Tuning t = [] {
     Tuning x;
     if (const char* e = getenv("AR_TILE_KB")) x.tile_bytes = strtoull(e, nullptr, 10) * 1024;
+    if (const char* e = getenv("AR_LINE_TILE_KB")) x.line_tile_bytes = strtoull(e, nullptr, 10) * 1024;
     if (const char* e = getenv("AR_RING_SKEW")) { x.ring_skew = strtoull(e, nullptr, 10); x.ring_skew_set = true; }
     if (const char* e = getenv("AR_RING_WINDOW")) x.ring_window = strtoull(e, nullptr, 10);
     if (const char* e = getenv("AR_LAG")) x.lag = strtoull(e, nullptr, 10);
@@ -162,6 +167,21 @@ ar_status ar_comm_check(ar_comm_t c, ar_stream_t stream, int* err_rank, int* err
   if (hipMemcpy(&h, c->ctl, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return AR_ERR_HIP;
   if (!h.err_code) return AR_OK;
   c->broken = true;
+  if (debug_enabled()) {
+    fprintf(stderr,
+            "[ar] latched error %d: first blocked wait rank %d step %d; flag %llu held %llu, awaited %llu "
+            "(call counter %llu); last calls:\n",
+            (int)h.err_code, h.err_key == 0xffffffffu ? -1 : (int)(h.err_key & 0xff),
+            h.err_key == 0xffffffffu ? -1 : (int)(h.err_key >> 8), (unsigned long long)h.diag[1],
+            (unsigned long long)h.diag[2], (unsigned long long)h.diag[3], (unsigned long long)h.diag[4]);
+    ar_call_record recs[CallLog::CAP];
+    const int n = c->log.copy(recs, CallLog::CAP);
+    for (int i = 0; i < n; ++i) {
+      char line[320];
+      format_record(line, sizeof(line), recs[i]);
+      fprintf(stderr, "[ar]   %s\n", line);
+    }
+  }
   if (err_rank) *err_rank = h.err_key == 0xffffffffu ? -1 : (int)(h.err_key & 0xff);
   if (err_step) *err_step = h.err_key == 0xffffffffu ? -1 : (int)(h.err_key >> 8);
   return (ar_status)h.err_code;
@@ -181,6 +201,12 @@ ar_status ar_debug_state(ar_comm_t c, ar_stream_t stream, uint64_t* out, int n) 
   const uint64_t words[10] = {h.diag[0], h.diag[1], h.diag[2], h.diag[3], h.diag[4], h.diag[5],
                               h.epoch, h.ticket, h.done, h.abort};
   for (int i = 0; i < n && i < 10; ++i) out[i] = words[i];
+  return AR_OK;
+}
+
+ar_status ar_debug_calls(ar_comm_t c, ar_call_record* out, int max, int* n_out) {
+  if (!c || !n_out || max < 0 || (max > 0 && !out)) return AR_ERR_INVALID;
+  *n_out = c->log.copy(out, max);
   return AR_OK;
 }
 
@@ -316,8 +342,29 @@ static ar_status run(ar_comm_t c, int op, const void* const* send, void* const* 
   a.timeout = c->timeout_ticks;
   a.inj_rank = c->inj_rank;
   a.inj_step = c->inj_step;
-  return ar::launch_collective(a, c->device, (hipStream_t)stream, c->max_workgroups) == hipSuccess ? AR_OK
-                                                                                             : AR_ERR_HIP;
+  LaunchInfo info;
+  if (ar::launch_collective(a, c->device, (hipStream_t)stream, c->max_workgroups, &info) != hipSuccess)
+    return AR_ERR_HIP;
+  ar_call_record rec = {};
+  rec.op = op;
+  rec.algo = g.algo;
+  rec.proto = g.proto;
+  rec.dtype = g.dtype;
+  rec.nranks = g.nranks;
+  rec.in_place = g.in_place;
+  rec.grid = info.grid;
+  rec.batch = info.batch;
+  rec.counter_free = info.counter_free;
+  rec.count = count;
+  rec.ntasks = g.ntasks;
+  rec.tile_bytes = g.tile * (uint64_t)g.esize;
+  c->log.add(rec);
+  if (debug_enabled()) {
+    char line[320];
+    format_record(line, sizeof(line), c->log.ring[(c->log.logged - 1) % CallLog::CAP]);
+    fprintf(stderr, "[ar] %s\n", line);
+  }
+  return AR_OK;
 }
 
 extern "C" {

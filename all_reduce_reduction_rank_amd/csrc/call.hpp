@@ -22,7 +22,16 @@ ar_status plan_call(int op, int n, const void* const* send, void* const* recv, u
                     int algo, int proto, uint64_t chunk_bytes, uint64_t max_bytes, uint64_t max_line_bytes,
                     const Tuning& tune, Geometry* out);
 
-hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uint32_t max_workgroups);
+// How a call was launched (for the call log and AR_DEBUG).
+struct LaunchInfo {
+  uint32_t grid = 0, batch = 0, counter_free = 0;
+};
+
+hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uint32_t max_workgroups,
+                             LaunchInfo* info = nullptr);
+
+// AR_DEBUG is set in the environment (read once).
+bool debug_enabled();
 hipError_t launch_reset(Ctl* c, hipStream_t stream);
 
 }  // namespace ar

@@ -14,11 +14,11 @@
 // all-gather, ring = reduce-scatter + all-gather); the transfer encodings
 // follow the former page's section "Protocols" (see device.hpp).
 #include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 
-#include "device.hpp"
-#include "plan.hpp"
+#include "call.hpp"
 
 namespace ar {
 
@@ -34,6 +34,10 @@ constexpr int U_SIMPLE = 4;  // 16-byte vectors in flight per thread per source
 constexpr int U_LL = 4;      // LL words per thread per pass
 constexpr int U_LL128 = 4;   // LL128 line groups (8 lines of a wave) per pass of the N-term gather
 constexpr int U_LL128_PASS = 4;  // ... and per pass of a one- or two-term pass (ring, send, copy)
+// Line groups of the N-term gather whose payload loads go out together.
+// Measured at N=8, 256 MiB fp32: two-shot LL128 2742 us with 1 and 2821 with
+// 2; one-shot LL128 4624 and 4459; 30 KiB tiles keep that split.
+constexpr int GATHER_GROUPS = 1;
 
 // =============================================================== Simple path
 // dst = fold(term(0), ..., term(n-1)) over `nbytes` (whole elements, at most
@@ -283,10 +287,16 @@ __device__ __forceinline__ bool wg_wait(const KArgs& a, const uint64_t* f, uint6
 // the next step's store of s+1 and move the flag backwards.  The barrier that
 // ends every task in the ticket loop keeps this lane-0 store from sharing a
 // divergent path with the next ticket fetch.
+// The host's debug injection: rank program `rank` withholds what it sends at
+// step `step` (a Simple signal, the flag of each LL or LL128 line).
+__device__ __forceinline__ bool withheld(const KArgs& a, int step, int rank) {
+  return rank == a.inj_rank && step == a.inj_step;
+}
+
 __device__ __forceinline__ void wg_signal(const KArgs& a, uint64_t* f, uint64_t v, int step, int rank) {
   wait_mem();
   __syncthreads();
-  if (threadIdx.x == 0 && !(rank == a.inj_rank && step == a.inj_step)) raise_flag(f, v);
+  if (threadIdx.x == 0 && !withheld(a, step, rank)) raise_flag(f, v);
 }
 
 // ============================================================ LL / LL128 path
@@ -429,7 +439,7 @@ __device__ __forceinline__ void ll_pass(const KArgs& a, Terms terms, int nterms,
       if (w >= nwords) continue;
       const uint32_t r = (nterms > 1) ? acc[u].narrow() : val[u];
       if (out_plain) st_word(out_plain + 4 * w, r, (uint32_t)umin(4, nbytes - 4 * w), es);
-      if (out_lines) st_flag((uint64_t*)out_lines + w, ((uint64_t)flag << 32) | r);
+      if (out_lines && !withheld(a, step, rank)) st_flag((uint64_t*)out_lines + w, ((uint64_t)flag << 32) | r);
     }
   }
 }
@@ -602,7 +612,7 @@ __device__ __forceinline__ void ll128_pass(const KArgs& a, Terms terms, int nter
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint64_t line = l0 + (uint64_t)u * 8 + grp;
-        if (q == 7 && line < nlines)
+        if (q == 7 && line < nlines && !withheld(a, step, rank))
           st_flag((uint64_t*)(out_lines + line * LL128_LINE + LL128_DATA), flag);
       }
     }
@@ -629,6 +639,18 @@ __device__ __forceinline__ void ll128_gather(const KArgs& a, Terms terms, int nt
   constexpr int FLAG_LOADS = (MAX_RANKS * 32 + 63) / 64;
   const int pi = plain_term(terms, nterms);
   const int li = line_term(terms, nterms);
+  // One buffer resource per term slot: a line term's staging, or an empty
+  // resource (reads give zeros, nothing is fetched) for the plain term and
+  // for slots past nterms.
+  Rsrc rl[MAX_RANKS];
+  bool is_line[MAX_RANKS];
+#pragma unroll
+  for (int i = 0; i < MAX_RANKS; ++i) {  // no early exit: terms past nterms read nothing
+    const LTerm tm = terms(i);             // address arithmetic only
+    is_line[i] = i < nterms && tm.lines != nullptr;
+    rl[i] = make_rsrc(is_line[i] ? tm.lines : a.lines, is_line[i] ? (uint32_t)(nlines * LL128_LINE) : 0u);
+  }
+  const Rsrc rout = make_rsrc(out_lines ? out_lines : a.lines, out_lines ? (uint32_t)(nlines * LL128_LINE) : 0u);
   for (uint64_t l0 = (uint64_t)wave * U_LL128 * 8; l0 < nlines; l0 += 4ull * U_LL128 * 8) {
     {
       // Terms 2k and 2k+1 are evaluated for the wave (uniform), each lane
@@ -676,44 +698,45 @@ __device__ __forceinline__ void ll128_gather(const KArgs& a, Terms terms, int nt
       }
     }
     // Every lane of the wave is past its polls: all flags of the pass are
-    // seen.  Per line group, every term's piece in one round trip.
+    // seen.  Payload: every term's piece of GATHER_GROUPS line groups in one
+    // round trip (a lane past the tile's last line reads outside the buffer
+    // resource and gets zeros; a term past nterms reads through an empty
+    // one), then the sums in term order.
 #pragma unroll
-    for (int u = 0; u < U_LL128; ++u) {
-      const uint32_t line = (uint32_t)(l0 + (uint64_t)u * 8 + grp);
-      const uint64_t off = (uint64_t)line * LL128_DATA + 16ull * q;
-      const uint32_t nb = (line < nlines && off < nbytes) ? (uint32_t)umin(lane_cap, nbytes - off) : 0u;
-      // Every line term's piece with no branch between the loads, then the
-      // plain term's piece, so they all go out before the first wait (a lane
-      // past the tile's last line reads outside the buffer resource and gets
-      // zeros; the plain term's slot reads through an empty one).
-      uint4 x[MAX_RANKS];
-      bool is_line[MAX_RANKS];
+    for (int u0 = 0; u0 < U_LL128; u0 += GATHER_GROUPS) {
+      uint4 x[GATHER_GROUPS][MAX_RANKS];
+      uint4 xp[GATHER_GROUPS];
+      uint32_t nb[GATHER_GROUPS];
 #pragma unroll
-      for (int i = 0; i < MAX_RANKS; ++i) {  // no early exit: terms past nterms read nothing
-        const LTerm tm = terms(i);             // address arithmetic only
-        is_line[i] = i < nterms && tm.lines != nullptr;
-        const Rsrc rl = make_rsrc(is_line[i] ? tm.lines : a.lines, is_line[i] ? (uint32_t)(nlines * LL128_LINE) : 0u);
-        x[i] = cld16(rl, line * LL128_LINE + 16u * q);
+      for (int gi = 0; gi < GATHER_GROUPS; ++gi) {
+        const uint32_t line = (uint32_t)(l0 + (uint64_t)(u0 + gi) * 8 + grp);
+        const uint64_t off = (uint64_t)line * LL128_DATA + 16ull * q;
+        nb[gi] = (line < nlines && off < nbytes) ? (uint32_t)umin(lane_cap, nbytes - off) : 0u;
+#pragma unroll
+        for (int i = 0; i < MAX_RANKS; ++i) x[gi][i] = cld16(rl[i], line * LL128_LINE + 16u * q);
+        xp[gi] = make_uint4(0, 0, 0, 0);
+        if (pi >= 0 && nb[gi]) xp[gi] = ld_piece(terms(pi).plain + off, nb[gi], es);
       }
-      uint4 xp = make_uint4(0, 0, 0, 0);
-      if (pi >= 0 && nb) xp = ld_piece(terms(pi).plain + off, nb, es);
       // Nothing may use a loaded value before the last load is issued: the
       // scheduler would otherwise wait out each load before the next.
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < MAX_RANKS; ++i) {
-        const uint4 lv = q < 7 ? x[i] : make_uint4(x[i].x, x[i].y, 0, 0);
-        x[i] = !nb ? make_uint4(0, 0, 0, 0) : (is_line[i] ? lv : xp);
-      }
-      Vec<DT> acc = Vec<DT>::widen(x[0]);
+      for (int gi = 0; gi < GATHER_GROUPS; ++gi) {
+        const uint32_t line = (uint32_t)(l0 + (uint64_t)(u0 + gi) * 8 + grp);
+        const uint64_t off = (uint64_t)line * LL128_DATA + 16ull * q;
 #pragma unroll
-      for (int i = 1; i < MAX_RANKS; ++i)
-        if (i < nterms) acc.add(Vec<DT>::widen(x[i]));
-      const uint4 res = nterms > 1 ? acc.narrow() : x[0];
-      if (out_plain && nb) st_piece(out_plain + off, res, nb, es);
-      if (out_lines && line < nlines) {
-        const Rsrc rl = make_rsrc(out_lines, (uint32_t)(nlines * LL128_LINE));
-        cst16(rl, line * LL128_LINE + 16u * q, q < 7 ? res : make_uint4(res.x, res.y, 0, 0));
+        for (int i = 0; i < MAX_RANKS; ++i) {
+          const uint4 lv = q < 7 ? x[gi][i] : make_uint4(x[gi][i].x, x[gi][i].y, 0, 0);
+          x[gi][i] = !nb[gi] ? make_uint4(0, 0, 0, 0) : (is_line[i] ? lv : xp[gi]);
+        }
+        Vec<DT> acc = Vec<DT>::widen(x[gi][0]);
+#pragma unroll
+        for (int i = 1; i < MAX_RANKS; ++i)
+          if (i < nterms) acc.add(Vec<DT>::widen(x[gi][i]));
+        const uint4 res = nterms > 1 ? acc.narrow() : x[gi][0];
+        if (out_plain && nb[gi]) st_piece(out_plain + off, res, nb[gi], es);
+        if (out_lines && line < nlines)
+          cst16(rout, line * LL128_LINE + 16u * q, q < 7 ? res : make_uint4(res.x, res.y, 0, 0));
       }
     }
     if (out_lines) {
@@ -721,7 +744,7 @@ __device__ __forceinline__ void ll128_gather(const KArgs& a, Terms terms, int nt
 #pragma unroll
       for (int u = 0; u < U_LL128; ++u) {
         const uint32_t line = (uint32_t)(l0 + (uint64_t)u * 8 + grp);
-        if (q == 7 && line < nlines)
+        if (q == 7 && line < nlines && !withheld(a, step, rank))
           st_flag((uint64_t*)(out_lines + (uint64_t)line * LL128_LINE + LL128_DATA), flag);
       }
     }
@@ -1025,8 +1048,78 @@ constexpr bool never_waits() {
   return KIND == K_COPY || (PROTO == PROTO_SIMPLE && (KIND == K_ONESHOT || KIND == K_RS_DIRECT || KIND == K_AG_DIRECT));
 }
 
+// A workgroup leaves the call (thread 0): counts its finished tasks, and the
+// last workgroup out re-arms the counters and advances the call counter.
+// Relaxed is enough: every ticket fetch and the epoch load of this workgroup
+// have returned before this add is issued, and the next call's kernel starts
+// after this one's end-of-kernel cache write-back.
+__device__ __forceinline__ void finish_workgroup(const KArgs& a, uint32_t finished) {
+  __hip_atomic_fetch_add(&a.ctl->diag[5], (uint64_t)finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t d = __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (d == gridDim.x - 1) {  // last workgroup out: rearm for the next call
+    __hip_atomic_store(&a.ctl->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.ctl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&a.ctl->epoch, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.rearm_errors) {  // every other workgroup has exited: no wait can raise the abort again
+      __hip_atomic_store(&a.ctl->abort, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctl->err_code, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctl->err_key, 0xffffffffu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctl->diag[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Small one-shot calls over LL / LL128 (g.colocated): workgroup b is rank
+// b % N's program on tile b / N.  It puts its input tile on the wire, then
+// gathers every rank's lines of the tile and sums them: the send and the
+// receive of a (tile, rank) in one workgroup, with no ticket fetch between
+// them, so a decode-sized call is one round trip for the epoch and the
+// input, the line stores, and the polls of the peers' lines.  The N
+// workgroups of a tile wait on each other, so the grid (at most
+// COLOCATED_WORKGROUPS) must be resident at once; launch_collective runs the
+// ticketed schedule instead when the workgroup budget is smaller.
+template <int DT, int PROTO>
+__device__ __forceinline__ void colocated_oneshot(const KArgs& a) {
+  __shared__ uint64_t s_epoch;
+  __shared__ uint32_t s_abort;
+  if (threadIdx.x == 0) {  // both loads issued before either value is used: one round trip
+    const uint64_t e = __hip_atomic_load(&a.ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t ab = ld_u32(&a.ctl->abort);
+    s_epoch = e;
+    s_abort = ab;
+  }
+  __syncthreads();
+  const uint64_t epoch = uniform64(s_epoch);
+  const bool aborted = uniform(s_abort) != 0;
+  uint32_t finished = 0;
+  if (!aborted) {  // a latched error: run nothing
+    const int n = a.g.nranks;
+    Task k;
+    k.rank = (int32_t)(blockIdx.x % (uint32_t)n);
+    k.peer = 0; k.step = 0; k.block = 0; k.chain = 0;
+    k.tile = blockIdx.x / (uint32_t)n;
+    tile_range(a.g, a.g.total, k.tile, &k.lo, &k.hi);
+    if (k.hi > k.lo) {
+      k.phase = PH_SEND;
+      run_task<DT, PROTO, K_ONESHOT>(a, k, epoch);
+      __syncthreads();
+      k.phase = PH_RECV_FOLD;
+      run_task<DT, PROTO, K_ONESHOT>(a, k, epoch);
+      finished = 2;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) finish_workgroup(a, finished);
+}
+
 template <int DT, int PROTO, int KIND>
 __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
+  if constexpr (KIND == K_ONESHOT && PROTO != PROTO_SIMPLE) {
+    if (a.colocate) {
+      colocated_oneshot<DT, PROTO>(a);
+      return;
+    }
+  }
   if constexpr (never_waits<PROTO, KIND>()) {
     // When the grid covers every ticket at once, tasks that never wait need
     // neither the counter nor its re-arming: workgroup b runs its own
@@ -1048,10 +1141,14 @@ __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
   // A call that starts with the abort word set (an earlier call's latched
   // error) runs nothing.  An abort raised during the call is seen by the
   // waits, so the fetches below need not read it: the first fetch then goes
-  // out together with these two loads, one round trip for all three.
+  // out together with these two loads, one round trip for all three.  The
+  // loaded values reach LDS only after the fetch is issued: a store of the
+  // epoch to LDS right after its load made the compiler wait out each load
+  // in turn (three round trips before the first task).
   uint32_t aborted = 0;
+  uint64_t epoch0 = 0;
   if (threadIdx.x == 0) {
-    s_epoch = __hip_atomic_load(&a.ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    epoch0 = __hip_atomic_load(&a.ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     aborted = ld_u32(&a.ctl->abort);
   }
   const uint32_t ntasks = (uint32_t)a.g.ntasks;
@@ -1070,6 +1167,7 @@ __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
     // cannot be dispatched until one of them exits.
     if (threadIdx.x == 0) {
       const uint32_t t = __hip_atomic_fetch_add(&a.ctl->ticket, batch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_epoch = epoch0;
       s_ticket = aborted ? 0xffffffffu : t;
     }
     __syncthreads();
@@ -1095,24 +1193,7 @@ __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
     // end, every later fetch would come back empty.
     if (one_fetch || first >= ntasks || ntasks - first <= batch) more = false;
   }
-  if (threadIdx.x == 0) {
-    // Relaxed is enough: every ticket fetch and the epoch load of this
-    // workgroup have returned before this add is issued, and the next call's
-    // kernel starts after this one's end-of-kernel cache write-back.
-    __hip_atomic_fetch_add(&a.ctl->diag[5], (uint64_t)finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t d = __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d == gridDim.x - 1) {  // last workgroup out: rearm for the next call
-      __hip_atomic_store(&a.ctl->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(&a.ctl->epoch, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (a.rearm_errors) {  // every other workgroup has exited: no wait can raise the abort again
-        __hip_atomic_store(&a.ctl->abort, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.ctl->err_code, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.ctl->err_key, 0xffffffffu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.ctl->diag[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
+  if (threadIdx.x == 0) finish_workgroup(a, finished);
 }
 
 // Clears a latched error (one thread).
@@ -1194,14 +1275,28 @@ int resident_workgroups(KernelFn f, int device) {
     per_cu = 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) cus = 1;
   if (per_cu < 1) per_cu = 1;
-  if (per_cu > DEFAULT_WG_PER_CU) per_cu = DEFAULT_WG_PER_CU;
+  static const int wg_per_cu = [] {
+    const char* e = getenv("AR_WG_PER_CU");
+    const int v = e ? atoi(e) : DEFAULT_WG_PER_CU;
+    return v < 1 ? 1 : (v > 16 ? 16 : v);
+  }();
+  if (per_cu > wg_per_cu) per_cu = wg_per_cu;
   const int total = per_cu * cus;
   std::lock_guard<std::mutex> lock(mu);
   if (used < 256) seen[used++] = {f, device, total};
   return total;
 }
 
-hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uint32_t max_workgroups) {
+bool debug_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("AR_DEBUG");
+    return e && *e && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uint32_t max_workgroups,
+                             LaunchInfo* info) {
   KernelFn f = pick_kernel(a.g.dtype, a.g.proto, a.g.kind);
   if (!f) return hipErrorInvalidValue;
   uint64_t cap = (uint64_t)resident_workgroups(f, device);
@@ -1228,6 +1323,14 @@ hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uin
                           (a.g.proto == PROTO_SIMPLE && !barrier &&
                            (a.g.kind == K_ONESHOT || a.g.kind == K_RS_DIRECT || a.g.kind == K_AG_DIRECT));
   b.fixed = (waits_free && grid * b.batch >= a.g.ntasks) ? 1u : 0u;
+  // One workgroup per (tile, rank) of a small line-protocol one-shot, when
+  // the budget lets them all be resident; otherwise the ticketed schedule.
+  b.colocate = 0;
+  if (a.g.colocated && a.g.tiles * (uint64_t)a.g.nranks <= cap) {
+    b.colocate = 1;
+    b.batch = 1;
+    grid = a.g.tiles * (uint64_t)a.g.nranks;
+  }
   // One-shot out of place folds every term of a pass at once while its N
   // inputs are small; beyond that the same fold ran slower than one term at
   // a time.  Measured at N=8 (us, one term at a time -> fold): bf16 4 MiB per
@@ -1243,6 +1346,11 @@ hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uin
   b.fold = (a.g.kind == K_ONESHOT && !a.g.in_place &&
             (uint64_t)a.g.nranks * a.g.total * (uint64_t)a.g.esize <= fold_max) ? 1u : 0u;
   hipLaunchKernelGGL(f, dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, b);
+  if (info) {
+    info->grid = (uint32_t)grid;
+    info->batch = b.batch;
+    info->counter_free = b.fixed | b.colocate;
+  }
   return hipGetLastError();
 }
 

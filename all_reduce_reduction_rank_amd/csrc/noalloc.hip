@@ -26,11 +26,13 @@
 // eager call) race on the array: the caller must order them.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <mutex>
 
 #include "call.hpp"
+#include "calllog.hpp"
 
 using namespace ar;
 
@@ -123,5 +125,25 @@ extern "C" ar_status ar_allreduce_noalloc(int nranks, const void* const* send, v
   a.inj_rank = -1;
   a.inj_step = -1;
   a.rearm_errors = 1;
-  return launch_collective(a, dev, (hipStream_t)stream, 0) == hipSuccess ? AR_OK : AR_ERR_HIP;
+  LaunchInfo info;
+  if (launch_collective(a, dev, (hipStream_t)stream, 0, &info) != hipSuccess) return AR_ERR_HIP;
+  if (debug_enabled()) {
+    ar_call_record r = {};
+    r.op = OP_ALLREDUCE;
+    r.algo = g.algo;
+    r.proto = g.proto;
+    r.dtype = g.dtype;
+    r.nranks = g.nranks;
+    r.in_place = g.in_place;
+    r.grid = info.grid;
+    r.batch = info.batch;
+    r.counter_free = info.counter_free;
+    r.count = count;
+    r.ntasks = g.ntasks;
+    r.tile_bytes = g.tile * (uint64_t)g.esize;
+    char line[320];
+    format_record(line, sizeof(line), r);
+    fprintf(stderr, "[ar] noalloc %s\n", line);
+  }
+  return AR_OK;
 }

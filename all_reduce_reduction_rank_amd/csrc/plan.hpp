@@ -37,6 +37,11 @@ constexpr uint64_t FIXED_GRID_TASKS = 512;
 // reduce-scatter 256 MiB 8: 0.882, 16: 0.874.
 constexpr uint64_t RING_WINDOW_BYTES = 32ull << 20;
 constexpr uint64_t LL128_TILE_UNIT = 3840;  // 32 lines of 120 payload bytes: one wave pass
+// A one-shot call over LL or LL128 whose tiles fit this many workgroups (one
+// per tile and rank) runs each rank's send and receive of a tile in one
+// workgroup, with no ticket counter: the N workgroups of a tile wait on each
+// other, so the grid is kept small enough to be resident at once.
+constexpr uint64_t COLOCATED_WORKGROUPS = 64;
 constexpr uint64_t LL128_ALIGN = 240;       // 2 lines: a multiple of 16 bytes and of 120 bytes
 
 inline int esize_of(int dtype) { return dtype == DT_BF16 ? 2 : 4; }
@@ -113,6 +118,7 @@ inline bool select_schedule(int op, int nranks, int dtype, uint64_t rank_bytes, 
 // Tuning knobs (no effect on results): 0 keeps the built-in choice.
 struct Tuning {
   uint64_t tile_bytes = 0;  // Simple tile size
+  uint64_t line_tile_bytes = 0;  // LL / LL128 tile payload (LL128: rounded to whole wave passes)
   uint64_t ring_skew = 0;   // ring order: 0 windowed, k >= 1 skewed diagonal
   uint64_t ring_window = 0; // ring window (loops) for the windowed order
   bool ring_skew_set = false;
@@ -134,7 +140,14 @@ struct Tuning {
 //                 tile row, and with 16 KiB tiles at 8-32 MiB each fetch of
 //                 the ticket counter covers one small tile (N=8 8 MiB: 65 us
 //                 against 32 at 128 KiB; N=2 32 MiB: 65 against 29)
-// LL up to 16 KiB; LL128 whole wave passes.
+// LL up to 32 KiB; LL128 whole wave passes (3840 payload bytes each), up to
+// 8 (30 KiB), one-shot 16, direct reduce-scatter 4.  Measured at N=8, 256 MiB
+// fp32 (us, the earlier caps of 16 KiB and 4 passes -> these): LL128 two-shot
+// 2737 -> 2356, ring 2362 -> 2311, all-gather 1042 -> 913, one-shot 4628 ->
+// 4164 (4421 at 8 passes); LL two-shot 2767 -> 2569, ring 2995 -> 2883,
+// all-gather 1113 -> 1066, one-shot 5542 -> 5378.  The reduce-scatter ran
+// slower with larger tiles (LL128 1447 at 4 passes, 1549 at 8).  5 MiB bf16
+// (tokens 512): two-shot LL128 89 -> 88, one-shot LL128 108 -> 96.
 inline uint64_t simple_tile_cap(uint64_t rank_bytes, int kind, bool in_place) {
   uint64_t hi = 131072;
   if (kind == K_RING || kind == K_TREE) hi = 32768;
@@ -148,8 +161,9 @@ inline uint64_t simple_tile_cap(uint64_t rank_bytes, int kind, bool in_place) {
 inline uint64_t pick_tile_bytes(int proto, uint64_t rank_bytes, int kind, bool in_place) {
   const uint64_t want = floor_pow2(rank_bytes / 128 + 1);
   if (proto == PROTO_SIMPLE) return clampu(want, 4096, simple_tile_cap(rank_bytes, kind, in_place));
-  if (proto == PROTO_LL) return clampu(want, 4096, 16384);
-  return LL128_TILE_UNIT * clampu(floor_pow2(want / LL128_TILE_UNIT + 1), 1, 4);
+  if (proto == PROTO_LL) return clampu(want, 4096, 32768);
+  const uint64_t passes = kind == K_ONESHOT ? 16 : (kind == K_RS_DIRECT ? 4 : 8);
+  return LL128_TILE_UNIT * clampu(floor_pow2(want / LL128_TILE_UNIT + 1), 1, passes);
 }
 
 // Tickets a workgroup takes per fetch.  Every fetch is an atomic on one
@@ -217,6 +231,24 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
   uint64_t tile_b = pick_tile_bytes(proto, rank_bytes, g.kind, in_place != 0);
   if (tune.tile_bytes && !lines && !(g.kind == K_ONESHOT && in_place))
     tile_b = clampu(tune.tile_bytes / 16 * 16, 4096, 512 * 1024);
+  if (tune.line_tile_bytes && lines)
+    tile_b = proto == PROTO_LL128 ? LL128_TILE_UNIT * clampu(tune.line_tile_bytes / LL128_TILE_UNIT, 1, 64)
+                                  : clampu(tune.line_tile_bytes / 16 * 16, 1024, 256 * 1024);
+  // Small one-shot calls over the line protocols run one workgroup per
+  // (tile, rank) when they fit COLOCATED_WORKGROUPS workgroups; LL128 tiles
+  // grow to fit (up to 16 wave passes: the waves of a workgroup then share
+  // the tile's lines), LL tiles do not (an LL workgroup walks a larger tile
+  // in passes one after another).  Measured at N=8 bf16, us per call in a
+  // HIP graph (ticketed -> one workgroup per tile and rank): LL 10 KiB
+  // 9.83 -> 9.35; LL128 10 KiB 11.93 -> 10.96, 80 KiB 16.6 -> 12.4; LL
+  // 80 KiB with tiles grown to fit: 14.3 -> 20.9, so it stays ticketed.
+  bool colocated = false;
+  if (lines && g.kind == K_ONESHOT && !tune.line_tile_bytes && rank_bytes) {
+    const uint64_t max_tiles = COLOCATED_WORKGROUPS / n;
+    const uint64_t need = cdiv(cdiv(rank_bytes, max_tiles), LL128_TILE_UNIT) * LL128_TILE_UNIT;
+    if (cdiv(rank_bytes, tile_b) <= max_tiles) colocated = true;
+    else if (proto == PROTO_LL128 && need <= 16 * LL128_TILE_UNIT) { tile_b = need; colocated = true; }
+  }
   // Tasks that never wait (Simple one-shot out of place, direct RS and AG)
   // skip the ticket counter when one grid covers them all.  A call that
   // would just miss that grid takes tiles large enough to fit in it: above
@@ -323,6 +355,7 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
         g.per_group = 2 * n;
         g.groups = g.tiles ? g.tiles + lag : 0;
         g.nslots = n;
+        g.colocated = colocated && g.tiles * n <= COLOCATED_WORKGROUPS ? 1 : 0;
       }
       break;
     case K_TWOSHOT:

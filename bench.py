@@ -39,6 +39,10 @@ WORKLOADS = {
     # TP activations: N=8 bf16 [tokens, 5120]
     "tp-decode-t1": dict(op="allreduce", nranks=8, bytes=1 * 5120 * 2, dtype="bf16", dist="normal",
                          algo="oneshot", proto="ll", chunk=0),
+    "tp-decode-t8": dict(op="allreduce", nranks=8, bytes=8 * 5120 * 2, dtype="bf16", dist="normal",
+                         algo="oneshot", proto="ll", chunk=0),
+    "tp-decode-t64": dict(op="allreduce", nranks=8, bytes=64 * 5120 * 2, dtype="bf16", dist="normal",
+                          algo="oneshot", proto="ll128", chunk=0),
     "tp-prefill-t512": dict(op="allreduce", nranks=8, bytes=512 * 5120 * 2, dtype="bf16", dist="normal",
                             algo="twoshot", proto="ll128", chunk=0),
     # bf16 of the same size as the fp32 bucket (N=8 N(0,1), fp32 accumulate,
@@ -115,33 +119,114 @@ def traffic_from_profile(name):
 
 def cpu_threads():
     """Host threads the threaded oracle run uses: the cores this process may
-    run on, at most 16 (a GPU machine's CPU share)."""
+    run on, within the CPU share the environment grants (OMP_NUM_THREADS,
+    when set: a shared GPU host gives each GPU's jobs a share of its cores)."""
     try:
-        return max(1, min(16, len(os.sched_getaffinity(0))))
+        cores = max(1, len(os.sched_getaffinity(0)))
     except AttributeError:
-        return max(1, min(16, os.cpu_count() or 1))
+        cores = max(1, os.cpu_count() or 1)
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(cores, int(share))) if share.isdigit() and int(share) > 0 else cores
 
 
-def cpu_baseline_threaded(w, min_seconds, threads):
-    """T copies of the single-thread sample run side by side on T host
-    threads (NumPy releases the GIL in its loops), each on its own inputs:
-    the throughput the oracle reaches when every core runs it."""
+def host_ram_bytes():
+    try:
+        return os.sysconf("SC_PAGE_SIZE") * os.sysconf("SC_PHYS_PAGES")
+    except (ValueError, OSError, AttributeError):
+        return 0
+
+
+def split_parts(w, host, parts, blocks):
+    """`parts` disjoint reduced problems that together are the whole call:
+    part t holds the t-th piece of every block (all-reduce: the N blocks, the
+    tree's two halves; reduce-scatter: every rank's N slices; all-gather:
+    every rank's shard), so every element keeps its block and its summation
+    order.  None when the blocks are not all of one length (then the call is
+    not split).  Pieces are whole 16-byte vectors."""
+    import numpy as np
+
+    es = {"f32": 4, "bf16": 2, "i32": 4}[w["dtype"]]
+    vec = 16 // es
+    lens = {hi - lo for lo, hi in blocks}
+    if len(lens) != 1:
+        return None
+    blen = lens.pop()
+    piece = max(vec, -(-blen // parts // vec) * vec)
+    out = []
+    for a in range(0, blen, piece):
+        b = min(blen, a + piece)
+        if (b - a) % vec and w["op"] == "allreduce":
+            return None  # all-reduce blocks are whole vectors: a reduced problem must keep them so
+        idx = np.concatenate([np.arange(lo + a, lo + b) for lo, _ in blocks])
+        out.append([x[idx] for x in host])
+    return out
+
+
+def cpu_baseline_threaded(w, threads, runs=3):
+    """One oracle call split over `threads` host threads: each thread runs the
+    oracle as it stands on its own disjoint piece of every block (NumPy
+    releases the GIL in its loops), so together they compute the whole call
+    once.  The workload's full size when its inputs and outputs fit in a
+    quarter of host memory, else 256 MiB per rank.  Median of `runs`; the
+    split itself is done before the clock starts."""
     from concurrent.futures import ThreadPoolExecutor
 
-    def one(_):
-        return cpu_baseline(w, min_seconds, seed=1 + _)
+    from all_reduce_reduction_rank_amd import inputs
+    from oracle import collectives, fused, geometry
 
-    t0 = time.perf_counter()
+    es = {"f32": 4, "bf16": 2, "i32": 4}[w["dtype"]]
+    n = w["nranks"]
+    size = w["bytes"]
+    ram = host_ram_bytes()
+    if ram and 3 * n * size > ram // 4:
+        size = min(size, 256 << 20)
+    if w["op"] == "allreduce_rmsnorm":
+        rows, hidden = size // (w["hidden"] * es), w["hidden"]
+        host = inputs.rank_inputs(n, rows * hidden, w["dtype"], w["dist"], seed=1, cfg=9)
+        res = inputs.rank_inputs(n, rows * hidden, w["dtype"], w["dist"], seed=1001, cfg=9)
+        weight = inputs.rank_inputs(1, hidden, w["dtype"], w["dist"], seed=3, cfg=9)[0]
+        per = -(-rows // threads)
+        jobs = []
+        for r0 in range(0, rows, per):
+            r1 = min(rows, r0 + per)
+            sl = slice(r0 * hidden, r1 * hidden)
+            jobs.append(lambda sl=sl, k=r1 - r0: fused.allreduce_rmsnorm(
+                [x[sl] for x in host], [x[sl].copy() for x in res], weight, k, hidden, 1e-5, w["dtype"]))
+    else:
+        count = size // es
+        if w["op"] == "allreduce":
+            host = inputs.rank_inputs(n, count, w["dtype"], w["dist"], seed=1, cfg=9)
+            halves = w["algo"] == "tree"
+            blocks = geometry.ar_blocks(count, 2 if halves else n, w["dtype"])
+            fn = collectives.allreduce
+        elif w["op"] == "reduce_scatter":
+            rc = count // n
+            host = inputs.rank_inputs(n, n * rc, w["dtype"], w["dist"], seed=1, cfg=9)
+            blocks = [(j * rc, (j + 1) * rc) for j in range(n)]
+            fn = collectives.reduce_scatter
+        else:
+            sc = count // n
+            host = inputs.rank_inputs(n, sc, w["dtype"], w["dist"], seed=1, cfg=9)
+            blocks = [(0, sc)]
+            fn = collectives.allgather
+        parts = split_parts(w, host, threads, blocks) or [host]
+        chunk = w["chunk"] or collectives.DEFAULT_CHUNK_BYTES
+        jobs = [lambda p=p: fn(p, w["dtype"], w["algo"], chunk_bytes=chunk) for p in parts]
+    times = []
     with ThreadPoolExecutor(threads) as pool:
-        runs = list(pool.map(one, range(threads)))
-    el = time.perf_counter() - t0
-    total = sum(r["_bytes"] for r in runs)
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            list(pool.map(lambda job: job(), jobs))
+            times.append(time.perf_counter() - t0)
+    t = sorted(times)[len(times) // 2]
     return {
-        "value": round(total / el / 1e9, 4),
+        "value": round(size / t / 1e9, 4),
         "unit": "GB/s",
-        "cores": threads,
+        "cores": min(threads, len(jobs)),
         "kind": "oracle",
-        "sample": f"{threads} threads, each: " + runs[0]["sample"],
+        "sample": f"{w['op']} {w['algo']} N={n} {w['dtype']} {w['dist']}, {size / 2**20:.4g} MiB per rank, "
+                  f"one call split over {len(jobs)} disjoint piece(s) of every block on {min(threads, len(jobs))} "
+                  f"threads, median of {runs} runs ({', '.join(f'{x:.3f}' for x in times)} s)",
     }
 
 
@@ -347,12 +432,12 @@ def main():
         out["hbm_measured_frac"] = round(traffic / t / 1e9 / HBM_PEAK_GBPS, 4)
         out["hbm_measured_bytes_per_payload_byte"] = round(traffic / (n * s), 4)
     if args.cpu_seconds > 0:
-        # the oracle as it stands (one thread), then T copies side by side
+        # the oracle as it stands on one thread, then one call split over
+        # every usable core
         base = cpu_baseline(w, args.cpu_seconds / 2)
         base.pop("_bytes")
         out["cpu_baseline"] = base
-        threaded = cpu_baseline_threaded(w, args.cpu_seconds / 2, cpu_threads())
-        out["cpu_baseline_threads"] = threaded
+        out["cpu_baseline_threads"] = cpu_baseline_threaded(w, cpu_threads())
     comm.close()
     print(json.dumps(out))
 

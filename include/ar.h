@@ -40,10 +40,14 @@
  *     cannot wait (Simple one-shot out of place, direct reduce-scatter or
  *     all-gather, small enough that one grid covers all its tiles) still
  *     runs in full.  Once ar_comm_check has seen the error, every call
- *     returns AR_ERR_BROKEN until ar_comm_reset.  Nothing is printed.
+ *     returns AR_ERR_BROKEN until ar_comm_reset.  Nothing is printed unless
+ *     the environment variable AR_DEBUG is set (see ar_debug_calls).
  *   - Measurement overrides, read once per process from the environment;
  *     they change how work is cut and ordered, never a result:
- *     AR_TILE_KB (Simple tile), AR_BATCH (tickets per counter fetch, 1..16),
+ *     AR_TILE_KB (Simple tile), AR_LINE_TILE_KB (LL / LL128 tile payload;
+ *     LL128 rounds it down to whole 3840-byte wave passes), AR_BATCH (tickets
+ *     per counter fetch, 1..16), AR_WG_PER_CU (resident workgroups per CU a
+ *     call's grid may take, 1..16, at most what fits),
  *     AR_LAG (receiver groups behind their senders), AR_RING_WINDOW and
  *     AR_RING_SKEW (ring ticket order), AR_ONESHOT_FOLD_MIB (largest N*S of
  *     a one-shot that loads every term of a pass at once).
@@ -239,10 +243,17 @@ ar_status ar_plan_bytes(int nranks, ar_op op, size_t count, ar_dtype dtype, ar_a
                         uint64_t* hbm_read, uint64_t* hbm_write, uint64_t* link_bytes,
                         uint64_t* ntasks);
 
-/* Test hook: from the next call on, the rank program `rank` does not signal
- * after step `step` (Simple protocol schedules), and waits give up after
+/* Test hook: from the next call on, the rank program `rank` withholds what
+ * it sends at step `step` -- with Simple the signal after that step, with LL
+ * the lines it writes (payload and flag are one 8-byte store), with LL128
+ * the flag word of every line it writes -- and waits give up after
  * `timeout_us` microseconds (0 keeps the default of 5 s).  rank = -1 clears
- * the injection.  Used to exercise the timeout path from the host. */
+ * the injection.  Steps of the line protocols: ring -- step 0 puts a block on
+ * the wire, step s >= 1 receives what step s-1 wrote (the last step writes
+ * nothing); two-shot -- 0 a rank sends its slices, 1 an owner sums and
+ * publishes its block, 2 a rank receives the sums; one-shot, direct
+ * reduce-scatter and all-gather -- 0 sends, 1 receives.  Used to exercise
+ * the timeout path from the host. */
 ar_status ar_debug_inject(ar_comm_t comm, int rank, int step, uint64_t timeout_us);
 
 /* Test hook: synchronize `stream` and copy up to n (<= 10) words of the
@@ -282,6 +293,34 @@ ar_status ar_debug_state(ar_comm_t comm, ar_stream_t stream, uint64_t* out, int 
 ar_status ar_allreduce_noalloc(int nranks, const void* const* sendbufs, void* const* recvbufs,
                                size_t count, ar_dtype dtype, ar_algo algo, ar_proto proto,
                                size_t chunk_bytes, ar_stream_t stream);
+
+/* One entry of a communicator's call log (ar_debug_calls): the schedule a
+ * call launched, with AUTO choices resolved. */
+typedef struct {
+  uint64_t seq;          /* 1 for the communicator's first launched call, then 2, 3, ... */
+  int32_t op;            /* ar_op */
+  int32_t algo, proto;   /* ar_algo, ar_proto (never AUTO) */
+  int32_t dtype;         /* ar_dtype */
+  int32_t nranks, in_place;
+  uint32_t grid;         /* workgroups launched */
+  uint32_t batch;        /* tickets a workgroup takes per fetch */
+  uint32_t counter_free; /* 1: the call ran without the ticket counter */
+  uint32_t pad;
+  uint64_t count;        /* the call's count argument */
+  uint64_t ntasks;       /* tasks of the call's kernel */
+  uint64_t tile_bytes;   /* payload bytes per task tile */
+} ar_call_record;
+
+/* Test and debug hook ([H] "Common environment variables and debugging":
+ * the library reports the schedules it built, and a flight recorder keeps
+ * the recent collectives so that a hang can be traced to the call a rank
+ * missed).  The communicator logs the last 16 calls it launched; this copies
+ * the most recent min(max, 16) of them, oldest first, into out and sets
+ * *n_out to how many.  With the environment variable AR_DEBUG set, each call
+ * also prints its record to stderr when it launches, and ar_comm_check
+ * prints the timeout diagnostics and the log when it finds a latched error.
+ * Host only, no synchronization.  Errors: AR_ERR_INVALID. */
+ar_status ar_debug_calls(ar_comm_t comm, ar_call_record* out, int max, int* n_out);
 
 /* Static description of a status code. */
 const char* ar_status_string(ar_status status);

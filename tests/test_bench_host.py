@@ -50,3 +50,35 @@ def test_kernel_hash_ignores_comments_and_layout():
     changed = "int f(int x) {\n  return x + 2;\n}\n"
     assert profiling._code_only(code) == profiling._code_only(edited)
     assert profiling._code_only(code) != profiling._code_only(changed)
+
+
+def test_threaded_baseline_split_is_the_whole_call():
+    # The pieces the threaded baseline hands to its threads, put back in
+    # place, give exactly the oracle's result on the whole call.
+    import numpy as np
+
+    from all_reduce_reduction_rank_amd import inputs
+    from oracle import collectives, geometry
+
+    for algo in ("ring", "twoshot", "oneshot", "tree"):
+        w = dict(op="allreduce", nranks=4, bytes=4 * 4 * 8 * 25, dtype="f32", algo=algo, chunk=0)
+        count = w["bytes"] // 4
+        host = inputs.rank_inputs(4, count, "f32", "normal", seed=2, cfg=9)
+        blocks = geometry.ar_blocks(count, 2 if algo == "tree" else 4, "f32")
+        parts = bench.split_parts(w, host, 3, blocks)
+        assert parts is not None and len(parts) == 3
+        whole = collectives.allreduce(host, "f32", algo)
+        blen = blocks[0][1] - blocks[0][0]
+        piece = -(-blen // 3 // 4) * 4
+        for t, p in enumerate(parts):
+            got = collectives.allreduce(p, "f32", algo)
+            a, b = t * piece, min(blen, (t + 1) * piece)
+            idx = np.concatenate([np.arange(lo + a, lo + b) for lo, _ in blocks])
+            for r in range(4):
+                assert np.array_equal(got[r].view(np.uint32), whole[r][idx].view(np.uint32)), (algo, t, r)
+
+
+def test_threaded_baseline_runs_small():
+    w = dict(op="reduce_scatter", nranks=4, bytes=1 << 16, dtype="bf16", dist="normal", algo="ring", chunk=0)
+    rec = bench.cpu_baseline_threaded(w, 4, runs=1)
+    assert rec["kind"] == "oracle" and rec["cores"] == 4 and rec["value"] > 0

@@ -428,6 +428,155 @@ def test_withheld_signal_times_out_and_names_the_blocked_rank(algo, n, rank, ste
     c.close()
 
 
+@pytest.mark.parametrize("algo,proto,n,rank,step", [
+    ("oneshot", "ll", 4, 2, 0), ("oneshot", "ll128", 8, 0, 0),
+    ("twoshot", "ll", 4, 1, 0), ("twoshot", "ll128", 8, 3, 1),
+    ("ring", "ll", 4, 1, 2), ("ring", "ll128", 8, 5, 9), ("ring", "ll128", 3, 0, 0)])
+def test_withheld_line_flags_time_out_and_name_the_blocked_rank(algo, proto, n, rank, step):
+    # Forced from the host: one rank program writes its lines of one step
+    # without their flags (LL: does not write them) and waits are limited to
+    # 50 ms; every wave of the kernel still exits.  The blocked (rank, step)
+    # reported is the first one the oracle's transfer graph predicts.
+    from oracle import sim
+
+    c = Comm(n, 1 << 20, 1 << 20)
+    count = 64 * n  # one tile per block: nothing else is still running at the timeout
+    host = inputs.rank_inputs(n, count, "f32", "normal", seed=5)
+    send = [to_dev(x, "f32") for x in host]
+    recv = [empty(count, "f32") for _ in range(n)]
+    c.inject(rank, step, timeout_us=50_000)
+    _say("inject-lines", algo, proto, n, rank, step)
+    c.allreduce(send, recv, algo=algo, proto=proto)
+    status, r, s = c.check()
+    assert status == "AR_ERR_TIMEOUT"
+    _, first = sim.blocked("allreduce", algo, n, withheld=(rank, step), proto=proto)
+    assert (r, s) == first
+    with pytest.raises(ARError) as e:
+        c.allreduce(send, recv, algo=algo, proto=proto)
+    assert e.value.status == 7
+    c.inject(-1, -1)
+    c.reset()
+    run_ok = [empty(count, "f32") for _ in range(n)]
+    c.allreduce(send, run_ok, algo=algo, proto=proto)
+    torch.cuda.synchronize()
+    want = C.allreduce(host, "f32", algo)
+    for q in range(n):
+        assert_same(to_host(run_ok[q], "f32"), want[q], f"after reset rank {q}")
+    assert c.check()[0] == "AR_OK"
+    c.close()
+
+
+@pytest.mark.parametrize("op,proto", [("reduce_scatter", "ll128"), ("allgather", "ll")])
+def test_withheld_line_flags_direct_rs_ag(op, proto):
+    from oracle import sim
+
+    n, rank = 4, 2
+    c = Comm(n, 1 << 20, 1 << 20)
+    shard = 64
+    full = inputs.rank_inputs(n, n * shard, "f32", "normal", seed=6)
+    if op == "reduce_scatter":
+        send = [to_dev(x, "f32") for x in full]
+        recv = [empty(shard, "f32") for _ in range(n)]
+    else:
+        send = [to_dev(x[:shard], "f32") for x in full]
+        recv = [empty(n * shard, "f32") for _ in range(n)]
+    c.inject(rank, 0, timeout_us=50_000)
+    _say("inject-lines", op, proto, n, rank)
+    getattr(c, op)(send, recv, algo="oneshot", proto=proto)
+    status, r, s = c.check()
+    assert status == "AR_ERR_TIMEOUT"
+    assert (r, s) == sim.blocked(op, "twoshot", n, withheld=(rank, 0), proto=proto)[1]
+    c.inject(-1, -1)
+    c.reset()
+    getattr(c, op)(send, recv, algo="oneshot", proto=proto)
+    assert c.check()[0] == "AR_OK"
+    c.close()
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
+@pytest.mark.parametrize("n", [2, 5, 8])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "i32"])
+def test_small_line_one_shot_runs_one_workgroup_per_tile_and_rank(dt, n, proto):
+    # Decode-sized one-shot calls over LL / LL128 run each (tile, rank) as one
+    # workgroup with no ticket counter; the call log shows it, and the results
+    # equal the oracle's out of place and in place.  With a workgroup budget
+    # below the grid the same call takes the ticketed schedule.
+    c = Comm(n, 1 << 20, 1 << 20)
+    for count in (1, 999, 5120, 40960 if proto == "ll128" else 3000):
+        host = inputs.rank_inputs(n, count, dt, _dist(dt), seed=count, cfg=80)
+        want = C.allreduce(host, dt, "oneshot")
+        send = [to_dev(x, dt) for x in host]
+        recv = [empty(count, dt) for _ in range(n)]
+        _say("coloc", dt, n, proto, count)
+        c.allreduce(send, recv, algo="oneshot", proto=proto)
+        torch.cuda.synchronize()
+        assert c.debug_calls(1)[0]["counter_free"] == 1, (dt, n, proto, count)
+        for r in range(n):
+            assert_same(to_host(recv[r], dt), want[r], f"coloc {proto} {dt} N={n} count={count} rank {r}")
+        c.allreduce(send, None, algo="oneshot", proto=proto)  # in place
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_same(to_host(send[r], dt), want[r], f"coloc in place {proto} {dt} N={n} count={count} rank {r}")
+    c.set_max_workgroups(n - 1 if n > 2 else 1)
+    host = inputs.rank_inputs(n, 5120, dt, _dist(dt), seed=1, cfg=81)
+    send = [to_dev(x, dt) for x in host]
+    recv = [empty(5120, dt) for _ in range(n)]
+    c.allreduce(send, recv, algo="oneshot", proto=proto)
+    torch.cuda.synchronize()
+    assert c.debug_calls(1)[0]["counter_free"] == 0
+    want = C.allreduce(host, dt, "oneshot")
+    for r in range(n):
+        assert_same(to_host(recv[r], dt), want[r], f"budget {proto} {dt} N={n} rank {r}")
+    assert c.check()[0] == "AR_OK"
+    c.close()
+
+
+def test_call_log_after_three_calls():
+    n = 4
+    c = Comm(n, 1 << 20, 1 << 20)
+    host = inputs.rank_inputs(n, 4096, "f32", "normal", seed=7)
+    send = [to_dev(x, "f32") for x in host]
+    recv = [empty(4096, "f32") for _ in range(n)]
+    c.allreduce(send, recv, algo="ring", proto="simple")
+    c.reduce_scatter(send, [t[:1024] for t in recv], algo="oneshot", proto="ll128")
+    c.allreduce(send, recv, algo="auto", proto="auto")
+    torch.cuda.synchronize()
+    recs = c.debug_calls()
+    assert [r["seq"] for r in recs] == [1, 2, 3]
+    assert [(r["op"], r["algo"], r["proto"]) for r in recs[:2]] == [
+        ("allreduce", "ring", "simple"), ("reduce_scatter", "oneshot", "ll128")]
+    assert recs[2]["algo"] != "auto" and recs[2]["proto"] in ("simple", "ll", "ll128")
+    assert [r["count"] for r in recs] == [4096, 1024, 4096]
+    assert all(r["nranks"] == n and r["grid"] >= 1 and r["ntasks"] >= 1 for r in recs)
+    assert [r["seq"] for r in c.debug_calls(2)] == [2, 3]
+    assert c.check()[0] == "AR_OK"
+    c.close()
+
+
+def test_ar_debug_prints_each_plan_and_the_log_on_a_timeout():
+    import os
+    import subprocess
+    code = (
+        "import torch\n"
+        "from all_reduce_reduction_rank_amd import Comm\n"
+        "c = Comm(4, 1 << 20, 0)\n"
+        "x = [torch.ones(256, device='cuda') for _ in range(4)]\n"
+        "y = [torch.empty(256, device='cuda') for _ in range(4)]\n"
+        "c.allreduce(x, y, algo='twoshot')\n"
+        "c.inject(1, 2, timeout_us=50000)\n"
+        "c.allreduce(x, y, algo='ring')\n"
+        "print(c.check())\n")
+    env = dict(os.environ, AR_DEBUG="1")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, env=env)
+    assert res.returncode == 0, res.stderr
+    err = res.stderr
+    assert "[ar] call 1: allreduce twoshot/simple f32 N=4 count=256" in err
+    assert "[ar] call 2: allreduce ring/simple f32 N=4 count=256" in err
+    assert "[ar] latched error 6: first blocked wait rank 2 step 3" in err
+    assert "[ar]   call 1: allreduce twoshot" in err and "[ar]   call 2: allreduce ring" in err
+    assert "AR_ERR_TIMEOUT" in res.stdout
+
+
 # ------------------------------------------------------ automatic choice
 @pytest.mark.parametrize("n", [2, 3, 8])
 @pytest.mark.parametrize("dt", ["f32", "bf16", "i32"])

@@ -303,3 +303,48 @@ def test_tree_bytes(n):
     assert sum(t.link) == 2 * (n - 1) * s
     with pytest.raises(ValueError):
         traffic.tally("allreduce", "tree", "ll", n, count, "f32")
+
+
+# ------------------------------------------- signals of the line protocols
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+def test_line_ring_withheld_flags_block_the_rest_of_one_chain(n, proto):
+    # 2N-1 steps per block (a first send, N-1 reduce receives, N-1 copy
+    # receives); withholding the flags of step s blocks steps s+1 .. 2N-2 of
+    # that block only, the first of them on the next rank around the ring.
+    steps = 2 * n - 1
+    for r in range(n):
+        for s in range(steps - 1):
+            stuck, first = sim.blocked("allreduce", "ring", n, withheld=(r, s), proto=proto)
+            assert first == ((r + 1) % n, s + 1)
+            assert len(stuck) == steps - 1 - s
+        # the last step writes no lines: nothing waits on it
+        assert sim.blocked("allreduce", "ring", n, withheld=(r, steps - 1), proto=proto)[0] == []
+    for op in ("reduce_scatter", "allgather"):  # N steps per block
+        stuck, first = sim.blocked(op, "ring", n, withheld=(0, 0), proto=proto)
+        assert first == (1, 1) and len(stuck) == n - 1
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
+def test_line_two_shot_withheld_flags(proto):
+    n = 4
+    # a sender that withholds its slices blocks every other owner's sum, then
+    # every rank's receive of those sums
+    stuck, first = sim.blocked("allreduce", "twoshot", n, withheld=(1, 0), proto=proto)
+    assert first == (0, 1)
+    assert stuck == [(0, 1), (2, 1), (3, 1), (0, 2), (1, 2), (2, 2), (3, 2)]
+    # an owner that withholds its published sum blocks every other rank's step 2
+    stuck, first = sim.blocked("allreduce", "twoshot", n, withheld=(2, 1), proto=proto)
+    assert stuck == [(0, 2), (1, 2), (3, 2)] and first == (0, 2)
+
+
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
+def test_line_one_shot_and_direct_withheld_flags(proto):
+    n = 8
+    stuck, first = sim.blocked("allreduce", "oneshot", n, withheld=(0, 0), proto=proto)
+    assert stuck == [(r, 1) for r in range(1, n)] and first == (1, 1)
+    stuck, _ = sim.blocked("allreduce", "oneshot", n, withheld=(0, 0), in_place=True, proto=proto)
+    assert stuck == [(r, 1) for r in range(n)]  # in place the rank reads its own lines too
+    for op in ("reduce_scatter", "allgather"):
+        stuck, first = sim.blocked(op, "twoshot", n, withheld=(5, 0), proto=proto)
+        assert stuck == [(r, 1) for r in range(n) if r != 5] and first == (0, 1)
