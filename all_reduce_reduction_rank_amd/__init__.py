@@ -4,4 +4,4 @@ Simple, LL and LL128 transports.  The work runs in hand-written HIP kernels
 (libar.so, C ABI in include/ar.h); ``binding`` marshals arguments to it."""
 
 from .binding import (ALGOS, DTYPES, OPS, PROTOS, ARError, Comm, allreduce_noalloc, library,  # noqa: F401
-                      plan_bytes, select)
+                      plan_bytes, select, stream_ceiling)

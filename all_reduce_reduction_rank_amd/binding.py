@@ -40,7 +40,7 @@ SYMBOLS = (
     "ar_comm_create", "ar_comm_destroy", "ar_comm_check", "ar_comm_reset",
     "ar_comm_workspace_bytes", "ar_comm_set_max_workgroups", "ar_allreduce", "ar_allreduce_rmsnorm", "ar_reduce_scatter", "ar_allgather",
     "ar_plan_bytes", "ar_select", "ar_debug_inject", "ar_debug_state", "ar_status_string",
-    "ar_allreduce_noalloc", "ar_debug_calls",
+    "ar_allreduce_noalloc", "ar_debug_calls", "ar_stream_ceiling",
 )
 
 
@@ -77,6 +77,7 @@ def _declare(lib):
         getattr(lib, name).argtypes = [P, PP, PP, S, I, I, I, S, P]
     lib.ar_allreduce_noalloc.argtypes = [I, PP, PP, S, I, I, I, S, P]
     lib.ar_debug_calls.argtypes = [P, ctypes.POINTER(CallRecord), I, ctypes.POINTER(I)]
+    lib.ar_stream_ceiling.argtypes = [I, PP, I, PP, S, P, I, I, I, P]
     lib.ar_plan_bytes.argtypes = [I, I, S, I, I, I, S, I, ctypes.POINTER(U64), ctypes.POINTER(U64),
                                   ctypes.POINTER(U64), ctypes.POINTER(U64)]
     lib.ar_select.argtypes = [I, I, S, I, I, I, S, ctypes.POINTER(I), ctypes.POINTER(I),
@@ -301,6 +302,23 @@ def allreduce_noalloc(send, recv=None, algo="ring", proto="simple", chunk_bytes=
     _check(_lib().ar_allreduce_noalloc(n, s, r, count, DTYPES[dt], _algo(algo), _proto(proto), chunk_bytes,
                                        _stream_handle(stream)), "ar_allreduce_noalloc")
     return recv
+
+
+def stream_ceiling(src, dst, sink=None, nt_loads=False, nt_stores=False, unroll=8, wg_per_cu=0, stream=None):
+    """ar_stream_ceiling: one streaming pass reading every tensor of `src`
+    and writing every tensor of `dst` (all contiguous device tensors of the
+    same byte size; a measurement aid), plain or non-temporal."""
+    tensors = list(src) + list(dst)
+    nbytes = tensors[0].numel() * tensors[0].element_size()
+    for t in tensors:
+        if not t.is_cuda or not t.is_contiguous() or t.numel() * t.element_size() != nbytes:
+            raise ValueError("streams must be contiguous device tensors of one byte size")
+    s = (ctypes.c_void_p * max(1, len(src)))(*[t.data_ptr() for t in src])
+    d = (ctypes.c_void_p * max(1, len(dst)))(*[t.data_ptr() for t in dst])
+    _check(_lib().ar_stream_ceiling(len(src), s, len(dst), d, nbytes,
+                                    ctypes.c_void_p(sink.data_ptr() if sink is not None else 0),
+                                    int(nt_loads) | 2 * int(nt_stores), unroll, wg_per_cu, _stream_handle(stream)),
+           "ar_stream_ceiling")
 
 
 def select(nranks, op, count, dtype, algo="auto", proto="auto", max_line_bytes_per_rank=0):

@@ -13,7 +13,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libar.so")
-SOURCES = ("api.hip", "kernels.hip", "rmsnorm.hip", "noalloc.hip")
+SOURCES = ("api.hip", "kernels.hip", "rmsnorm.hip", "noalloc.hip", "ceiling.hip")
 
 # -packed-fp32-ops: keep hipcc from fusing float adds into packed-FP32
 # instructions.  No fast-math, no denormal flushing: fp32 adds stay IEEE.

@@ -68,11 +68,100 @@ WORKLOADS = {
     # write S); its counter readings scale the others' to bytes
     "copy-256MiB": dict(op="allreduce", nranks=1, bytes=256 << 20, dtype="f32", dist="normal",
                         algo="ring", proto="simple", chunk=0),
+    # streaming ceilings (ar_stream_ceiling): `reads` source and `writes`
+    # destination streams of `bytes` each, far larger than the 256 MB MALL
+    "ceiling-read": dict(op="ceiling", reads=1, writes=0, bytes=2 << 30),
+    "ceiling-write": dict(op="ceiling", reads=0, writes=1, bytes=2 << 30),
+    "ceiling-copy": dict(op="ceiling", reads=1, writes=1, bytes=1 << 30),
+    "ceiling-add8": dict(op="ceiling", reads=8, writes=1, bytes=512 << 20),
+    "ceiling-read3-write2": dict(op="ceiling", reads=3, writes=2, bytes=512 << 20),
 }
+CEILING_STREAM_BYTES = 512 << 20  # per stream of the ceiling run beside a collective: twice the MALL
 MALL_BYTES = 256 << 20
 DEFAULT_WORKLOAD = "grad-bucket-256MiB"
 
 from all_reduce_reduction_rank_amd.profiling import kernel_hash  # noqa: E402
+
+
+def mix_streams(read_bytes, write_bytes):
+    """(reads, writes) streams of a ceiling run whose read:write ratio is the
+    closest one to a schedule's (at most 8 reads and 2 writes)."""
+    if write_bytes == 0:
+        return 1, 0
+    ratio = read_bytes / write_bytes
+    best = None
+    for wr in (1, 2):
+        for rd in range(0, 9):
+            err = abs(rd / wr - ratio)
+            if best is None or err < best[0] - 1e-12:
+                best = (err, rd, wr)
+    return best[1], best[2]
+
+
+def run_ceiling(reads, writes, nbytes, steps, warmup):
+    """Time ar_stream_ceiling over `reads` + `writes` streams of `nbytes` in
+    every configuration it offers -- plain or non-temporal loads and stores,
+    4, 8 or 16 vectors per thread in flight, 1, 2, 4 or every workgroup per
+    CU -- and keep the fastest: (microseconds per call, GB/s over every
+    stream's bytes, the configuration)."""
+    import torch
+
+    from all_reduce_reduction_rank_amd import stream_ceiling
+
+    src = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i + 1) for i in range(reads)]
+    dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(writes)]
+    sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = None
+    for nt_l in ((False, True) if reads else (False,)):
+        for nt_s in ((False, True) if writes else (False,)):
+            for unroll in (4, 8, 16):
+                for per_cu in (1, 2, 4, 0):
+                    def once():
+                        stream_ceiling(src, dst, sink, nt_l, nt_s, unroll, per_cu, stream=stream)
+                    for _ in range(warmup):
+                        once()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    torch.cuda.synchronize()
+                    e0.record(stream)
+                    for _ in range(steps):
+                        once()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    us = e0.elapsed_time(e1) * 1e3 / steps
+                    conf = (f"{'nt' if nt_l else 'plain'} loads, {'nt' if nt_s else 'plain'} stores, "
+                            f"{unroll} in flight, {per_cu or 'all'} per CU")
+                    if best is None or us < best[0]:
+                        best = (us, conf)
+    del src, dst
+    torch.cuda.empty_cache()
+    return best[0], (reads + writes) * nbytes / (best[0] * 1e-6) / 1e9, best[1]
+
+
+def ceiling_main(args, w):
+    """One JSON line for a streaming-ceiling workload."""
+    us, gbps, hints = run_ceiling(w["reads"], w["writes"], w["bytes"], args.steps, args.warmup)
+    out = {
+        "metric": "all-reduce algbw/busbw GB/s and % of HBM peak vs message size, N=8",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic (constant bytes)",
+        "config": {"workload": args.workload, "reads": w["reads"], "writes": w["writes"],
+                   "bytes_per_stream": w["bytes"], "best_of": hints,
+                   "note": "streaming-ceiling measurement aid, not a collective"},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "kernel_hash": kernel_hash(),
+    }
+    print(json.dumps(out))
 
 
 def busbw_factor(op, n):
@@ -286,6 +375,8 @@ def main():
     ap.add_argument("--algo", choices=("oneshot", "twoshot", "ring", "tree", "auto"))
     ap.add_argument("--proto", choices=("simple", "ll", "ll128", "auto"))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample length; 0 skips it")
+    ap.add_argument("--no-ceiling", dest="ceiling", action="store_false",
+                    help="skip the streaming-ceiling run beside the collective")
     ap.add_argument("--max-workgroups", type=int, default=0,
                     help="workgroup budget of the collective's kernel (0: the default, up to 3 per CU)")
     args = ap.parse_args()
@@ -300,6 +391,10 @@ def main():
     from all_reduce_reduction_rank_amd import Comm, inputs, plan_bytes, select
 
     w = dict(WORKLOADS[args.workload])
+    if w["op"] == "ceiling":
+        torch.cuda.set_device(0)
+        ceiling_main(args, w)
+        return
     if args.algo:
         w["algo"] = args.algo
     if args.proto:
@@ -382,7 +477,7 @@ def main():
     s = w["bytes"]
     t = ms / 1e3
     if op == "allreduce_rmsnorm":
-        plan = {"hbm": fused_hbm_bytes(w)}
+        plan = {"hbm": fused_hbm_bytes(w), "read": n * (n + 2) * w["bytes"], "write": 2 * n * w["bytes"]}
     else:
         plan = plan_bytes(n, op, count, dt, w["algo"], w["proto"], chunk_bytes=w["chunk"])
     algbw = s / t / 1e9
@@ -426,7 +521,22 @@ def main():
             "traffic": traffic,
         },
         "kernel_hash": kernel_hash(),
+        # what the counters behind `traffic` count: requests from the XCDs' L2
+        # caches to the data fabric; the 256 MB MALL sits behind them, so a
+        # hit there counts like an HBM access (no memory-side counter is
+        # exposed on gfx950)
+        "traffic_level": "L2-to-fabric requests (TCC_EA), MALL hits included",
     }
+    if args.ceiling:
+        # the practical ceiling for this schedule's mix of reads and writes:
+        # a pure streaming kernel with the closest read:write ratio, on
+        # streams of twice the MALL, timed in the same run
+        rd, wrs = mix_streams(plan["read"], plan["write"])
+        c_us, c_gbps, c_hints = run_ceiling(rd, wrs, CEILING_STREAM_BYTES, 5, 1)
+        out["ceiling"] = {"reads": rd, "writes": wrs, "bytes_per_stream": CEILING_STREAM_BYTES, "best_of": c_hints,
+                          "schedule_read_write_ratio": round(plan["read"] / max(1, plan["write"]), 3),
+                          "GBps": round(c_gbps, 1), "frac_of_peak": round(c_gbps / HBM_PEAK_GBPS, 4)}
+        out["ceiling_frac"] = round(achieved / c_gbps, 4)
     if traffic:
         out["hbm_measured_GBps"] = round(traffic / t / 1e9, 1)
         out["hbm_measured_frac"] = round(traffic / t / 1e9 / HBM_PEAK_GBPS, 4)

@@ -322,6 +322,25 @@ typedef struct {
  * Host only, no synchronization.  Errors: AR_ERR_INVALID. */
 ar_status ar_debug_calls(ar_comm_t comm, ar_call_record* out, int max, int* n_out);
 
+/* Measurement aid, not a collective: a streaming kernel that reads `nread`
+ * (0..8) source buffers and writes `nwrite` (0..2) destination buffers of
+ * `bytes` each (a multiple of 16, at most 2 GiB), 16-byte vectors; `flags`
+ * bit 0 makes the loads and bit 1 the stores non-temporal (plain
+ * otherwise); `unroll` (4, 8 or 16) vectors per thread per source in flight
+ * (with more than two sources, about 2*unroll loads per thread in all);
+ * `wg_per_cu` caps the workgroups per CU (0: every one that fits).
+ * Timed on buffers larger than the 256 MB MALL it gives the practical HBM
+ * bandwidth of this GPU for that mix of reads and writes, the ceiling that a
+ * collective with the same mix can be held against ([H] "Reading
+ * nccl-tests": bus bandwidth is compared with the hardware's own).  Each
+ * destination receives the exclusive or of the sources (with no source,
+ * values made from the vector index).  `sink`: a device word written only to
+ * keep the loads of a read-only run (nwrite 0) alive; NULL otherwise allowed.
+ * Errors: AR_ERR_INVALID (counts, alignment, null pointers, flags, unroll),
+ * AR_ERR_HIP. */
+ar_status ar_stream_ceiling(int nread, const void* const* src, int nwrite, void* const* dst, size_t bytes,
+                            void* sink, int flags, int unroll, int wg_per_cu, ar_stream_t stream);
+
 /* Static description of a status code. */
 const char* ar_status_string(ar_status status);
 

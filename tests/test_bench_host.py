@@ -21,6 +21,10 @@ def test_counts_per_operation():
 
 def test_every_workload_is_well_formed():
     for name, w in bench.WORKLOADS.items():
+        if w["op"] == "ceiling":
+            assert 0 <= w["reads"] <= 8 and 0 <= w["writes"] <= 2 and w["reads"] + w["writes"] > 0, name
+            assert w["bytes"] % 16 == 0 and w["bytes"] >= 2 * bench.MALL_BYTES, name
+            continue
         count, n_in, n_out = bench.counts(w)
         assert count > 0 and n_in > 0 and n_out > 0, name
         if w["op"] == "allreduce_rmsnorm":
@@ -82,3 +86,12 @@ def test_threaded_baseline_runs_small():
     w = dict(op="reduce_scatter", nranks=4, bytes=1 << 16, dtype="bf16", dist="normal", algo="ring", chunk=0)
     rec = bench.cpu_baseline_threaded(w, 4, runs=1)
     assert rec["kind"] == "oracle" and rec["cores"] == 4 and rec["value"] > 0
+
+
+def test_mix_streams_matches_schedule_ratios():
+    assert bench.mix_streams(21, 14) == (3, 2)      # ring: 21 S read, 14 S written
+    assert bench.mix_streams(8, 1) == (8, 1)        # direct reduce-scatter
+    assert bench.mix_streams(1, 1) == (1, 1)
+    assert bench.mix_streams(5, 0) == (1, 0)        # nothing written: a read stream
+    r, w = bench.mix_streams(15, 8)                 # two-shot: 15 S read, 8 S written
+    assert abs(r / w - 15 / 8) <= 0.125
