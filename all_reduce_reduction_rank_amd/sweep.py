@@ -153,15 +153,18 @@ def summary(recs, table_ranks=None):
         cols = [c for c in combos(op) if any((r["algo"], r["proto"]) == c for r in rows)]
         lines.append(f"\n### {op}, N={n}, {dt} (µs per call)\n")
         if table_ranks is None or n in table_ranks:
-            lines.append("| bytes/rank | " + " | ".join(f"{a}/{p}" for a, p in cols) + " | fastest |")
-            lines.append("|---:|" + "---:|" * len(cols) + "---|")
+            lines.append("(MALL: yes when the call's inputs and outputs, 2 N S, fit in twice the 256 MB "
+                         "last-level cache, so repeated calls run largely from it; those rows are not HBM-bound.)\n")
+            lines.append("| bytes/rank | MALL | " + " | ".join(f"{a}/{p}" for a, p in cols) + " | fastest |")
+            lines.append("|---:|---|" + "---:|" * len(cols) + "---|")
         for s in sizes:
             if table_ranks is not None and n not in table_ranks:
                 break
             t = {(r["algo"], r["proto"]): best_time(r) for r in rows if r["bytes"] == s}
+            resident = any(r.get("cache_resident") for r in rows if r["bytes"] == s)
             fast = min(t, key=t.get)
             cells = [f"{t[c]:.1f}" if c in t else "" for c in cols]
-            lines.append(f"| {s} | " + " | ".join(cells) + f" | {fast[0]}/{fast[1]} |")
+            lines.append(f"| {s} | {'yes' if resident else 'no'} | " + " | ".join(cells) + f" | {fast[0]}/{fast[1]} |")
         lines.append("")
         t_all = {}
         for r in rows:

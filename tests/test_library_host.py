@@ -134,3 +134,18 @@ def test_noalloc_device_array_holds_every_schedule_up_to_one_gib():
                 for recv in (outs, ptrs):  # out of place, in place
                     st = lib.ar_allreduce_noalloc(n, ptrs, recv, count, dt, algo, 0, 0, None)
                     assert st == 5, (n, algo, dt, recv is ptrs, st)
+
+
+def test_stream_ceiling_argument_errors_need_no_device():
+    import ctypes
+    lib = binding.library()
+    P = ctypes.c_void_p
+    bufs = (P * 8)(*[0x100000 * (i + 1) for i in range(8)])
+    outs = (P * 2)(*[0x10000000 * (i + 1) for i in range(2)])
+    st = lambda r, w, nbytes, flags=0, unroll=8, per_cu=0, sink=None: lib.ar_stream_ceiling(  # noqa: E731
+        r, bufs, w, outs, nbytes, sink, flags, unroll, per_cu, None)
+    assert st(9, 1, 4096) == 1 and st(1, 3, 4096) == 1 and st(0, 0, 4096) == 1   # stream counts
+    assert st(1, 1, 4100) == 1 and st(1, 1, (2 << 30) + 16) == 1                  # size
+    assert st(1, 1, 4096, flags=4) == 1 and st(1, 1, 4096, unroll=5) == 1        # flags, unroll
+    assert st(1, 1, 4096, per_cu=-1) == 1
+    assert st(1, 0, 4096) == 1                                                    # read-only needs a sink

