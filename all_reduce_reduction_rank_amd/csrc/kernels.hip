@@ -34,10 +34,6 @@ constexpr int U_SIMPLE = 4;  // 16-byte vectors in flight per thread per source
 constexpr int U_LL = 4;      // LL words per thread per pass
 constexpr int U_LL128 = 4;   // LL128 line groups (8 lines of a wave) per pass of the N-term gather
 constexpr int U_LL128_PASS = 4;  // ... and per pass of a one- or two-term pass (ring, send, copy)
-// Line groups of the N-term gather whose payload loads go out together.
-// Measured at N=8, 256 MiB fp32: two-shot LL128 2742 us with 1 and 2821 with
-// 2; one-shot LL128 4624 and 4459; 30 KiB tiles keep that split.
-constexpr int GATHER_GROUPS = 1;
 
 // =============================================================== Simple path
 // dst = fold(term(0), ..., term(n-1)) over `nbytes` (whole elements, at most
@@ -639,18 +635,6 @@ __device__ __forceinline__ void ll128_gather(const KArgs& a, Terms terms, int nt
   constexpr int FLAG_LOADS = (MAX_RANKS * 32 + 63) / 64;
   const int pi = plain_term(terms, nterms);
   const int li = line_term(terms, nterms);
-  // One buffer resource per term slot: a line term's staging, or an empty
-  // resource (reads give zeros, nothing is fetched) for the plain term and
-  // for slots past nterms.
-  Rsrc rl[MAX_RANKS];
-  bool is_line[MAX_RANKS];
-#pragma unroll
-  for (int i = 0; i < MAX_RANKS; ++i) {  // no early exit: terms past nterms read nothing
-    const LTerm tm = terms(i);             // address arithmetic only
-    is_line[i] = i < nterms && tm.lines != nullptr;
-    rl[i] = make_rsrc(is_line[i] ? tm.lines : a.lines, is_line[i] ? (uint32_t)(nlines * LL128_LINE) : 0u);
-  }
-  const Rsrc rout = make_rsrc(out_lines ? out_lines : a.lines, out_lines ? (uint32_t)(nlines * LL128_LINE) : 0u);
   for (uint64_t l0 = (uint64_t)wave * U_LL128 * 8; l0 < nlines; l0 += 4ull * U_LL128 * 8) {
     {
       // Terms 2k and 2k+1 are evaluated for the wave (uniform), each lane
@@ -698,45 +682,44 @@ __device__ __forceinline__ void ll128_gather(const KArgs& a, Terms terms, int nt
       }
     }
     // Every lane of the wave is past its polls: all flags of the pass are
-    // seen.  Payload: every term's piece of GATHER_GROUPS line groups in one
-    // round trip (a lane past the tile's last line reads outside the buffer
-    // resource and gets zeros; a term past nterms reads through an empty
-    // one), then the sums in term order.
+    // seen.  Per line group, every term's piece in one round trip.
 #pragma unroll
-    for (int u0 = 0; u0 < U_LL128; u0 += GATHER_GROUPS) {
-      uint4 x[GATHER_GROUPS][MAX_RANKS];
-      uint4 xp[GATHER_GROUPS];
-      uint32_t nb[GATHER_GROUPS];
+    for (int u = 0; u < U_LL128; ++u) {
+      const uint32_t line = (uint32_t)(l0 + (uint64_t)u * 8 + grp);
+      const uint64_t off = (uint64_t)line * LL128_DATA + 16ull * q;
+      const uint32_t nb = (line < nlines && off < nbytes) ? (uint32_t)umin(lane_cap, nbytes - off) : 0u;
+      // Every line term's piece with no branch between the loads, then the
+      // plain term's piece, so they all go out before the first wait (a lane
+      // past the tile's last line reads outside the buffer resource and gets
+      // zeros; the plain term's slot reads through an empty one).
+      uint4 x[MAX_RANKS];
+      bool is_line[MAX_RANKS];
 #pragma unroll
-      for (int gi = 0; gi < GATHER_GROUPS; ++gi) {
-        const uint32_t line = (uint32_t)(l0 + (uint64_t)(u0 + gi) * 8 + grp);
-        const uint64_t off = (uint64_t)line * LL128_DATA + 16ull * q;
-        nb[gi] = (line < nlines && off < nbytes) ? (uint32_t)umin(lane_cap, nbytes - off) : 0u;
-#pragma unroll
-        for (int i = 0; i < MAX_RANKS; ++i) x[gi][i] = cld16(rl[i], line * LL128_LINE + 16u * q);
-        xp[gi] = make_uint4(0, 0, 0, 0);
-        if (pi >= 0 && nb[gi]) xp[gi] = ld_piece(terms(pi).plain + off, nb[gi], es);
+      for (int i = 0; i < MAX_RANKS; ++i) {  // no early exit: terms past nterms read nothing
+        const LTerm tm = terms(i);             // address arithmetic only
+        is_line[i] = i < nterms && tm.lines != nullptr;
+        const Rsrc rl = make_rsrc(is_line[i] ? tm.lines : a.lines, is_line[i] ? (uint32_t)(nlines * LL128_LINE) : 0u);
+        x[i] = cld16(rl, line * LL128_LINE + 16u * q);
       }
+      uint4 xp = make_uint4(0, 0, 0, 0);
+      if (pi >= 0 && nb) xp = ld_piece(terms(pi).plain + off, nb, es);
       // Nothing may use a loaded value before the last load is issued: the
       // scheduler would otherwise wait out each load before the next.
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int gi = 0; gi < GATHER_GROUPS; ++gi) {
-        const uint32_t line = (uint32_t)(l0 + (uint64_t)(u0 + gi) * 8 + grp);
-        const uint64_t off = (uint64_t)line * LL128_DATA + 16ull * q;
+      for (int i = 0; i < MAX_RANKS; ++i) {
+        const uint4 lv = q < 7 ? x[i] : make_uint4(x[i].x, x[i].y, 0, 0);
+        x[i] = !nb ? make_uint4(0, 0, 0, 0) : (is_line[i] ? lv : xp);
+      }
+      Vec<DT> acc = Vec<DT>::widen(x[0]);
 #pragma unroll
-        for (int i = 0; i < MAX_RANKS; ++i) {
-          const uint4 lv = q < 7 ? x[gi][i] : make_uint4(x[gi][i].x, x[gi][i].y, 0, 0);
-          x[gi][i] = !nb[gi] ? make_uint4(0, 0, 0, 0) : (is_line[i] ? lv : xp[gi]);
-        }
-        Vec<DT> acc = Vec<DT>::widen(x[gi][0]);
-#pragma unroll
-        for (int i = 1; i < MAX_RANKS; ++i)
-          if (i < nterms) acc.add(Vec<DT>::widen(x[gi][i]));
-        const uint4 res = nterms > 1 ? acc.narrow() : x[gi][0];
-        if (out_plain && nb[gi]) st_piece(out_plain + off, res, nb[gi], es);
-        if (out_lines && line < nlines)
-          cst16(rout, line * LL128_LINE + 16u * q, q < 7 ? res : make_uint4(res.x, res.y, 0, 0));
+      for (int i = 1; i < MAX_RANKS; ++i)
+        if (i < nterms) acc.add(Vec<DT>::widen(x[i]));
+      const uint4 res = nterms > 1 ? acc.narrow() : x[0];
+      if (out_plain && nb) st_piece(out_plain + off, res, nb, es);
+      if (out_lines && line < nlines) {
+        const Rsrc rl = make_rsrc(out_lines, (uint32_t)(nlines * LL128_LINE));
+        cst16(rl, line * LL128_LINE + 16u * q, q < 7 ? res : make_uint4(res.x, res.y, 0, 0));
       }
     }
     if (out_lines) {

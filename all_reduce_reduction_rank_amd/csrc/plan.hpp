@@ -147,7 +147,10 @@ struct Tuning {
 // 4164 (4421 at 8 passes); LL two-shot 2767 -> 2569, ring 2995 -> 2883,
 // all-gather 1113 -> 1066, one-shot 5542 -> 5378.  The reduce-scatter ran
 // slower with larger tiles (LL128 1447 at 4 passes, 1549 at 8).  5 MiB bf16
-// (tokens 512): two-shot LL128 89 -> 88, one-shot LL128 108 -> 96.
+// (tokens 512): two-shot LL128 89 -> 88, one-shot LL128 108 -> 96.  At
+// N <= 4 the message-size sweep measured one-shot LL128 5-13 % and two-shot
+// LL 1-11 % slower from 128 MiB with the larger tiles: there they keep 4
+// passes and 16 KiB.
 inline uint64_t simple_tile_cap(uint64_t rank_bytes, int kind, bool in_place) {
   uint64_t hi = 131072;
   if (kind == K_RING || kind == K_TREE) hi = 32768;
@@ -158,11 +161,12 @@ inline uint64_t simple_tile_cap(uint64_t rank_bytes, int kind, bool in_place) {
   return hi;
 }
 
-inline uint64_t pick_tile_bytes(int proto, uint64_t rank_bytes, int kind, bool in_place) {
+inline uint64_t pick_tile_bytes(int proto, uint64_t rank_bytes, int kind, bool in_place, int nranks = 8) {
   const uint64_t want = floor_pow2(rank_bytes / 128 + 1);
   if (proto == PROTO_SIMPLE) return clampu(want, 4096, simple_tile_cap(rank_bytes, kind, in_place));
-  if (proto == PROTO_LL) return clampu(want, 4096, 32768);
-  const uint64_t passes = kind == K_ONESHOT ? 16 : (kind == K_RS_DIRECT ? 4 : 8);
+  if (proto == PROTO_LL) return clampu(want, 4096, kind == K_TWOSHOT && nranks <= 4 ? 16384 : 32768);
+  const uint64_t passes =
+      kind == K_ONESHOT ? (nranks <= 4 ? 4 : 16) : (kind == K_RS_DIRECT ? 4 : 8);
   return LL128_TILE_UNIT * clampu(floor_pow2(want / LL128_TILE_UNIT + 1), 1, passes);
 }
 
@@ -228,7 +232,7 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
 
   const bool lines = proto != PROTO_SIMPLE;
   const uint64_t rank_bytes = g.total * es;
-  uint64_t tile_b = pick_tile_bytes(proto, rank_bytes, g.kind, in_place != 0);
+  uint64_t tile_b = pick_tile_bytes(proto, rank_bytes, g.kind, in_place != 0, nranks);
   if (tune.tile_bytes && !lines && !(g.kind == K_ONESHOT && in_place))
     tile_b = clampu(tune.tile_bytes / 16 * 16, 4096, 512 * 1024);
   if (tune.line_tile_bytes && lines)
