@@ -1052,51 +1052,237 @@ __device__ __forceinline__ void finish_workgroup(const KArgs& a, uint32_t finish
   }
 }
 
+// Workgroup 0 of a colocated call (thread 0) moves the call counter on.
+// Every workgroup adds itself to `done` once its epoch load has returned, so a
+// full count means no workgroup of the call can still read the old epoch.
+// `counted` is a load of the count issued earlier, with the receive's loads.
+// The wait ends in practice at once: a workgroup counts itself in before any
+// wait of its own.  It is bounded all the same; it ignores the abort word,
+// because a workgroup not yet counted in still reads the epoch after an abort.
+__device__ __forceinline__ void advance_epoch(const KArgs& a, uint64_t epoch, uint32_t counted) {
+  if (counted < gridDim.x) {
+    uint32_t level = 0, polls = 0;
+    uint64_t t0 = 0;
+    while (true) {
+      poll_sleep(level);
+      if (ld_u32(&a.ctl->done) >= gridDim.x) break;
+      if (++polls % POLL_CHECK_EVERY) continue;
+      const uint64_t now = wall_clock64();
+      if (!t0) t0 = now;
+      else if (now - t0 > a.timeout) { raise_timeout(a.ctl, 0, 0); break; }
+    }
+  }
+  __hip_atomic_store(&a.ctl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&a.ctl->epoch, epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The send and the receive of a colocated LL (tile, rank), written out for
+// latency: `pre` holds the rank's input words (the whole tile: one pass, U_LL
+// words per thread, loaded with the epoch).  They go on the wire as lines;
+// then every peer's lines of the tile load at once, and the sum runs in rank
+// order with `pre` as the rank's own term, as the generic pass sums it.
+// Bounded buffer accesses replace the per-lane tail branches: behind such a
+// branch the compiler waited for each batch of loads before issuing the next
+// (the generic pass took three round trips here, one for the input pointer,
+// one for the input words, one for the lines).  While any line is missing,
+// a poll reloads every peer line of the tile at once (a line already seen
+// does not change during the call), so a late peer costs one round trip,
+// not one per term; a reload of only the missing lines made the compiler
+// wait after each term.
+template <int DT>
+__device__ __forceinline__ void colocated_ll(const KArgs& a, const Task& k, uint64_t epoch,
+                                             const uint32_t (&pre)[U_LL], uint64_t nbytes, uint32_t& counted) {
+  const int n = a.g.nranks;
+  const int r = k.rank;
+  const uint32_t nwords = (uint32_t)cdiv(nbytes, 4);
+  const uint32_t flag = (uint32_t)(epoch % 0xffffffffull) + 1u;
+  // Staging of this tile for rank i: tile_lines + i * slot_stride (slot_tile,
+  // computed once: per term, the compiler re-read the arguments and waited).
+  const uint64_t slot_stride = uniform64(a.g.slot_lines * a.g.line_bytes);
+  const char* tile_lines = a.lines + uniform64(k.tile * a.g.tile_lines * a.g.line_bytes);
+  if (!withheld(a, 0, r)) {
+    const Rsrc own = make_rsrc(tile_lines + (uint64_t)r * slot_stride, nwords * 8);
+#pragma unroll
+    for (int u = 0; u < U_LL; ++u)
+      cst8(own, 8 * (threadIdx.x + (uint32_t)u * WG_THREADS), make_uint2(pre[u], flag));
+  }
+  // The peers store their lines at about the same time: loads issued before
+  // this workgroup's own stores have landed mostly came back unwritten and
+  // cost a poll (t=1 decode, N=8 bf16: 7.0 us per call without this wait,
+  // 6.0 us with it).
+  wait_mem();
+  if (blockIdx.x == 0) counted = ld_u32(&a.ctl->done);
+  uint2 got[MAX_RANKS][U_LL];  // (payload word, flag) of each peer's lines
+#pragma unroll
+  for (int i = 0; i < MAX_RANKS; ++i) {
+    if (i >= n) break;
+    if (i == r) continue;
+    const Rsrc li = make_rsrc(tile_lines + (uint64_t)i * slot_stride, nwords * 8);
+#pragma unroll
+    for (int u = 0; u < U_LL; ++u) got[i][u] = cld8(li, 8 * (threadIdx.x + (uint32_t)u * WG_THREADS));
+  }
+  // Lanes past the tile read zeros and count as ready.
+  auto missing = [&](int i, int u) {
+    return threadIdx.x + (uint32_t)u * WG_THREADS < nwords && got[i][u].y != flag;
+  };
+  bool ready = true;
+#pragma unroll
+  for (int i = 0; i < MAX_RANKS; ++i) {
+    if (i >= n) break;
+    if (i == r) continue;
+#pragma unroll
+    for (int u = 0; u < U_LL; ++u) ready = ready && !missing(i, u);
+  }
+  if (!ready) {
+    PollClock clock;
+    uint32_t level = 0;
+    while (true) {
+      poll_sleep(level);
+      ready = true;
+#pragma unroll
+      for (int i = 0; i < MAX_RANKS; ++i) {
+        if (i >= n) break;
+        if (i == r) continue;
+        const Rsrc li = make_rsrc(tile_lines + (uint64_t)i * slot_stride, nwords * 8);
+#pragma unroll
+        for (int u = 0; u < U_LL; ++u) got[i][u] = cld8(li, 8 * (threadIdx.x + (uint32_t)u * WG_THREADS));
+      }
+#pragma unroll
+      for (int i = 0; i < MAX_RANKS; ++i) {
+        if (i >= n) break;
+        if (i == r) continue;
+#pragma unroll
+        for (int u = 0; u < U_LL; ++u) ready = ready && !missing(i, u);
+      }
+      if (ready) break;
+      const int st = clock.tick(a);
+      if (st == POLL_ABORTED) { note_blocked(a.ctl, 1, r); return; }
+      if (st == POLL_TIMED_OUT) { raise_timeout(a.ctl, 1, r); return; }
+    }
+  }
+  const Rsrc out = make_rsrc(a.out[r] + k.lo * (uint64_t)Elem<DT>::size, (uint32_t)nbytes);
+#pragma unroll
+  for (int u = 0; u < U_LL; ++u) {
+    uint32_t res = pre[u];
+    if (n > 1) {
+      Word<DT> acc;
+#pragma unroll
+      for (int i = 0; i < MAX_RANKS; ++i) {
+        if (i >= n) break;
+        const Word<DT> x = Word<DT>::widen(i == r ? pre[u] : got[i][u].x);
+        if (i == 0) acc = x; else acc.add(x);
+      }
+      res = acc.narrow();
+    }
+    const uint32_t off = 4 * (threadIdx.x + (uint32_t)u * WG_THREADS);
+    if constexpr (Elem<DT>::size == 2) {
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)res, out, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(res >> 16), out, off + 2, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(res, out, off, 0, 0);
+    }
+  }
+}
+
 // Small one-shot calls over LL / LL128 (g.colocated): workgroup b is rank
 // b % N's program on tile b / N.  It puts its input tile on the wire, then
 // gathers every rank's lines of the tile and sums them: the send and the
 // receive of a (tile, rank) in one workgroup, with no ticket fetch between
-// them, so a decode-sized call is one round trip for the epoch and the
-// input, the line stores, and the polls of the peers' lines.  The N
-// workgroups of a tile wait on each other, so the grid (at most
+// them.  The N workgroups of a tile wait on each other, so the grid (at most
 // COLOCATED_WORKGROUPS) must be resident at once; launch_collective runs the
 // ticketed schedule instead when the workgroup budget is smaller.
+//
+// Round trips of a decode-sized LL call: the epoch, loaded together with the
+// rank's input words; the line stores; the loads of the peers' lines.  No
+// workgroup waits on the return of an atomic: the last-workgroup-out count of
+// the ticketed schedule is replaced by advance_epoch in workgroup 0.
 template <int DT, int PROTO>
 __device__ __forceinline__ void colocated_oneshot(const KArgs& a) {
   __shared__ uint64_t s_epoch;
   __shared__ uint32_t s_abort;
-  if (threadIdx.x == 0) {  // both loads issued before either value is used: one round trip
+  const Geometry& g = a.g;
+  const int n = g.nranks;
+  Task k;
+  // Scalar registers: a rank held in a vector register made the compiler
+  // fetch a.in[rank] with a vector load and wait for it.
+  k.rank = (int32_t)uniform(blockIdx.x % (uint32_t)n);
+  k.peer = 0; k.step = 0; k.block = 0; k.chain = 0;
+  k.tile = uniform(blockIdx.x / (uint32_t)n);
+  tile_range(g, g.total, k.tile, &k.lo, &k.hi);
+  const int r = k.rank;
+  const int es = Elem<DT>::size;
+  const uint64_t nbytes = (k.hi - k.lo) * (uint64_t)es;
+  // Bounded buffer loads (bytes past the tile read as 0) need no per-lane
+  // branch: behind a branch, the compiler waited for these loads before the
+  // epoch load went out.  bf16 words load as two halves, since a bf16 tile
+  // may start on any 2-byte boundary.
+  uint32_t pre[U_LL];
+  if constexpr (PROTO == PROTO_LL) {
+    static_assert(U_LL * WG_THREADS * 4 == LL_COLOCATED_TILE, "a colocated LL tile is one pass");
+    const Rsrc src = make_rsrc(a.in[r] + k.lo * (uint64_t)es, (uint32_t)nbytes);
+#pragma unroll
+    for (int u = 0; u < U_LL; ++u) {
+      const uint32_t off = 4 * (threadIdx.x + (uint32_t)u * WG_THREADS);
+      if constexpr (Elem<DT>::size == 2)
+        pre[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(src, off, 0, 0) |
+                 ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(src, off + 2, 0, 0) << 16);
+      else
+        pre[u] = __builtin_amdgcn_raw_buffer_load_b32(src, off, 0, 0);
+    }
+  }
+  if (threadIdx.x == 0) {
     const uint64_t e = __hip_atomic_load(&a.ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t ab = ld_u32(&a.ctl->abort);
     s_epoch = e;
     s_abort = ab;
   }
   __syncthreads();
+  // Issued after the barrier, which follows the LDS store of the loaded
+  // epoch: the count never runs ahead of the load.
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint64_t epoch = uniform64(s_epoch);
   const bool aborted = uniform(s_abort) != 0;
-  uint32_t finished = 0;
-  if (!aborted) {  // a latched error: run nothing
-    const int n = a.g.nranks;
-    Task k;
-    k.rank = (int32_t)(blockIdx.x % (uint32_t)n);
-    k.peer = 0; k.step = 0; k.block = 0; k.chain = 0;
-    k.tile = blockIdx.x / (uint32_t)n;
-    tile_range(a.g, a.g.total, k.tile, &k.lo, &k.hi);
-    if (k.hi > k.lo) {
+  uint32_t finished = 0, counted = 0;
+  if (!aborted && k.hi > k.lo) {  // a latched error: run nothing
+    if constexpr (PROTO == PROTO_LL) {
+      colocated_ll<DT>(a, k, epoch, pre, nbytes, counted);
+    } else {
       k.phase = PH_SEND;
       run_task<DT, PROTO, K_ONESHOT>(a, k, epoch);
       __syncthreads();
+      if (blockIdx.x == 0) counted = ld_u32(&a.ctl->done);
       k.phase = PH_RECV_FOLD;
       run_task<DT, PROTO, K_ONESHOT>(a, k, epoch);
-      finished = 2;
     }
+    finished = 2;
+  } else if (blockIdx.x == 0) {
+    counted = ld_u32(&a.ctl->done);
   }
-  __syncthreads();
-  if (threadIdx.x == 0) finish_workgroup(a, finished);
+  // No barrier before the epoch moves on: it needs only the full count, and
+  // behind a barrier (which waits for the output stores) workgroup 0's two
+  // stores would land one round trip after every other workgroup's last.
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(&a.ctl->diag[5], (uint64_t)finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x == 0) advance_epoch(a, epoch, counted);
+  }
+}
+
+// Loads one word of every 64-byte line of the kernel arguments, all issued
+// before one wait, so the argument loads the compiler places later (each
+// followed by a wait for its value) hit the scalar cache.  Without it a
+// decode-sized call spent most of its time in such misses, one after another.
+__device__ __forceinline__ void warm_kernel_args() {
+  typedef const uint32_t __attribute__((address_space(4))) * KPtr;
+  const KPtr p = (KPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t x = 0;
+#pragma unroll
+  for (uint32_t i = 0; i < (sizeof(KArgs) + 63) / 64; ++i) x ^= p[16 * i];
+  asm volatile("" ::"s"(x));
 }
 
 template <int DT, int PROTO, int KIND>
 __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
+  warm_kernel_args();
   if constexpr (KIND == K_ONESHOT && PROTO != PROTO_SIMPLE) {
     if (a.colocate) {
       colocated_oneshot<DT, PROTO>(a);
@@ -1309,7 +1495,7 @@ hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uin
   // One workgroup per (tile, rank) of a small line-protocol one-shot, when
   // the budget lets them all be resident; otherwise the ticketed schedule.
   b.colocate = 0;
-  if (a.g.colocated && a.g.tiles * (uint64_t)a.g.nranks <= cap) {
+  if (a.g.colocated && !a.rearm_errors && a.g.tiles * (uint64_t)a.g.nranks <= cap) {
     b.colocate = 1;
     b.batch = 1;
     grid = a.g.tiles * (uint64_t)a.g.nranks;

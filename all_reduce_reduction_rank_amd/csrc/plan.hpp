@@ -42,6 +42,9 @@ constexpr uint64_t LL128_TILE_UNIT = 3840;  // 32 lines of 120 payload bytes: on
 // workgroup, with no ticket counter: the N workgroups of a tile wait on each
 // other, so the grid is kept small enough to be resident at once.
 constexpr uint64_t COLOCATED_WORKGROUPS = 64;
+// A colocated LL tile is one pass of a workgroup (4 words per thread), so its
+// send loads the whole tile with the call's first round trip.
+constexpr uint64_t LL_COLOCATED_TILE = 4096;
 constexpr uint64_t LL128_ALIGN = 240;       // 2 lines: a multiple of 16 bytes and of 120 bytes
 
 inline int esize_of(int dtype) { return dtype == DT_BF16 ? 2 : 4; }
@@ -244,13 +247,15 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
   // the tile's lines), LL tiles do not (an LL workgroup walks a larger tile
   // in passes one after another).  Measured at N=8 bf16, us per call in a
   // HIP graph (ticketed -> one workgroup per tile and rank): LL 10 KiB
-  // 9.83 -> 9.35; LL128 10 KiB 11.93 -> 10.96, 80 KiB 16.6 -> 12.4; LL
+  // 9.83 -> 9.35 (6.0 once the LL tile became one pass with its own send
+  // and receive); LL128 10 KiB 11.93 -> 10.96, 80 KiB 16.6 -> 12.4; LL
   // 80 KiB with tiles grown to fit: 14.3 -> 20.9, so it stays ticketed.
   bool colocated = false;
   if (lines && g.kind == K_ONESHOT && !tune.line_tile_bytes && rank_bytes) {
     const uint64_t max_tiles = COLOCATED_WORKGROUPS / n;
     const uint64_t need = cdiv(cdiv(rank_bytes, max_tiles), LL128_TILE_UNIT) * LL128_TILE_UNIT;
-    if (cdiv(rank_bytes, tile_b) <= max_tiles) colocated = true;
+    if (cdiv(rank_bytes, tile_b) <= max_tiles && (proto == PROTO_LL128 || tile_b <= LL_COLOCATED_TILE))
+      colocated = true;
     else if (proto == PROTO_LL128 && need <= 16 * LL128_TILE_UNIT) { tile_b = need; colocated = true; }
   }
   // Tasks that never wait (Simple one-shot out of place, direct RS and AG)
