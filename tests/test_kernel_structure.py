@@ -6,7 +6,8 @@ lane-divergent region around the loop's back edge, the compiler split the
 loop by lane.  Lanes 1..63 then re-ran the task on a stale ticket at the
 barrier while lane 0 waited for them outside: an endless loop.  The kernels
 now keep every barrier of a task in the same loop as the ticket fetch.
-Also checks that no kernel spills vector registers to scratch memory.
+Also checks that no kernel spills vector registers to scratch memory, and
+that consumers order their payload loads after their flag loads.
 """
 
 import os
@@ -130,3 +131,71 @@ def test_fused_rmsnorm_kernel_keeps_its_row_in_registers(tmp_path):
     spills = re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)
     assert len(spills) == 4 and all(int(x) == 0 for x in spills)  # {bf16, fp32} x {one row, rows}
     assert not re.search(r"^\s+scratch_(load|store)", text, re.M)
+
+
+# ------------------------------------------------------------------ ordering
+# A consumer reads a flag with a relaxed device-scope load and then the
+# payload the flag publishes with device-scope (sc1) loads; no acquire fence
+# sits between them.  That is correct only while every payload load issues
+# after the flag value has come back: the producer's payload stores were
+# complete device-wide before its flag store, and sc1 loads read the
+# coherence point, not a stale cache.  The check: in the Simple and LL128
+# kernels, no 16-byte sc1 load (payload) issues while an 8-byte sc1 load (a
+# flag; LL128's flag word, Simple's flag array) is still in flight.  Loads
+# in flight are tracked in file order and kept across labels and branches,
+# which is stricter than any single execution path.  LL needs no such order:
+# its flag and payload arrive in one 8-byte load.
+_LOAD = re.compile(r"^\s+(?:global|buffer)_load_(\w+)\s")
+_WAIT = re.compile(r"s_waitcnt\s.*vmcnt\((\d+)\)")
+_SC1 = re.compile(r"\ssc1(?:\s|$)")
+
+
+def _payload_over_flag(body):
+    """(payload loads checked, payload loads issued while a flag load was in flight)."""
+    pending, checked, bad = [], 0, []
+    for line in body.split("\n"):
+        w = _WAIT.search(line)
+        if w:
+            keep = int(w.group(1))
+            pending = pending[len(pending) - keep:] if keep else []
+            continue
+        m = _LOAD.match(line)
+        if m:
+            sc1 = _SC1.search(line) is not None
+            if m.group(1) == "dwordx4" and sc1:
+                checked += 1
+                if "flag" in pending:
+                    bad.append(line.strip())
+            pending.append("flag" if m.group(1) == "dwordx2" and sc1 else "data")
+        elif re.match(r"^\s+(?:global|buffer)_(?:store|atomic)", line):
+            pending.append("data")  # stores and atomics count in vmcnt too
+    return checked, bad
+
+
+def test_the_order_check_sees_a_payload_load_over_a_flag():
+    flag = "\tglobal_load_dwordx2 v[2:3], v1, s[4:5] sc1"
+    data = "\tglobal_load_dword v6, v1, s[8:9]"
+    payload = "\tbuffer_load_dwordx4 v[8:11], v1, s[12:15], 0 offen sc1"
+    plain = "\tbuffer_load_dwordx4 v[8:11], v1, s[12:15], 0 offen"
+    assert _payload_over_flag("\n".join([flag, payload]))[1]
+    assert not _payload_over_flag("\n".join([flag, "\ts_waitcnt vmcnt(0)", payload]))[1]
+    assert not _payload_over_flag("\n".join([flag, data, "\ts_waitcnt vmcnt(1)", payload]))[1]
+    assert _payload_over_flag("\n".join([data, flag, "\ts_waitcnt vmcnt(1)", payload]))[1]
+    assert _payload_over_flag("\n".join([flag, ".LBB0_1:", "\ts_cbranch_scc1 .LBB0_2", payload]))[1]
+    assert not _payload_over_flag("\n".join([flag, plain]))[1]
+    assert _payload_over_flag("\n".join([flag, payload, plain])) == (1, [payload.strip()])
+
+
+def test_payload_loads_wait_for_their_flags(asm):
+    checked = 0
+    for m in _kernels(asm):
+        name = m.group(1)
+        proto = int(re.match(r"_ZN2ar17collective_kernelILi\dELi(\d)E", name).group(1))
+        if proto == 1:  # LL
+            continue
+        n, bad = _payload_over_flag(m.group(2))
+        checked += n
+        assert not bad, f"{name}: payload loads issued over a flag load: {bad[:3]}"
+    # The pattern must keep matching the code: a renamed instruction would
+    # otherwise pass vacuously.
+    assert checked >= 300, checked
