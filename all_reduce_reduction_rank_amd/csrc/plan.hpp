@@ -42,6 +42,9 @@ constexpr uint64_t LL128_TILE_UNIT = 3840;  // 32 lines of 120 payload bytes: on
 // workgroup, with no ticket counter: the N workgroups of a tile wait on each
 // other, so the grid is kept small enough to be resident at once.
 constexpr uint64_t COLOCATED_WORKGROUPS = 64;
+// LL's colocated workgroups each run one pass (one 4 KiB tile), so more of
+// them fit the same latency: up to this many.
+constexpr uint64_t COLOCATED_WORKGROUPS_LL = 256;
 // A colocated LL tile is one pass of a workgroup (4 words per thread), so its
 // send loads the whole tile with the call's first round trip.
 constexpr uint64_t LL_COLOCATED_TILE = 4096;
@@ -252,7 +255,7 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
   // 80 KiB with tiles grown to fit: 14.3 -> 20.9, so it stays ticketed.
   bool colocated = false;
   if (lines && g.kind == K_ONESHOT && !tune.line_tile_bytes && rank_bytes) {
-    const uint64_t max_tiles = COLOCATED_WORKGROUPS / n;
+    const uint64_t max_tiles = (proto == PROTO_LL ? COLOCATED_WORKGROUPS_LL : COLOCATED_WORKGROUPS) / n;
     const uint64_t need = cdiv(cdiv(rank_bytes, max_tiles), LL128_TILE_UNIT) * LL128_TILE_UNIT;
     if (cdiv(rank_bytes, tile_b) <= max_tiles && (proto == PROTO_LL128 || tile_b <= LL_COLOCATED_TILE))
       colocated = true;
@@ -364,7 +367,8 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
         g.per_group = 2 * n;
         g.groups = g.tiles ? g.tiles + lag : 0;
         g.nslots = n;
-        g.colocated = colocated && g.tiles * n <= COLOCATED_WORKGROUPS ? 1 : 0;
+        g.colocated =
+            colocated && g.tiles * n <= (proto == PROTO_LL ? COLOCATED_WORKGROUPS_LL : COLOCATED_WORKGROUPS) ? 1 : 0;
       }
       break;
     case K_TWOSHOT:

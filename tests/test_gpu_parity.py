@@ -500,9 +500,11 @@ def test_small_line_one_shot_runs_one_workgroup_per_tile_and_rank(dt, n, proto):
     # Decode-sized one-shot calls over LL / LL128 run each (tile, rank) as one
     # workgroup with no ticket counter; the call log shows it, and the results
     # equal the oracle's out of place and in place.  With a workgroup budget
-    # below the grid the same call takes the ticketed schedule.
+    # below the grid the same call takes the ticketed schedule.  LL's largest
+    # case (80 KiB per rank in 4-byte types: 20 tiles) needs up to 160
+    # workgroups, past LL128's cap of 64.
     c = Comm(n, 1 << 20, 1 << 20)
-    for count in (1, 999, 5120, 40960 if proto == "ll128" else 3000):
+    for count in (1, 999, 5120, 40960 if proto == "ll128" else 3000, 20480):
         host = inputs.rank_inputs(n, count, dt, _dist(dt), seed=count, cfg=80)
         want = C.allreduce(host, dt, "oneshot")
         send = [to_dev(x, dt) for x in host]
