@@ -1077,21 +1077,22 @@ __device__ __forceinline__ void advance_epoch(const KArgs& a, uint64_t epoch, ui
 }
 
 // The send and the receive of a colocated LL (tile, rank), written out for
-// latency: `pre` holds the rank's input words (the whole tile: one pass, U_LL
-// words per thread, loaded with the epoch).  They go on the wire as lines;
-// then every peer's lines of the tile load at once, and the sum runs in rank
-// order with `pre` as the rank's own term, as the generic pass sums it.
-// Bounded buffer accesses replace the per-lane tail branches: behind such a
-// branch the compiler waited for each batch of loads before issuing the next
-// (the generic pass took three round trips here, one for the input pointer,
-// one for the input words, one for the lines).  While any line is missing,
-// a poll reloads every peer line of the tile at once (a line already seen
-// does not change during the call), so a late peer costs one round trip,
-// not one per term; a reload of only the missing lines made the compiler
-// wait after each term.
-template <int DT>
+// latency: `pre` holds the rank's input words (the whole tile: `passes`
+// passes of U_LL words per thread, loaded with the epoch).  They go on the
+// wire as lines; then, pass by pass, every peer's lines load at once and the
+// sum runs in rank order with `pre` as the rank's own term, as the generic
+// pass sums it.  Bounded buffer accesses replace the per-lane tail
+// branches: behind such a branch the compiler waited for each batch of
+// loads before issuing the next (the generic pass took three round trips
+// here, one for the input pointer, one for the input words, one for the
+// lines).  While any line of a pass is missing, a poll reloads every peer
+// line of the pass at once (a line already seen does not change during the
+// call), so a late peer costs one round trip, not one per term; a reload of
+// only the missing lines made the compiler wait after each term.
+template <int DT, int PASSES>
 __device__ __forceinline__ void colocated_ll(const KArgs& a, const Task& k, uint64_t epoch,
-                                             const uint32_t (&pre)[U_LL], uint64_t nbytes, uint32_t& counted) {
+                                             const uint32_t (&pre)[PASSES][U_LL], int passes, uint64_t nbytes,
+                                             uint32_t& counted) {
   const int n = a.g.nranks;
   const int r = k.rank;
   const uint32_t nwords = (uint32_t)cdiv(nbytes, 4);
@@ -1103,8 +1104,10 @@ __device__ __forceinline__ void colocated_ll(const KArgs& a, const Task& k, uint
   if (!withheld(a, 0, r)) {
     const Rsrc own = make_rsrc(tile_lines + (uint64_t)r * slot_stride, nwords * 8);
 #pragma unroll
-    for (int u = 0; u < U_LL; ++u)
-      cst8(own, 8 * (threadIdx.x + (uint32_t)u * WG_THREADS), make_uint2(pre[u], flag));
+    for (int p = 0; p < PASSES; ++p)  // stores past the tile are dropped
+#pragma unroll
+      for (int u = 0; u < U_LL; ++u)
+        cst8(own, 8 * (threadIdx.x + (uint32_t)(p * U_LL + u) * WG_THREADS), make_uint2(pre[p][u], flag));
   }
   // The peers store their lines at about the same time: loads issued before
   // this workgroup's own stores have landed mostly came back unwritten and
@@ -1112,74 +1115,77 @@ __device__ __forceinline__ void colocated_ll(const KArgs& a, const Task& k, uint
   // 6.0 us with it).
   wait_mem();
   if (blockIdx.x == 0) counted = ld_u32(&a.ctl->done);
-  uint2 got[MAX_RANKS][U_LL];  // (payload word, flag) of each peer's lines
-#pragma unroll
-  for (int i = 0; i < MAX_RANKS; ++i) {
-    if (i >= n) break;
-    if (i == r) continue;
-    const Rsrc li = make_rsrc(tile_lines + (uint64_t)i * slot_stride, nwords * 8);
-#pragma unroll
-    for (int u = 0; u < U_LL; ++u) got[i][u] = cld8(li, 8 * (threadIdx.x + (uint32_t)u * WG_THREADS));
-  }
-  // Lanes past the tile read zeros and count as ready.
-  auto missing = [&](int i, int u) {
-    return threadIdx.x + (uint32_t)u * WG_THREADS < nwords && got[i][u].y != flag;
-  };
-  bool ready = true;
-#pragma unroll
-  for (int i = 0; i < MAX_RANKS; ++i) {
-    if (i >= n) break;
-    if (i == r) continue;
-#pragma unroll
-    for (int u = 0; u < U_LL; ++u) ready = ready && !missing(i, u);
-  }
-  if (!ready) {
-    PollClock clock;
-    uint32_t level = 0;
-    while (true) {
-      poll_sleep(level);
-      ready = true;
-#pragma unroll
-      for (int i = 0; i < MAX_RANKS; ++i) {
-        if (i >= n) break;
-        if (i == r) continue;
-        const Rsrc li = make_rsrc(tile_lines + (uint64_t)i * slot_stride, nwords * 8);
-#pragma unroll
-        for (int u = 0; u < U_LL; ++u) got[i][u] = cld8(li, 8 * (threadIdx.x + (uint32_t)u * WG_THREADS));
-      }
-#pragma unroll
-      for (int i = 0; i < MAX_RANKS; ++i) {
-        if (i >= n) break;
-        if (i == r) continue;
-#pragma unroll
-        for (int u = 0; u < U_LL; ++u) ready = ready && !missing(i, u);
-      }
-      if (ready) break;
-      const int st = clock.tick(a);
-      if (st == POLL_ABORTED) { note_blocked(a.ctl, 1, r); return; }
-      if (st == POLL_TIMED_OUT) { raise_timeout(a.ctl, 1, r); return; }
-    }
-  }
   const Rsrc out = make_rsrc(a.out[r] + k.lo * (uint64_t)Elem<DT>::size, (uint32_t)nbytes);
 #pragma unroll
-  for (int u = 0; u < U_LL; ++u) {
-    uint32_t res = pre[u];
-    if (n > 1) {
-      Word<DT> acc;
+  for (int p = 0; p < PASSES; ++p) {
+    if (p >= passes) break;
+    const uint32_t base = threadIdx.x + (uint32_t)(p * U_LL) * WG_THREADS;  // word of u = 0
+    uint2 got[MAX_RANKS][U_LL];  // (payload word, flag) of each peer's lines
 #pragma unroll
-      for (int i = 0; i < MAX_RANKS; ++i) {
-        if (i >= n) break;
-        const Word<DT> x = Word<DT>::widen(i == r ? pre[u] : got[i][u].x);
-        if (i == 0) acc = x; else acc.add(x);
-      }
-      res = acc.narrow();
+    for (int i = 0; i < MAX_RANKS; ++i) {
+      if (i >= n) break;
+      if (i == r) continue;
+      const Rsrc li = make_rsrc(tile_lines + (uint64_t)i * slot_stride, nwords * 8);
+#pragma unroll
+      for (int u = 0; u < U_LL; ++u) got[i][u] = cld8(li, 8 * (base + (uint32_t)u * WG_THREADS));
     }
-    const uint32_t off = 4 * (threadIdx.x + (uint32_t)u * WG_THREADS);
-    if constexpr (Elem<DT>::size == 2) {
-      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)res, out, off, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(res >> 16), out, off + 2, 0, 0);
-    } else {
-      __builtin_amdgcn_raw_buffer_store_b32(res, out, off, 0, 0);
+    // Lanes past the tile read zeros and count as ready.
+    auto missing = [&](int i, int u) { return base + (uint32_t)u * WG_THREADS < nwords && got[i][u].y != flag; };
+    bool ready = true;
+#pragma unroll
+    for (int i = 0; i < MAX_RANKS; ++i) {
+      if (i >= n) break;
+      if (i == r) continue;
+#pragma unroll
+      for (int u = 0; u < U_LL; ++u) ready = ready && !missing(i, u);
+    }
+    if (!ready) {
+      PollClock clock;
+      uint32_t level = 0;
+      while (true) {
+        poll_sleep(level);
+        ready = true;
+#pragma unroll
+        for (int i = 0; i < MAX_RANKS; ++i) {
+          if (i >= n) break;
+          if (i == r) continue;
+          const Rsrc li = make_rsrc(tile_lines + (uint64_t)i * slot_stride, nwords * 8);
+#pragma unroll
+          for (int u = 0; u < U_LL; ++u) got[i][u] = cld8(li, 8 * (base + (uint32_t)u * WG_THREADS));
+        }
+#pragma unroll
+        for (int i = 0; i < MAX_RANKS; ++i) {
+          if (i >= n) break;
+          if (i == r) continue;
+#pragma unroll
+          for (int u = 0; u < U_LL; ++u) ready = ready && !missing(i, u);
+        }
+        if (ready) break;
+        const int st = clock.tick(a);
+        if (st == POLL_ABORTED) { note_blocked(a.ctl, 1, r); return; }
+        if (st == POLL_TIMED_OUT) { raise_timeout(a.ctl, 1, r); return; }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U_LL; ++u) {
+      uint32_t res = pre[p][u];
+      if (n > 1) {
+        Word<DT> acc;
+#pragma unroll
+        for (int i = 0; i < MAX_RANKS; ++i) {
+          if (i >= n) break;
+          const Word<DT> x = Word<DT>::widen(i == r ? pre[p][u] : got[i][u].x);
+          if (i == 0) acc = x; else acc.add(x);
+        }
+        res = acc.narrow();
+      }
+      const uint32_t off = 4 * (base + (uint32_t)u * WG_THREADS);
+      if constexpr (Elem<DT>::size == 2) {
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)res, out, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(res >> 16), out, off + 2, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b32(res, out, off, 0, 0);
+      }
     }
   }
 }
@@ -1196,7 +1202,7 @@ __device__ __forceinline__ void colocated_ll(const KArgs& a, const Task& k, uint
 // rank's input words; the line stores; the loads of the peers' lines.  No
 // workgroup waits on the return of an atomic: the last-workgroup-out count of
 // the ticketed schedule is replaced by advance_epoch in workgroup 0.
-template <int DT, int PROTO>
+template <int DT, int PROTO, int PASSES>
 __device__ __forceinline__ void colocated_oneshot(const KArgs& a) {
   __shared__ uint64_t s_epoch;
   __shared__ uint32_t s_abort;
@@ -1212,23 +1218,31 @@ __device__ __forceinline__ void colocated_oneshot(const KArgs& a) {
   const int r = k.rank;
   const int es = Elem<DT>::size;
   const uint64_t nbytes = (k.hi - k.lo) * (uint64_t)es;
-  // Bounded buffer loads (bytes past the tile read as 0) need no per-lane
-  // branch: behind a branch, the compiler waited for these loads before the
-  // epoch load went out.  bf16 words load as two halves, since a bf16 tile
-  // may start on any 2-byte boundary.
-  uint32_t pre[U_LL];
+  // Bounded buffer loads (bytes past the tile read as 0, with no memory
+  // access) need no branch, per lane or per pass: behind a branch, the
+  // compiler waited for these loads before the epoch load went out.  bf16
+  // words load as two halves, since a bf16 tile may start on any 2-byte
+  // boundary.  The loads and stores of the PASSES passes are all issued,
+  // those past the tile included (they still cost address-unit time: a
+  // one-pass tile in the 8-pass kernel took 2 us longer), hence a one-pass
+  // kernel for one-pass tiles.
+  uint32_t pre[PASSES][U_LL];
+  int passes = 0;
   if constexpr (PROTO == PROTO_LL) {
-    static_assert(U_LL * WG_THREADS * 4 == LL_COLOCATED_TILE, "a colocated LL tile is one pass");
+    static_assert(U_LL * WG_THREADS * 4 == LL_COLOCATED_TILE, "a colocated LL pass is 4 KiB");
+    passes = (int)cdiv(nbytes, LL_COLOCATED_TILE);  // at most PASSES (launch_collective)
     const Rsrc src = make_rsrc(a.in[r] + k.lo * (uint64_t)es, (uint32_t)nbytes);
 #pragma unroll
-    for (int u = 0; u < U_LL; ++u) {
-      const uint32_t off = 4 * (threadIdx.x + (uint32_t)u * WG_THREADS);
-      if constexpr (Elem<DT>::size == 2)
-        pre[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(src, off, 0, 0) |
-                 ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(src, off + 2, 0, 0) << 16);
-      else
-        pre[u] = __builtin_amdgcn_raw_buffer_load_b32(src, off, 0, 0);
-    }
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+      for (int u = 0; u < U_LL; ++u) {
+        const uint32_t off = 4 * (threadIdx.x + (uint32_t)(p * U_LL + u) * WG_THREADS);
+        if constexpr (Elem<DT>::size == 2)
+          pre[p][u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(src, off, 0, 0) |
+                      ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(src, off + 2, 0, 0) << 16);
+        else
+          pre[p][u] = __builtin_amdgcn_raw_buffer_load_b32(src, off, 0, 0);
+      }
   }
   if (threadIdx.x == 0) {
     const uint64_t e = __hip_atomic_load(&a.ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1245,7 +1259,7 @@ __device__ __forceinline__ void colocated_oneshot(const KArgs& a) {
   uint32_t finished = 0, counted = 0;
   if (!aborted && k.hi > k.lo) {  // a latched error: run nothing
     if constexpr (PROTO == PROTO_LL) {
-      colocated_ll<DT>(a, k, epoch, pre, nbytes, counted);
+      colocated_ll<DT, PASSES>(a, k, epoch, pre, passes, nbytes, counted);
     } else {
       k.phase = PH_SEND;
       run_task<DT, PROTO, K_ONESHOT>(a, k, epoch);
@@ -1280,15 +1294,18 @@ __device__ __forceinline__ void warm_kernel_args() {
   asm volatile("" ::"s"(x));
 }
 
+// Small LL / LL128 one-shots (a.colocate) run in a kernel of their own: the
+// LL send holds a whole tile in registers, which in the ticketed kernel
+// would have cut the workgroups per CU of every LL one-shot call.
+template <int DT, int PROTO, int PASSES>
+__global__ __launch_bounds__(WG_THREADS) void colocated_kernel(KArgs a) {
+  warm_kernel_args();
+  colocated_oneshot<DT, PROTO, PASSES>(a);
+}
+
 template <int DT, int PROTO, int KIND>
 __global__ __launch_bounds__(WG_THREADS) void collective_kernel(KArgs a) {
   warm_kernel_args();
-  if constexpr (KIND == K_ONESHOT && PROTO != PROTO_SIMPLE) {
-    if (a.colocate) {
-      colocated_oneshot<DT, PROTO>(a);
-      return;
-    }
-  }
   if constexpr (never_waits<PROTO, KIND>()) {
     // When the grid covers every ticket at once, tasks that never wait need
     // neither the counter nor its re-arming: workgroup b runs its own
@@ -1402,6 +1419,22 @@ static KernelFn pick_proto(int proto, int kind) {
   }
 }
 
+// LL tiles of one 4 KiB pass take the one-pass kernel, larger ones (up to
+// LL_COLOCATED_PASSES passes) the many-pass kernel.
+static KernelFn pick_colocated(int dtype, int proto, uint64_t tile_bytes) {
+  constexpr int MP = (int)LL_COLOCATED_PASSES;
+  const bool one = tile_bytes <= LL_COLOCATED_TILE;
+  switch (dtype * 3 + proto) {
+    case DT_F32 * 3 + PROTO_LL: return one ? colocated_kernel<DT_F32, PROTO_LL, 1> : colocated_kernel<DT_F32, PROTO_LL, MP>;
+    case DT_F32 * 3 + PROTO_LL128: return colocated_kernel<DT_F32, PROTO_LL128, 1>;
+    case DT_BF16 * 3 + PROTO_LL: return one ? colocated_kernel<DT_BF16, PROTO_LL, 1> : colocated_kernel<DT_BF16, PROTO_LL, MP>;
+    case DT_BF16 * 3 + PROTO_LL128: return colocated_kernel<DT_BF16, PROTO_LL128, 1>;
+    case DT_I32 * 3 + PROTO_LL: return one ? colocated_kernel<DT_I32, PROTO_LL, 1> : colocated_kernel<DT_I32, PROTO_LL, MP>;
+    case DT_I32 * 3 + PROTO_LL128: return colocated_kernel<DT_I32, PROTO_LL128, 1>;
+    default: return nullptr;
+  }
+}
+
 KernelFn pick_kernel(int dtype, int proto, int kind) {
   switch (dtype) {
     case DT_F32: return pick_proto<DT_F32>(proto, kind);
@@ -1492,13 +1525,20 @@ hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uin
                           (a.g.proto == PROTO_SIMPLE && !barrier &&
                            (a.g.kind == K_ONESHOT || a.g.kind == K_RS_DIRECT || a.g.kind == K_AG_DIRECT));
   b.fixed = (waits_free && grid * b.batch >= a.g.ntasks) ? 1u : 0u;
-  // One workgroup per (tile, rank) of a small line-protocol one-shot, when
-  // the budget lets them all be resident; otherwise the ticketed schedule.
+  // One workgroup per (tile, rank) of a small line-protocol one-shot, in a
+  // kernel of its own, when the budget lets them all be resident; otherwise
+  // the ticketed schedule.
   b.colocate = 0;
-  if (a.g.colocated && !a.rearm_errors && a.g.tiles * (uint64_t)a.g.nranks <= cap) {
-    b.colocate = 1;
-    b.batch = 1;
-    grid = a.g.tiles * (uint64_t)a.g.nranks;
+  if (a.g.colocated && !a.rearm_errors) {
+    KernelFn fc = pick_colocated(a.g.dtype, a.g.proto, a.g.tile * (uint64_t)a.g.esize);
+    uint64_t ccap = fc ? (uint64_t)resident_workgroups(fc, device) : 0;
+    if (max_workgroups) ccap = umin(ccap, umax((uint64_t)max_workgroups, (uint64_t)a.g.nranks));
+    if (fc && a.g.tiles * (uint64_t)a.g.nranks <= ccap) {
+      f = fc;
+      b.colocate = 1;
+      b.batch = 1;
+      grid = a.g.tiles * (uint64_t)a.g.nranks;
+    }
   }
   // One-shot out of place folds every term of a pass at once while its N
   // inputs are small; beyond that the same fold ran slower than one term at

@@ -45,9 +45,11 @@ constexpr uint64_t COLOCATED_WORKGROUPS = 64;
 // LL's colocated workgroups each run one pass (one 4 KiB tile), so more of
 // them fit the same latency: up to this many.
 constexpr uint64_t COLOCATED_WORKGROUPS_LL = 256;
-// A colocated LL tile is one pass of a workgroup (4 words per thread), so its
-// send loads the whole tile with the call's first round trip.
+// A colocated LL tile is whole passes of a workgroup (4 words per thread,
+// 4 KiB), at most LL_COLOCATED_PASSES of them; its send loads the whole tile
+// with the call's first round trip.
 constexpr uint64_t LL_COLOCATED_TILE = 4096;
+constexpr uint64_t LL_COLOCATED_PASSES = 8;
 constexpr uint64_t LL128_ALIGN = 240;       // 2 lines: a multiple of 16 bytes and of 120 bytes
 
 inline int esize_of(int dtype) { return dtype == DT_BF16 ? 2 : 4; }
@@ -247,19 +249,28 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
   // Small one-shot calls over the line protocols run one workgroup per
   // (tile, rank) when they fit COLOCATED_WORKGROUPS workgroups; LL128 tiles
   // grow to fit (up to 16 wave passes: the waves of a workgroup then share
-  // the tile's lines), LL tiles do not (an LL workgroup walks a larger tile
-  // in passes one after another).  Measured at N=8 bf16, us per call in a
-  // HIP graph (ticketed -> one workgroup per tile and rank): LL 10 KiB
-  // 9.83 -> 9.35 (6.0 once the LL tile became one pass with its own send
-  // and receive); LL128 10 KiB 11.93 -> 10.96, 80 KiB 16.6 -> 12.4; LL
-  // 80 KiB with tiles grown to fit: 14.3 -> 20.9, so it stays ticketed.
+  // the tile's lines), LL tiles grow in whole 4 KiB passes (up to 8; the
+  // send loads them all at once, the receive walks them in turn).  Measured
+  // at N=8 bf16, us per call in a HIP graph (ticketed -> one workgroup per
+  // tile and rank): LL 10 KiB 9.83 -> 9.35 (6.0 once the LL workgroup got
+  // its own send and receive); LL128 10 KiB 11.93 -> 10.96, 80 KiB 16.6 ->
+  // 12.4.
   bool colocated = false;
   if (lines && g.kind == K_ONESHOT && !tune.line_tile_bytes && rank_bytes) {
     const uint64_t max_tiles = (proto == PROTO_LL ? COLOCATED_WORKGROUPS_LL : COLOCATED_WORKGROUPS) / n;
     const uint64_t need = cdiv(cdiv(rank_bytes, max_tiles), LL128_TILE_UNIT) * LL128_TILE_UNIT;
-    if (cdiv(rank_bytes, tile_b) <= max_tiles && (proto == PROTO_LL128 || tile_b <= LL_COLOCATED_TILE))
+    if (proto == PROTO_LL) {
+      const uint64_t need_ll = cdiv(cdiv(rank_bytes, max_tiles), LL_COLOCATED_TILE) * LL_COLOCATED_TILE;
+      if (need_ll <= LL_COLOCATED_PASSES * LL_COLOCATED_TILE) {
+        tile_b = umax(need_ll, LL_COLOCATED_TILE);
+        colocated = true;
+      }
+    } else if (cdiv(rank_bytes, tile_b) <= max_tiles) {
       colocated = true;
-    else if (proto == PROTO_LL128 && need <= 16 * LL128_TILE_UNIT) { tile_b = need; colocated = true; }
+    } else if (need <= 16 * LL128_TILE_UNIT) {
+      tile_b = need;
+      colocated = true;
+    }
   }
   // Tasks that never wait (Simple one-shot out of place, direct RS and AG)
   // skip the ticket counter when one grid covers them all.  A call that

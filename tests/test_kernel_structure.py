@@ -35,9 +35,16 @@ def _kernels(text):
     return list(re.finditer(r"^(_ZN2ar17collective_kernel\w+):(.*?)^\.Lfunc_end", text, re.S | re.M))
 
 
+def _colocated_kernels(text):
+    return list(re.finditer(r"^(_ZN2ar16colocated_kernel\w+):(.*?)^\.Lfunc_end", text, re.S | re.M))
+
+
 def test_every_kernel_compiled(asm):
     # 3 payload types x (3 protocols x 5 schedules + the Simple tree + 1 copy kernel)
     assert len(_kernels(asm)) == 51
+    # small one-shots, one workgroup per (tile, rank): 3 payload types x
+    # {LL one pass, LL up to 8 passes, LL128}
+    assert len(_colocated_kernels(asm)) == 9
 
 
 def _label_of(line):
@@ -188,9 +195,9 @@ def test_the_order_check_sees_a_payload_load_over_a_flag():
 
 def test_payload_loads_wait_for_their_flags(asm):
     checked = 0
-    for m in _kernels(asm):
+    for m in _kernels(asm) + _colocated_kernels(asm):
         name = m.group(1)
-        proto = int(re.match(r"_ZN2ar17collective_kernelILi\dELi(\d)E", name).group(1))
+        proto = int(re.match(r"_ZN2ar\d+\w+?_kernelILi\dELi(\d)E", name).group(1))
         if proto == 1:  # LL
             continue
         n, bad = _payload_over_flag(m.group(2))
