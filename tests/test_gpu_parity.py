@@ -38,6 +38,35 @@ def _say(*what):
     print("CASE", *what, flush=True, file=sys.stderr)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("n", [2, 8])
+def test_many_pass_colocated_ll_one_shot(dt, n):
+    # LL one-shots up to 8 passes (32 KiB) per workgroup: tiles of 5 and 8
+    # passes, a ragged tail, out of place and in place, all without the
+    # ticket counter and equal to the oracle.
+    es = 2 if dt == "bf16" else 4
+    tiles = 256 // n
+    c = Comm(n, tiles * 32768, tiles * 32768 * 4)
+    for passes, tail in ((5, 0), (8, 0), (5, 3)):
+        count = tiles * passes * 4096 // es - tail
+        host = inputs.rank_inputs(n, count, dt, _dist(dt), seed=passes + tail, cfg=82)
+        want = C.allreduce(host, dt, "oneshot")
+        send = [to_dev(x, dt) for x in host]
+        recv = [empty(count, dt) for _ in range(n)]
+        _say("coloc many-pass", dt, n, passes, count)
+        c.allreduce(send, recv, algo="oneshot", proto="ll")
+        torch.cuda.synchronize()
+        assert c.debug_calls(1)[0]["counter_free"] == 1, (dt, n, passes, count)
+        for r in range(n):
+            assert_same(to_host(recv[r], dt), want[r], f"coloc many-pass {dt} N={n} count={count} rank {r}")
+        c.allreduce(send, None, algo="oneshot", proto="ll")
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_same(to_host(send[r], dt), want[r], f"coloc many-pass in place {dt} N={n} count={count} rank {r}")
+    assert c.check()[0] == "AR_OK"
+    c.close()
+
+
 def run_allreduce(n, count, dt, algo, proto, chunk=0, seed=0, in_place=False, dist=None):
     host = inputs.rank_inputs(n, count, dt, dist or _dist(dt), seed=seed, cfg=100 + n)
     send = [to_dev(x, dt) for x in host]

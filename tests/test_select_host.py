@@ -59,8 +59,8 @@ def test_choice_is_the_measured_fastest_at_every_swept_point():
         worst = max(worst, ratios[-1])
     # A two-parameter line per cache band: on the committed sweep 98 % of
     # the 264 points pick the fastest and all are within 5 % (worst miss
-    # 1.03x, a 2 MiB reduce-scatter at N=2 whose eager time is the host's
-    # launch rate for both candidates).
+    # 1.03x, an N=2 bf16 reduce-scatter at 512 MiB where the direct and the
+    # ring schedule tie).
     assert worst <= 1.10, f"auto choice up to {worst:.2f}x the fastest measured"
     assert sum(r <= 1.05 for r in ratios) >= 0.97 * len(ratios)
 
@@ -132,6 +132,6 @@ def test_choice_generalizes_to_sizes_left_out_of_the_fit():
     within = sum(r <= 1.10 for r in ratios) / len(ratios)
     # Measured on the committed sweep (126 held-out points): the held-out
     # choice is the fastest at 99.2 % of them and every one is within 5 %
-    # (worst 1.03x, the same host-bound 2 MiB reduce-scatter point).
+    # (worst 1.004x).
     assert len(ratios) >= 100
     assert exact >= 0.90 and within >= 0.95 and ratios[-1] <= 1.3, (exact, within, ratios[-5:])
