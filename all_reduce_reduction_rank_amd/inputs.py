@@ -13,8 +13,9 @@ so every rank's buffer is reproducible on its own.  Distributions:
 ``int20``       int32 uniform on [-2**20, 2**20]
 ``ones``        every element 1
 
-A bf16 buffer holds the fp32 draws truncated to their top 16 bits (which are
-exact bf16 values); it is returned as the uint16 bit patterns.
+A bf16 buffer holds the fp32 draws converted by torch (nearest bf16, ties to
+even: a library conversion, not arithmetic of this module); it is returned
+as the uint16 bit patterns.
 """
 
 import numpy as np
@@ -47,8 +48,10 @@ def _draw(rng, size, dt, dist):
         raise ValueError(f"unknown distribution {dist!r}")
     if dt == "f32":
         return f
-    if dt == "bf16":
-        return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    if dt == "bf16":  # torch's conversion: nearest bf16, ties to even
+        import torch
+
+        return torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     if dt == "i32":
         return np.rint(f * 1024).astype(np.int32)
     raise ValueError(f"unknown payload type {dt!r}")
@@ -90,8 +93,8 @@ def device_rank_inputs(nranks: int, count: int, dt: str, dist: str, seed: int = 
             raise ValueError(f"unknown distribution {dist!r}")
         if dt == "f32":
             out.append(t)
-        elif dt == "bf16":  # top 16 bits of the fp32 draws, as for the host generator
-            out.append((t.view(torch.int32) >> 16).to(torch.int16).view(torch.bfloat16))
+        elif dt == "bf16":  # nearest bf16, ties to even, as for the host generator
+            out.append(t.to(torch.bfloat16))
         else:
             out.append(torch.round(t * 1024).to(torch.int32))
     return out

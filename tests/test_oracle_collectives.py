@@ -343,3 +343,22 @@ def test_tree_is_not_defined_for_reduce_scatter_or_all_gather(n):
         C.reduce_scatter(x, "f32", "tree")
     with pytest.raises(ValueError):
         C.allgather(x, "f32", "tree")
+
+
+def test_bf16_inputs_are_the_nearest_bf16_of_the_fp32_draws():
+    # The seeded bf16 buffers are the same draws as the fp32 ones, rounded to
+    # the nearest bf16 (ties to even).  Checked against the definition: the
+    # chosen value is a bf16 (low 16 bits zero as fp32) and no other bf16 is
+    # closer; on a tie its last mantissa bit is even.
+    for dist in ("uniform", "normal", "normal_1e-3", "int20"):
+        b = inputs.rank_inputs(2, 20000, "bf16", dist, seed=7, cfg=3)[1]
+        f = inputs.rank_inputs(2, 20000, "f32", dist, seed=7, cfg=3)[1].astype(np.float64)
+        def as_f64(bits):  # bf16 bit patterns (wrapped to 16 bits) as float64; NaN patterns -> inf
+            x = ((bits.astype(np.uint32) & 0xFFFF) << 16).view(np.float32).astype(np.float64)
+            return np.where(np.isnan(x), np.inf, x)
+        v = as_f64(b)
+        up, down = as_f64(b.astype(np.int64) + 1), as_f64(b.astype(np.int64) - 1)
+        err = np.abs(v - f)
+        assert np.all(err <= np.abs(up - f)) and np.all(err <= np.abs(down - f)), dist
+        tie = (err == np.abs(up - f)) | (err == np.abs(down - f))
+        assert np.all((b[tie] & 1) == 0), dist
