@@ -1190,6 +1190,154 @@ __device__ __forceinline__ void colocated_ll(const KArgs& a, const Task& k, uint
   }
 }
 
+// LL128 counterpart of colocated_ll.  A workgroup pass is 128 lines: line
+// L = 128 p + 32 wave + 8 u + group, lane q of the group owning bytes
+// [16q, 16q+16) of it (lane 7: 8 payload bytes and the flag word).  `pre`
+// holds the rank's payload pieces of every pass, loaded with the epoch.
+// Send: every line whole with its flag word 0, wait until they are visible,
+// then the flag words, and wait for those too (R15's order).  Receive, pass
+// by pass: every peer's flag words at once (a poll reloads them all), then
+// every peer's payload pieces at once, summed in rank order with `pre` as
+// the rank's own term.  Bounded buffer accesses stand in for tail branches;
+// per-element loads and stores keep ragged and 2-byte-aligned bf16 tails
+// exact.
+constexpr int U_C128 = 4;  // line groups of a wave per pass
+template <int DT>
+__device__ __forceinline__ uint4 load_piece_bounded(Rsrc src, uint32_t off, bool full) {
+  // `full`: 16 bytes (lanes 0..6), else 8 (lane 7); past the tile: zeros.
+  const uint32_t hi = full ? off + 8 : 0x7ffffff0u;
+  if constexpr (Elem<DT>::size == 2) {
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t o = (d < 2 ? off + 4 * d : hi + 4 * (d - 2));
+      w[d] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(src, o, 0, 0) |
+             ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(src, o + 2, 0, 0) << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    return make_uint4(__builtin_amdgcn_raw_buffer_load_b32(src, off, 0, 0),
+                      __builtin_amdgcn_raw_buffer_load_b32(src, off + 4, 0, 0),
+                      __builtin_amdgcn_raw_buffer_load_b32(src, hi, 0, 0),
+                      __builtin_amdgcn_raw_buffer_load_b32(src, hi + 4, 0, 0));
+  }
+}
+template <int DT>
+__device__ __forceinline__ void store_piece_bounded(Rsrc dst, uint32_t off, bool full, const uint4& v) {
+  const uint32_t hi = full ? off + 8 : 0x7ffffff0u;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t o = d < 2 ? off + 4 * d : hi + 4 * (d - 2);
+    if constexpr (Elem<DT>::size == 2) {
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)w[d], dst, o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w[d] >> 16), dst, o + 2, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(w[d], dst, o, 0, 0);
+    }
+  }
+}
+
+template <int DT, int PASSES>
+__device__ __forceinline__ void colocated_ll128(const KArgs& a, const Task& k, uint64_t epoch,
+                                                const uint4 (&pre)[PASSES][U_C128], int passes, uint64_t nbytes,
+                                                uint32_t& counted) {
+  const int n = a.g.nranks;
+  const int r = k.rank;
+  const uint32_t nlines = (uint32_t)cdiv(nbytes, LL128_DATA);
+  const uint64_t flag = epoch + 1;
+  const uint32_t wave = uniform(threadIdx.x / 64), lane = threadIdx.x % 64, q = lane % 8, grp = lane / 8;
+  const bool full = q < 7;
+  auto line_of = [&](int p, int u) { return (uint32_t)(p * 128) + wave * 32 + (uint32_t)u * 8 + grp; };
+  const uint64_t slot_stride = uniform64(a.g.slot_lines * a.g.line_bytes);
+  const char* tile_lines = a.lines + uniform64(k.tile * a.g.tile_lines * a.g.line_bytes);
+  const Rsrc own = make_rsrc(tile_lines + (uint64_t)r * slot_stride, nlines * LL128_LINE);
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p)  // whole lines, flag word 0; past the tile: dropped
+#pragma unroll
+    for (int u = 0; u < U_C128; ++u)
+      cst16(own, line_of(p, u) * LL128_LINE + 16 * q,
+            full ? pre[p][u] : make_uint4(pre[p][u].x, pre[p][u].y, 0, 0));
+  wait_mem();
+  if (!withheld(a, 0, r)) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+      for (int u = 0; u < U_C128; ++u)  // lane 7 of each group: its line's flag word
+        cst8(own, q == 7 ? line_of(p, u) * LL128_LINE + LL128_DATA : 0x7ffffff0u,
+             make_uint2((uint32_t)flag, (uint32_t)(flag >> 32)));
+  }
+  wait_mem();
+  if (blockIdx.x == 0) counted = ld_u32(&a.ctl->done);
+  const Rsrc out = make_rsrc(a.out[r] + k.lo * (uint64_t)Elem<DT>::size, (uint32_t)nbytes);
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    if (p >= passes) break;
+    uint2 fl[MAX_RANKS][U_C128];
+    auto load_flags = [&]() {
+#pragma unroll
+      for (int i = 0; i < MAX_RANKS; ++i) {
+        if (i >= n) break;
+        if (i == r) continue;
+        const Rsrc li = make_rsrc(tile_lines + (uint64_t)i * slot_stride, nlines * LL128_LINE);
+#pragma unroll
+        for (int u = 0; u < U_C128; ++u) fl[i][u] = cld8(li, line_of(p, u) * LL128_LINE + LL128_DATA);
+      }
+    };
+    auto all_seen = [&]() {
+      bool ok = true;
+#pragma unroll
+      for (int i = 0; i < MAX_RANKS; ++i) {
+        if (i >= n) break;
+        if (i == r) continue;
+#pragma unroll
+        for (int u = 0; u < U_C128; ++u)
+          ok = ok && (line_of(p, u) >= nlines || (((uint64_t)fl[i][u].y << 32) | fl[i][u].x) == flag);
+      }
+      return ok;
+    };
+    load_flags();
+    if (!all_seen()) {
+      PollClock clock;
+      uint32_t level = 0;
+      while (true) {
+        poll_sleep(level);
+        load_flags();
+        if (all_seen()) break;
+        const int st = clock.tick(a);
+        if (st == POLL_ABORTED) { note_blocked(a.ctl, 1, r); return; }
+        if (st == POLL_TIMED_OUT) { raise_timeout(a.ctl, 1, r); return; }
+      }
+    }
+    // Flags seen: the payload pieces, at device scope, all peers at once.
+    uint4 pv[MAX_RANKS][U_C128];
+#pragma unroll
+    for (int i = 0; i < MAX_RANKS; ++i) {
+      if (i >= n) break;
+      if (i == r) continue;
+      const Rsrc li = make_rsrc(tile_lines + (uint64_t)i * slot_stride, nlines * LL128_LINE);
+#pragma unroll
+      for (int u = 0; u < U_C128; ++u) pv[i][u] = cld16(li, line_of(p, u) * LL128_LINE + 16 * q);
+    }
+#pragma unroll
+    for (int u = 0; u < U_C128; ++u) {
+      uint4 res = pre[p][u];
+      if (n > 1) {
+        Vec<DT> acc;
+#pragma unroll
+        for (int i = 0; i < MAX_RANKS; ++i) {
+          if (i >= n) break;
+          const Vec<DT> x = Vec<DT>::widen(i == r ? pre[p][u] : pv[i][u]);
+          if (i == 0) acc = x; else acc.add(x);
+        }
+        res = acc.narrow();
+      }
+      // Lane 7's upper half (the peers' flag words) is never stored.
+      store_piece_bounded<DT>(out, line_of(p, u) * LL128_DATA + 16 * q, full, res);
+    }
+  }
+}
+
 // Small one-shot calls over LL / LL128 (g.colocated): workgroup b is rank
 // b % N's program on tile b / N.  It puts its input tile on the wire, then
 // gathers every rank's lines of the tile and sums them: the send and the
@@ -1227,11 +1375,12 @@ __device__ __forceinline__ void colocated_oneshot(const KArgs& a) {
   // one-pass tile in the 8-pass kernel took 2 us longer), hence a one-pass
   // kernel for one-pass tiles.
   uint32_t pre[PASSES][U_LL];
+  uint4 pre128[PASSES][U_C128];
   int passes = 0;
+  const Rsrc src = make_rsrc(a.in[r] + k.lo * (uint64_t)es, (uint32_t)nbytes);
   if constexpr (PROTO == PROTO_LL) {
     static_assert(U_LL * WG_THREADS * 4 == LL_COLOCATED_TILE, "a colocated LL pass is 4 KiB");
     passes = (int)cdiv(nbytes, LL_COLOCATED_TILE);  // at most PASSES (launch_collective)
-    const Rsrc src = make_rsrc(a.in[r] + k.lo * (uint64_t)es, (uint32_t)nbytes);
 #pragma unroll
     for (int p = 0; p < PASSES; ++p)
 #pragma unroll
@@ -1242,6 +1391,17 @@ __device__ __forceinline__ void colocated_oneshot(const KArgs& a) {
                       ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(src, off + 2, 0, 0) << 16);
         else
           pre[p][u] = __builtin_amdgcn_raw_buffer_load_b32(src, off, 0, 0);
+      }
+  } else {
+    static_assert(4 * U_C128 * 8 * LL128_DATA == LL128_COLOCATED_PASS, "a colocated LL128 pass is 128 lines");
+    passes = (int)cdiv(nbytes, LL128_COLOCATED_PASS);  // at most PASSES (launch_collective)
+    const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+      for (int u = 0; u < U_C128; ++u) {
+        const uint32_t line = (uint32_t)(p * 128) + wave * 32 + (uint32_t)u * 8 + lane / 8;
+        pre128[p][u] = load_piece_bounded<DT>(src, line * LL128_DATA + 16 * (lane % 8), lane % 8 < 7);
       }
   }
   if (threadIdx.x == 0) {
@@ -1261,12 +1421,7 @@ __device__ __forceinline__ void colocated_oneshot(const KArgs& a) {
     if constexpr (PROTO == PROTO_LL) {
       colocated_ll<DT, PASSES>(a, k, epoch, pre, passes, nbytes, counted);
     } else {
-      k.phase = PH_SEND;
-      run_task<DT, PROTO, K_ONESHOT>(a, k, epoch);
-      __syncthreads();
-      if (blockIdx.x == 0) counted = ld_u32(&a.ctl->done);
-      k.phase = PH_RECV_FOLD;
-      run_task<DT, PROTO, K_ONESHOT>(a, k, epoch);
+      colocated_ll128<DT, PASSES>(a, k, epoch, pre128, passes, nbytes, counted);
     }
     finished = 2;
   } else if (blockIdx.x == 0) {
@@ -1419,18 +1574,21 @@ static KernelFn pick_proto(int proto, int kind) {
   }
 }
 
-// LL tiles of one 4 KiB pass take the one-pass kernel, larger ones (up to
-// LL_COLOCATED_PASSES passes) the many-pass kernel.
+// Tiles of one pass take the one-pass kernels, larger ones (up to
+// LL_COLOCATED_PASSES / LL128_COLOCATED_PASSES passes) the many-pass ones.
 static KernelFn pick_colocated(int dtype, int proto, uint64_t tile_bytes) {
-  constexpr int MP = (int)LL_COLOCATED_PASSES;
-  const bool one = tile_bytes <= LL_COLOCATED_TILE;
+  constexpr int MP = (int)LL_COLOCATED_PASSES, MP128 = (int)LL128_COLOCATED_PASSES;
+  const bool one = tile_bytes <= (proto == PROTO_LL ? LL_COLOCATED_TILE : LL128_COLOCATED_PASS);
   switch (dtype * 3 + proto) {
     case DT_F32 * 3 + PROTO_LL: return one ? colocated_kernel<DT_F32, PROTO_LL, 1> : colocated_kernel<DT_F32, PROTO_LL, MP>;
-    case DT_F32 * 3 + PROTO_LL128: return colocated_kernel<DT_F32, PROTO_LL128, 1>;
+    case DT_F32 * 3 + PROTO_LL128:
+      return one ? colocated_kernel<DT_F32, PROTO_LL128, 1> : colocated_kernel<DT_F32, PROTO_LL128, MP128>;
     case DT_BF16 * 3 + PROTO_LL: return one ? colocated_kernel<DT_BF16, PROTO_LL, 1> : colocated_kernel<DT_BF16, PROTO_LL, MP>;
-    case DT_BF16 * 3 + PROTO_LL128: return colocated_kernel<DT_BF16, PROTO_LL128, 1>;
+    case DT_BF16 * 3 + PROTO_LL128:
+      return one ? colocated_kernel<DT_BF16, PROTO_LL128, 1> : colocated_kernel<DT_BF16, PROTO_LL128, MP128>;
     case DT_I32 * 3 + PROTO_LL: return one ? colocated_kernel<DT_I32, PROTO_LL, 1> : colocated_kernel<DT_I32, PROTO_LL, MP>;
-    case DT_I32 * 3 + PROTO_LL128: return colocated_kernel<DT_I32, PROTO_LL128, 1>;
+    case DT_I32 * 3 + PROTO_LL128:
+      return one ? colocated_kernel<DT_I32, PROTO_LL128, 1> : colocated_kernel<DT_I32, PROTO_LL128, MP128>;
     default: return nullptr;
   }
 }

@@ -40,16 +40,19 @@ constexpr uint64_t LL128_TILE_UNIT = 3840;  // 32 lines of 120 payload bytes: on
 // A one-shot call over LL or LL128 whose tiles fit this many workgroups (one
 // per tile and rank) runs each rank's send and receive of a tile in one
 // workgroup, with no ticket counter: the N workgroups of a tile wait on each
-// other, so the grid is kept small enough to be resident at once.
-constexpr uint64_t COLOCATED_WORKGROUPS = 64;
-// LL's colocated workgroups each run one pass (one 4 KiB tile), so more of
-// them fit the same latency: up to this many.
-constexpr uint64_t COLOCATED_WORKGROUPS_LL = 256;
+// other, so the grid is kept well below what is resident at once (a third of
+// it at three workgroups per CU; launch_collective checks).  Their own send
+// and receive keep the latency from growing with the grid.
+constexpr uint64_t COLOCATED_WORKGROUPS = 256;
 // A colocated LL tile is whole passes of a workgroup (4 words per thread,
 // 4 KiB), at most LL_COLOCATED_PASSES of them; its send loads the whole tile
 // with the call's first round trip.
 constexpr uint64_t LL_COLOCATED_TILE = 4096;
 constexpr uint64_t LL_COLOCATED_PASSES = 8;
+// A colocated LL128 tile is whole workgroup passes of 128 lines (4 waves x
+// 32 lines: 15 KiB of payload), at most LL128_COLOCATED_PASSES of them.
+constexpr uint64_t LL128_COLOCATED_PASS = 4 * 3840;
+constexpr uint64_t LL128_COLOCATED_PASSES = 2;
 constexpr uint64_t LL128_ALIGN = 240;       // 2 lines: a multiple of 16 bytes and of 120 bytes
 
 inline int esize_of(int dtype) { return dtype == DT_BF16 ? 2 : 4; }
@@ -247,28 +250,20 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
     tile_b = proto == PROTO_LL128 ? LL128_TILE_UNIT * clampu(tune.line_tile_bytes / LL128_TILE_UNIT, 1, 64)
                                   : clampu(tune.line_tile_bytes / 16 * 16, 1024, 256 * 1024);
   // Small one-shot calls over the line protocols run one workgroup per
-  // (tile, rank) when they fit COLOCATED_WORKGROUPS workgroups; LL128 tiles
-  // grow to fit (up to 16 wave passes: the waves of a workgroup then share
-  // the tile's lines), LL tiles grow in whole 4 KiB passes (up to 8; the
-  // send loads them all at once, the receive walks them in turn).  Measured
-  // at N=8 bf16, us per call in a HIP graph (ticketed -> one workgroup per
-  // tile and rank): LL 10 KiB 9.83 -> 9.35 (6.0 once the LL workgroup got
-  // its own send and receive); LL128 10 KiB 11.93 -> 10.96, 80 KiB 16.6 ->
-  // 12.4.
+  // (tile, rank) when they fit COLOCATED_WORKGROUPS workgroups.  Tiles are
+  // whole workgroup passes (LL: 4 KiB, up to 8; LL128: 128 lines, up to 2):
+  // the send loads the whole tile at once, the receive walks the passes in
+  // turn.  Graph time at N=8, ticketed -> colocated: LL bf16 10 KiB 9.8 ->
+  // 6.0 us, 640 KiB 50.7 -> 31.9; LL128 bf16 640 KiB 35.6 -> 24.0, fp32
+  // 128 KiB 15.8 -> 8.8.
   bool colocated = false;
   if (lines && g.kind == K_ONESHOT && !tune.line_tile_bytes && rank_bytes) {
-    const uint64_t max_tiles = (proto == PROTO_LL ? COLOCATED_WORKGROUPS_LL : COLOCATED_WORKGROUPS) / n;
-    const uint64_t need = cdiv(cdiv(rank_bytes, max_tiles), LL128_TILE_UNIT) * LL128_TILE_UNIT;
-    if (proto == PROTO_LL) {
-      const uint64_t need_ll = cdiv(cdiv(rank_bytes, max_tiles), LL_COLOCATED_TILE) * LL_COLOCATED_TILE;
-      if (need_ll <= LL_COLOCATED_PASSES * LL_COLOCATED_TILE) {
-        tile_b = umax(need_ll, LL_COLOCATED_TILE);
-        colocated = true;
-      }
-    } else if (cdiv(rank_bytes, tile_b) <= max_tiles) {
-      colocated = true;
-    } else if (need <= 16 * LL128_TILE_UNIT) {
-      tile_b = need;
+    const uint64_t max_tiles = COLOCATED_WORKGROUPS / n;
+    const uint64_t pass = proto == PROTO_LL ? LL_COLOCATED_TILE : LL128_COLOCATED_PASS;
+    const uint64_t passes = proto == PROTO_LL ? LL_COLOCATED_PASSES : LL128_COLOCATED_PASSES;
+    const uint64_t need = cdiv(cdiv(rank_bytes, max_tiles), pass) * pass;
+    if (need <= passes * pass) {
+      tile_b = umax(need, pass);
       colocated = true;
     }
   }
@@ -378,8 +373,7 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
         g.per_group = 2 * n;
         g.groups = g.tiles ? g.tiles + lag : 0;
         g.nslots = n;
-        g.colocated =
-            colocated && g.tiles * n <= (proto == PROTO_LL ? COLOCATED_WORKGROUPS_LL : COLOCATED_WORKGROUPS) ? 1 : 0;
+        g.colocated = colocated && g.tiles * n <= COLOCATED_WORKGROUPS ? 1 : 0;
       }
       break;
     case K_TWOSHOT:

@@ -38,31 +38,34 @@ def _say(*what):
     print("CASE", *what, flush=True, file=sys.stderr)
 
 
+@pytest.mark.parametrize("proto", ["ll", "ll128"])
 @pytest.mark.parametrize("dt", ["f32", "bf16", "i32"])
 @pytest.mark.parametrize("n", [2, 8])
-def test_many_pass_colocated_ll_one_shot(dt, n):
-    # LL one-shots up to 8 passes (32 KiB) per workgroup: tiles of 5 and 8
-    # passes, a ragged tail, out of place and in place, all without the
-    # ticket counter and equal to the oracle.
+def test_many_pass_colocated_line_one_shot(dt, n, proto):
+    # Line one-shots of several passes per workgroup (LL: 4 KiB passes, up
+    # to 8; LL128: 128-line passes of 15 KiB, up to 2), a ragged tail, out
+    # of place and in place, all without the ticket counter and equal to the
+    # oracle.
     es = 2 if dt == "bf16" else 4
     tiles = 256 // n
-    c = Comm(n, tiles * 32768, tiles * 32768 * 4)
-    for passes, tail in ((5, 0), (8, 0), (5, 3)):
-        count = tiles * passes * 4096 // es - tail
+    pass_bytes, cases = (4096, ((5, 0), (8, 0), (5, 3))) if proto == "ll" else (15360, ((2, 0), (2, 3)))
+    c = Comm(n, tiles * pass_bytes * 8, tiles * pass_bytes * 8 * 4)
+    for passes, tail in cases:
+        count = tiles * passes * pass_bytes // es - tail
         host = inputs.rank_inputs(n, count, dt, _dist(dt), seed=passes + tail, cfg=82)
         want = C.allreduce(host, dt, "oneshot")
         send = [to_dev(x, dt) for x in host]
         recv = [empty(count, dt) for _ in range(n)]
-        _say("coloc many-pass", dt, n, passes, count)
-        c.allreduce(send, recv, algo="oneshot", proto="ll")
+        _say("coloc many-pass", proto, dt, n, passes, count)
+        c.allreduce(send, recv, algo="oneshot", proto=proto)
         torch.cuda.synchronize()
         assert c.debug_calls(1)[0]["counter_free"] == 1, (dt, n, passes, count)
         for r in range(n):
-            assert_same(to_host(recv[r], dt), want[r], f"coloc many-pass {dt} N={n} count={count} rank {r}")
-        c.allreduce(send, None, algo="oneshot", proto="ll")
+            assert_same(to_host(recv[r], dt), want[r], f"coloc many-pass {proto} {dt} N={n} count={count} rank {r}")
+        c.allreduce(send, None, algo="oneshot", proto=proto)
         torch.cuda.synchronize()
         for r in range(n):
-            assert_same(to_host(send[r], dt), want[r], f"coloc many-pass in place {dt} N={n} count={count} rank {r}")
+            assert_same(to_host(send[r], dt), want[r], f"coloc many-pass in place {proto} {dt} N={n} count={count} rank {r}")
     assert c.check()[0] == "AR_OK"
     c.close()
 
@@ -548,10 +551,12 @@ def test_small_line_one_shot_runs_one_workgroup_per_tile_and_rank(dt, n, proto):
         torch.cuda.synchronize()
         for r in range(n):
             assert_same(to_host(send[r], dt), want[r], f"coloc in place {proto} {dt} N={n} count={count} rank {r}")
+    # A budget below the grid (20480 elements: at least 3 tiles per rank for
+    # either protocol, so more than max(budget, N) workgroups).
     c.set_max_workgroups(n - 1 if n > 2 else 1)
-    host = inputs.rank_inputs(n, 5120, dt, _dist(dt), seed=1, cfg=81)
+    host = inputs.rank_inputs(n, 20480, dt, _dist(dt), seed=1, cfg=81)
     send = [to_dev(x, dt) for x in host]
-    recv = [empty(5120, dt) for _ in range(n)]
+    recv = [empty(20480, dt) for _ in range(n)]
     c.allreduce(send, recv, algo="oneshot", proto=proto)
     torch.cuda.synchronize()
     assert c.debug_calls(1)[0]["counter_free"] == 0

@@ -43,8 +43,8 @@ def test_every_kernel_compiled(asm):
     # 3 payload types x (3 protocols x 5 schedules + the Simple tree + 1 copy kernel)
     assert len(_kernels(asm)) == 51
     # small one-shots, one workgroup per (tile, rank): 3 payload types x
-    # {LL one pass, LL up to 8 passes, LL128}
-    assert len(_colocated_kernels(asm)) == 9
+    # {LL one pass, LL up to 8 passes, LL128 one pass, LL128 up to 2 passes}
+    assert len(_colocated_kernels(asm)) == 12
 
 
 def _label_of(line):
