@@ -1202,11 +1202,13 @@ __device__ __forceinline__ void colocated_ll(const KArgs& a, const Task& k, uint
 // per-element loads and stores keep ragged and 2-byte-aligned bf16 tails
 // exact.
 constexpr int U_C128 = 4;  // line groups of a wave per pass
-template <int DT>
+// WORDS: every tile holds whole words (rank buffers are 16-byte aligned),
+// so bf16 loads and stores go a word at a time too (the host checks).
+template <int DT, bool WORDS = false>
 __device__ __forceinline__ uint4 load_piece_bounded(Rsrc src, uint32_t off, bool full) {
   // `full`: 16 bytes (lanes 0..6), else 8 (lane 7); past the tile: zeros.
   const uint32_t hi = full ? off + 8 : 0x7ffffff0u;
-  if constexpr (Elem<DT>::size == 2) {
+  if constexpr (Elem<DT>::size == 2 && !WORDS) {
     uint32_t w[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -1222,14 +1224,14 @@ __device__ __forceinline__ uint4 load_piece_bounded(Rsrc src, uint32_t off, bool
                       __builtin_amdgcn_raw_buffer_load_b32(src, hi + 4, 0, 0));
   }
 }
-template <int DT>
+template <int DT, bool WORDS = false>
 __device__ __forceinline__ void store_piece_bounded(Rsrc dst, uint32_t off, bool full, const uint4& v) {
   const uint32_t hi = full ? off + 8 : 0x7ffffff0u;
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t o = d < 2 ? off + 4 * d : hi + 4 * (d - 2);
-    if constexpr (Elem<DT>::size == 2) {
+    if constexpr (Elem<DT>::size == 2 && !WORDS) {
       __builtin_amdgcn_raw_buffer_store_b16((uint16_t)w[d], dst, o, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w[d] >> 16), dst, o + 2, 0, 0);
     } else {
@@ -1369,8 +1371,9 @@ __device__ __forceinline__ void colocated_oneshot(const KArgs& a) {
   // Bounded buffer loads (bytes past the tile read as 0, with no memory
   // access) need no branch, per lane or per pass: behind a branch, the
   // compiler waited for these loads before the epoch load went out.  bf16
-  // words load as two halves, since a bf16 tile may start on any 2-byte
-  // boundary.  The loads and stores of the PASSES passes are all issued,
+  // words load as two halves, since a bf16 tile may end mid-word (and a
+  // half-covered word would read as zero).  The loads and stores of the
+  // PASSES passes are all issued,
   // those past the tile included (they still cost address-unit time: a
   // one-pass tile in the 8-pass kernel took 2 us longer), hence a one-pass
   // kernel for one-pass tiles.
@@ -1447,6 +1450,237 @@ __device__ __forceinline__ void warm_kernel_args() {
 #pragma unroll
   for (uint32_t i = 0; i < (sizeof(KArgs) + 63) / 64; ++i) x ^= p[16 * i];
   asm volatile("" ::"s"(x));
+}
+
+// Small LL128 two-shots (a.colocate): workgroup b is rank r = b % N on tile
+// t = b / N of every block.  Step 0: r puts its tile t of every other block
+// j on the wire to j (slot r*N + j).  Step 1: r gathers tile t of its own
+// block from every peer (slot i*N + r), sums it in rank order with its own
+// input, keeps it and publishes it (slot N*N + r).  Step 2: r copies tile t
+// of every other block's sum (slot N*N + j) into its output.  Each step
+// covers every pass of the tile before its one wait; the lines are those of
+// colocated_ll128 (whole lines, flag word 0, then the flag words), the
+// waits poll every line of a step at once.  In place is safe: a workgroup
+// reads its input before writing the same bytes, and peers read only lines.
+template <int DT, int PASSES, bool WORDS>
+__device__ __forceinline__ void colocated_twoshot_ll128(const KArgs& a) {
+  __shared__ uint64_t s_epoch;
+  __shared__ uint32_t s_abort;
+  const Geometry& g = a.g;
+  const int n = g.nranks;
+  const int r = (int)uniform(blockIdx.x % (uint32_t)n);
+  const uint64_t t = uniform(blockIdx.x / (uint32_t)n);
+  constexpr int es = Elem<DT>::size;
+  const uint32_t wave = uniform(threadIdx.x / 64), lane = threadIdx.x % 64, q = lane % 8, grp = lane / 8;
+  const bool full = q < 7;
+  auto line_of = [&](int p, int u) { return (uint32_t)(p * 128) + wave * 32 + (uint32_t)u * 8 + grp; };
+  // Tile t of block j: byte offset into a rank buffer, bytes and lines.
+  auto tile_off = [&](int j) {
+    uint64_t lo, hi;
+    tile_range(g, block_len(g, (uint64_t)j), t, &lo, &hi);
+    return (block_lo(g, (uint64_t)j) + lo) * es;
+  };
+  auto tile_bytes = [&](int j) {
+    uint64_t lo, hi;
+    tile_range(g, block_len(g, (uint64_t)j), t, &lo, &hi);
+    return (uint32_t)((hi - lo) * es);
+  };
+  const uint64_t slot_stride = uniform64(g.slot_lines * g.line_bytes);
+  const char* tile_lines = a.lines + uniform64(t * g.tile_lines * g.line_bytes);
+  auto slot = [&](uint64_t sidx, uint32_t nb) {
+    return make_rsrc(tile_lines + sidx * slot_stride, (uint32_t)cdiv(nb, LL128_DATA) * LL128_LINE);
+  };
+  const uint64_t nn = (uint64_t)n * n;
+
+  // Step 0's first pass loads go out with the epoch.
+  uint4 sp[MAX_RANKS][U_C128];
+  auto load_send = [&](int p) {
+#pragma unroll
+    for (int j = 0; j < MAX_RANKS; ++j) {
+      if (j >= n) break;
+      if (j == r) continue;
+      const Rsrc src = make_rsrc(a.in[r] + tile_off(j), tile_bytes(j));
+#pragma unroll
+      for (int u = 0; u < U_C128; ++u) sp[j][u] = load_piece_bounded<DT, WORDS>(src, line_of(p, u) * LL128_DATA + 16 * q, full);
+    }
+  };
+  auto store_send = [&](int p) {
+#pragma unroll
+    for (int j = 0; j < MAX_RANKS; ++j) {
+      if (j >= n) break;
+      if (j == r) continue;
+      const Rsrc dst = slot((uint64_t)r * n + j, tile_bytes(j));
+#pragma unroll
+      for (int u = 0; u < U_C128; ++u)
+        cst16(dst, line_of(p, u) * LL128_LINE + 16 * q, full ? sp[j][u] : make_uint4(sp[j][u].x, sp[j][u].y, 0, 0));
+    }
+  };
+  load_send(0);
+  if (threadIdx.x == 0) {
+    const uint64_t e = __hip_atomic_load(&a.ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t ab = ld_u32(&a.ctl->abort);
+    s_epoch = e;
+    s_abort = ab;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t epoch = uniform64(s_epoch);
+  const bool aborted = uniform(s_abort) != 0;
+  const uint64_t flag = epoch + 1;
+  const uint2 flag2 = make_uint2((uint32_t)flag, (uint32_t)(flag >> 32));
+  uint32_t finished = 0, counted = 0;
+  const int passes = (int)cdiv(g.tile * es, LL128_COLOCATED_PASS);  // at most PASSES (launch_collective)
+  if (!aborted) {
+    // step 0: send
+    store_send(0);
+#pragma unroll
+    for (int p = 1; p < PASSES; ++p) {
+      if (p >= passes) break;
+      load_send(p);
+      store_send(p);
+    }
+    wait_mem();
+    if (!withheld(a, 0, r)) {
+#pragma unroll
+      for (int j = 0; j < MAX_RANKS; ++j) {
+        if (j >= n) break;
+        if (j == r) continue;
+        const Rsrc dst = slot((uint64_t)r * n + j, tile_bytes(j));
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+          for (int u = 0; u < U_C128; ++u)  // lane 7 of each group: its line's flag word
+            cst8(dst, q == 7 ? line_of(p, u) * LL128_LINE + LL128_DATA : 0x7ffffff0u, flag2);
+      }
+    }
+    wait_mem();
+    if (blockIdx.x == 0) counted = ld_u32(&a.ctl->done);
+    // A wait over the flag words of `slots` (slot index per peer, lines of
+    // the tile of that peer's block), every peer and line at once.
+    uint2 fl[MAX_RANKS][U_C128];
+    auto wait_flags = [&](int p, auto slot_of, auto nb_of, int step) -> bool {
+      auto load = [&]() {
+#pragma unroll
+        for (int i = 0; i < MAX_RANKS; ++i) {
+          if (i >= n) break;
+          if (i == r) continue;
+          const Rsrc src = slot(slot_of(i), nb_of(i));
+#pragma unroll
+          for (int u = 0; u < U_C128; ++u) fl[i][u] = cld8(src, line_of(p, u) * LL128_LINE + LL128_DATA);
+        }
+      };
+      auto seen = [&]() {
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < MAX_RANKS; ++i) {
+          if (i >= n) break;
+          if (i == r) continue;
+          const uint32_t nl = (uint32_t)cdiv(nb_of(i), LL128_DATA);
+#pragma unroll
+          for (int u = 0; u < U_C128; ++u)
+            ok = ok && (line_of(p, u) >= nl || (fl[i][u].x == flag2.x && fl[i][u].y == flag2.y));
+        }
+        return ok;
+      };
+      load();
+      if (seen()) return true;
+      PollClock clock;
+      uint32_t level = 0;
+      while (true) {
+        poll_sleep(level);
+        load();
+        if (seen()) return true;
+        const int st = clock.tick(a);
+        if (st == POLL_ABORTED) { note_blocked(a.ctl, step, r); return false; }
+        if (st == POLL_TIMED_OUT) { raise_timeout(a.ctl, step, r); return false; }
+      }
+    };
+    // step 1: gather, sum, keep and publish block r's tile
+    bool ok = true;
+    const uint32_t nb_r = tile_bytes(r);
+    const Rsrc own_in = make_rsrc(a.in[r] + tile_off(r), nb_r);
+    const Rsrc own_out = make_rsrc(a.out[r] + tile_off(r), nb_r);
+    const Rsrc pub = slot(nn + r, nb_r);
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      if (p >= passes || !ok) break;
+      uint4 mine[U_C128];
+#pragma unroll
+      for (int u = 0; u < U_C128; ++u) mine[u] = load_piece_bounded<DT, WORDS>(own_in, line_of(p, u) * LL128_DATA + 16 * q, full);
+      ok = wait_flags(p, [&](int i) { return (uint64_t)i * n + r; }, [&](int) { return nb_r; }, 1);
+      if (!ok) break;
+      uint4 pv[MAX_RANKS][U_C128];
+#pragma unroll
+      for (int i = 0; i < MAX_RANKS; ++i) {
+        if (i >= n) break;
+        if (i == r) continue;
+        const Rsrc src = slot((uint64_t)i * n + r, nb_r);
+#pragma unroll
+        for (int u = 0; u < U_C128; ++u) pv[i][u] = cld16(src, line_of(p, u) * LL128_LINE + 16 * q);
+      }
+#pragma unroll
+      for (int u = 0; u < U_C128; ++u) {
+        Vec<DT> acc;
+#pragma unroll
+        for (int i = 0; i < MAX_RANKS; ++i) {
+          if (i >= n) break;
+          const Vec<DT> x = Vec<DT>::widen(i == r ? mine[u] : pv[i][u]);
+          if (i == 0) acc = x; else acc.add(x);
+        }
+        const uint4 res = acc.narrow();
+        store_piece_bounded<DT, WORDS>(own_out, line_of(p, u) * LL128_DATA + 16 * q, full, res);
+        cst16(pub, line_of(p, u) * LL128_LINE + 16 * q, full ? res : make_uint4(res.x, res.y, 0, 0));
+      }
+    }
+    if (ok) {
+      wait_mem();
+      if (!withheld(a, 1, r)) {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+          for (int u = 0; u < U_C128; ++u)
+            cst8(pub, q == 7 ? line_of(p, u) * LL128_LINE + LL128_DATA : 0x7ffffff0u, flag2);
+      }
+      wait_mem();
+    }
+    // step 2: every other block's sum
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      if (p >= passes || !ok) break;
+      ok = wait_flags(p, [&](int j) { return nn + j; }, [&](int j) { return tile_bytes(j); }, 2);
+      if (!ok) break;
+      uint4 pv[MAX_RANKS][U_C128];
+#pragma unroll
+      for (int j = 0; j < MAX_RANKS; ++j) {
+        if (j >= n) break;
+        if (j == r) continue;
+        const Rsrc src = slot(nn + j, tile_bytes(j));
+#pragma unroll
+        for (int u = 0; u < U_C128; ++u) pv[j][u] = cld16(src, line_of(p, u) * LL128_LINE + 16 * q);
+      }
+#pragma unroll
+      for (int j = 0; j < MAX_RANKS; ++j) {
+        if (j >= n) break;
+        if (j == r) continue;
+        const Rsrc dst = make_rsrc(a.out[r] + tile_off(j), tile_bytes(j));
+#pragma unroll
+        for (int u = 0; u < U_C128; ++u) store_piece_bounded<DT, WORDS>(dst, line_of(p, u) * LL128_DATA + 16 * q, full, pv[j][u]);
+      }
+    }
+    finished = 3;
+  } else if (blockIdx.x == 0) {
+    counted = ld_u32(&a.ctl->done);
+  }
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(&a.ctl->diag[5], (uint64_t)finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x == 0) advance_epoch(a, epoch, counted);
+  }
+}
+
+template <int DT, int PASSES, bool WORDS>
+__global__ __launch_bounds__(WG_THREADS) void colocated_twoshot_kernel(KArgs a) {
+  warm_kernel_args();
+  colocated_twoshot_ll128<DT, PASSES, WORDS>(a);
 }
 
 // Small LL / LL128 one-shots (a.colocate) run in a kernel of their own: the
@@ -1593,6 +1827,29 @@ static KernelFn pick_colocated(int dtype, int proto, uint64_t tile_bytes) {
   }
 }
 
+// Colocated LL128 two-shots: one or two passes per tile; bf16 a word at a
+// time when `words` (4-byte aligned buffers, an even element count).
+static KernelFn pick_colocated_twoshot(int dtype, int proto, uint64_t tile_bytes, bool words) {
+  if (proto != PROTO_LL128) return nullptr;
+  constexpr int MP = (int)LL128_COLOCATED_PASSES;
+  const bool one = tile_bytes <= LL128_COLOCATED_PASS;
+  switch (dtype) {
+    case DT_F32: return one ? colocated_twoshot_kernel<DT_F32, 1, true> : colocated_twoshot_kernel<DT_F32, MP, true>;
+    case DT_BF16:
+      // Element by element a tile of two passes needs one workgroup per CU,
+      // and its grid (256 workgroups) more than half of that: ticketed.
+      if (words) return one ? colocated_twoshot_kernel<DT_BF16, 1, true> : colocated_twoshot_kernel<DT_BF16, MP, true>;
+      return one ? colocated_twoshot_kernel<DT_BF16, 1, false> : nullptr;
+    case DT_I32: return one ? colocated_twoshot_kernel<DT_I32, 1, true> : colocated_twoshot_kernel<DT_I32, MP, true>;
+    default: return nullptr;
+  }
+}
+
+// Every block and tile a whole number of words (rank buffers are 16-byte
+// aligned, blocks and tiles whole vectors, so only the buffer's end can
+// fall mid-word).
+static bool word_clean(const KArgs& a) { return (a.g.total * (uint64_t)a.g.esize) % 4 == 0; }
+
 KernelFn pick_kernel(int dtype, int proto, int kind) {
   switch (dtype) {
     case DT_F32: return pick_proto<DT_F32>(proto, kind);
@@ -1688,8 +1945,12 @@ hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uin
   // the ticketed schedule.
   b.colocate = 0;
   if (a.g.colocated && !a.rearm_errors) {
-    KernelFn fc = pick_colocated(a.g.dtype, a.g.proto, a.g.tile * (uint64_t)a.g.esize);
-    uint64_t ccap = fc ? (uint64_t)resident_workgroups(fc, device) : 0;
+    const uint64_t tile_bytes = a.g.tile * (uint64_t)a.g.esize;
+    KernelFn fc = a.g.kind == K_TWOSHOT ? pick_colocated_twoshot(a.g.dtype, a.g.proto, tile_bytes, word_clean(a))
+                                        : pick_colocated(a.g.dtype, a.g.proto, tile_bytes);
+    // At most half of what is resident: the N workgroups of a tile wait on
+    // each other, and another kernel may hold part of the GPU.
+    uint64_t ccap = fc ? (uint64_t)resident_workgroups(fc, device) / 2 : 0;
     if (max_workgroups) ccap = umin(ccap, umax((uint64_t)max_workgroups, (uint64_t)a.g.nranks));
     if (fc && a.g.tiles * (uint64_t)a.g.nranks <= ccap) {
       f = fc;

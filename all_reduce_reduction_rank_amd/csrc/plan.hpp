@@ -40,9 +40,9 @@ constexpr uint64_t LL128_TILE_UNIT = 3840;  // 32 lines of 120 payload bytes: on
 // A one-shot call over LL or LL128 whose tiles fit this many workgroups (one
 // per tile and rank) runs each rank's send and receive of a tile in one
 // workgroup, with no ticket counter: the N workgroups of a tile wait on each
-// other, so the grid is kept well below what is resident at once (a third of
-// it at three workgroups per CU; launch_collective checks).  Their own send
-// and receive keep the latency from growing with the grid.
+// other, so the grid is kept well below what is resident at once
+// (launch_collective allows at most half).  Their own send and receive keep
+// the latency from growing with the grid.
 constexpr uint64_t COLOCATED_WORKGROUPS = 256;
 // A colocated LL tile is whole passes of a workgroup (4 words per thread,
 // 4 KiB), at most LL_COLOCATED_PASSES of them; its send loads the whole tile
@@ -256,13 +256,23 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
   // turn.  Graph time at N=8, ticketed -> colocated: LL bf16 10 KiB 9.8 ->
   // 6.0 us, 640 KiB 50.7 -> 31.9; LL128 bf16 640 KiB 35.6 -> 24.0, fp32
   // 128 KiB 15.8 -> 8.8.
+  // Small LL128 two-shots likewise run one workgroup per (tile, rank), a
+  // tile being tile t of every block.
   bool colocated = false;
-  if (lines && g.kind == K_ONESHOT && !tune.line_tile_bytes && rank_bytes) {
+  const bool coloc_kind = g.kind == K_ONESHOT || (g.kind == K_TWOSHOT && proto == PROTO_LL128);
+  if (lines && coloc_kind && !tune.line_tile_bytes && rank_bytes) {
+    // Tiles are whole passes.  Rounding LL128 tiles to 32-line units
+    // instead (more, partly filled workgroups) ran no faster: t=512 two-shot
+    // 62.7 -> 63.4 us, t=8 one-shot 10.5 -> 12.0.  A two-shot whose blocks
+    // fit one pass stays ticketed: each workgroup would then run the three
+    // steps of its one tile in turn, where the ticketed schedule overlaps
+    // them (t=1 15.9 -> 23.6 us, t=8 22.4 -> 25.2 when colocated).
     const uint64_t max_tiles = COLOCATED_WORKGROUPS / n;
     const uint64_t pass = proto == PROTO_LL ? LL_COLOCATED_TILE : LL128_COLOCATED_PASS;
     const uint64_t passes = proto == PROTO_LL ? LL_COLOCATED_PASSES : LL128_COLOCATED_PASSES;
-    const uint64_t need = cdiv(cdiv(rank_bytes, max_tiles), pass) * pass;
-    if (need <= passes * pass) {
+    const uint64_t extent = g.kind == K_ONESHOT ? rank_bytes : g.block * es;
+    const uint64_t need = cdiv(cdiv(extent, max_tiles), pass) * pass;
+    if (need <= passes * pass && (g.kind == K_ONESHOT || extent > pass)) {
       tile_b = umax(need, pass);
       colocated = true;
     }
@@ -385,6 +395,7 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
         g.per_group = n * (2 * n - 1);
         g.groups = g.tiles ? g.tiles + 2 * lag : 0;
         g.nslots = n * n + n;
+        g.colocated = colocated && g.tiles * n <= COLOCATED_WORKGROUPS ? 1 : 0;
       }
       break;
     case K_RS_DIRECT:

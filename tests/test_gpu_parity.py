@@ -70,6 +70,40 @@ def test_many_pass_colocated_line_one_shot(dt, n, proto):
     c.close()
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("n", [2, 8])
+def test_colocated_ll128_two_shot(dt, n):
+    # Two-shot LL128 with one workgroup per (tile, rank): tiles of 1 and 2
+    # passes, a ragged count, out of place and in place; bf16 also with odd
+    # counts (loads and stores then go element by element, in a kernel that
+    # fits one workgroup per CU, so these grids stay within half of that:
+    # 128).  All without the ticket counter, equal to the oracle.
+    es = 2 if dt == "bf16" else 4
+    c = Comm(n, 2 << 20 << 3, 2 << 20 << 4)
+    cases = [(1, 0, 256), (2, 0, 256), (2, 4, 256)]
+    if dt == "bf16":
+        cases += [(1, 1, 128), (1, 3, 128)]
+    for passes, tail, grid in cases:
+        tiles = grid // n
+        count = n * tiles * passes * 15360 // es - tail
+        host = inputs.rank_inputs(n, count, dt, _dist(dt), seed=passes * 10 + tail, cfg=83)
+        want = C.allreduce(host, dt, "twoshot")
+        send = [to_dev(x, dt) for x in host]
+        recv = [empty(count, dt) for _ in range(n)]
+        _say("coloc two-shot", dt, n, passes, tail, grid, count)
+        c.allreduce(send, recv, algo="twoshot", proto="ll128")
+        torch.cuda.synchronize()
+        assert c.debug_calls(1)[0]["counter_free"] == 1, (dt, n, passes, count)
+        for r in range(n):
+            assert_same(to_host(recv[r], dt), want[r], f"coloc two-shot {dt} N={n} count={count} rank {r}")
+        c.allreduce(send, None, algo="twoshot", proto="ll128")
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_same(to_host(send[r], dt), want[r], f"coloc two-shot in place {dt} N={n} count={count} rank {r}")
+    assert c.check()[0] == "AR_OK"
+    c.close()
+
+
 def run_allreduce(n, count, dt, algo, proto, chunk=0, seed=0, in_place=False, dist=None):
     host = inputs.rank_inputs(n, count, dt, dist or _dist(dt), seed=seed, cfg=100 + n)
     send = [to_dev(x, dt) for x in host]

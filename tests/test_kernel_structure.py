@@ -39,12 +39,28 @@ def _colocated_kernels(text):
     return list(re.finditer(r"^(_ZN2ar16colocated_kernel\w+):(.*?)^\.Lfunc_end", text, re.S | re.M))
 
 
+def _colocated_twoshot_kernels(text):
+    return list(re.finditer(r"^(_ZN2ar24colocated_twoshot_kernel\w+):(.*?)^\.Lfunc_end", text, re.S | re.M))
+
+
+def _protocol(name):
+    """Protocol of a kernel: collective_kernel<DT, PROTO, KIND>,
+    colocated_kernel<DT, PROTO, PASSES>; colocated_twoshot_kernel<DT, PASSES,
+    WORDS> is LL128 only."""
+    if "colocated_twoshot_kernel" in name:
+        return 2
+    return int(re.match(r"_ZN2ar\d+\w+?_kernelILi\dELi(\d)E", name).group(1))
+
+
 def test_every_kernel_compiled(asm):
     # 3 payload types x (3 protocols x 5 schedules + the Simple tree + 1 copy kernel)
     assert len(_kernels(asm)) == 51
     # small one-shots, one workgroup per (tile, rank): 3 payload types x
     # {LL one pass, LL up to 8 passes, LL128 one pass, LL128 up to 2 passes}
     assert len(_colocated_kernels(asm)) == 12
+    # small LL128 two-shots: {1, 2 passes} x {fp32, int32, bf16 by words}
+    # and bf16 by elements in one pass
+    assert len(_colocated_twoshot_kernels(asm)) == 7
 
 
 def _label_of(line):
@@ -195,9 +211,9 @@ def test_the_order_check_sees_a_payload_load_over_a_flag():
 
 def test_payload_loads_wait_for_their_flags(asm):
     checked = 0
-    for m in _kernels(asm) + _colocated_kernels(asm):
+    for m in _kernels(asm) + _colocated_kernels(asm) + _colocated_twoshot_kernels(asm):
         name = m.group(1)
-        proto = int(re.match(r"_ZN2ar\d+\w+?_kernelILi\dELi(\d)E", name).group(1))
+        proto = _protocol(name)
         if proto == 1:  # LL
             continue
         n, bad = _payload_over_flag(m.group(2))
