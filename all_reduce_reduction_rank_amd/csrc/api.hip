@@ -57,7 +57,7 @@ static uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }
 
 // Tuning overrides read once from the environment (for measurements; they
 // never change results): AR_TILE_KB, AR_LINE_TILE_KB, AR_RING_SKEW,
-// AR_RING_WINDOW, AR_LAG.
+// AR_RING_WINDOW, AR_LAG, AR_COLOC_TILE_KB.
 static const Tuning& tuning() {
   static const Tuning t = [] {
     Tuning x;
@@ -66,6 +66,10 @@ static const Tuning& tuning() {
     if (const char* e = getenv("AR_RING_SKEW")) { x.ring_skew = strtoull(e, nullptr, 10); x.ring_skew_set = true; }
     if (const char* e = getenv("AR_RING_WINDOW")) x.ring_window = strtoull(e, nullptr, 10);
     if (const char* e = getenv("AR_LAG")) x.lag = strtoull(e, nullptr, 10);
+    if (const char* e = getenv("AR_COLOC_TILE_KB")) {
+      x.coloc_tile_bytes = strtoull(e, nullptr, 10) * 1024;
+      x.coloc_tile_set = true;
+    }
     return x;
   }();
   return t;

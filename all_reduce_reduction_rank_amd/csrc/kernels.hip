@@ -1452,6 +1452,70 @@ __device__ __forceinline__ void warm_kernel_args() {
   asm volatile("" ::"s"(x));
 }
 
+// Simple two-shots of mid-size blocks (a.colocate, make_geometry's rule):
+// workgroup b is rank r = b % N on tile t = b / N of every block.  It folds
+// tile t of its own block r over every rank's input (the ticketed fold:
+// same summation order), raises that tile's flag (step 0), then, block by
+// block starting after its own, waits for tile t's flag and copies the sum
+// into its output (step 1).  The same flags, tags and steps as the ticketed
+// schedule; in place is safe for the same reason: a block's sum is copied
+// over a rank's input only after that block's owner has read it.
+template <int DT>
+__device__ __forceinline__ void colocated_twoshot_simple(const KArgs& a) {
+  __shared__ uint64_t s_epoch;
+  __shared__ uint32_t s_abort;
+  const Geometry& g = a.g;
+  const int n = g.nranks;
+  const int r = (int)uniform(blockIdx.x % (uint32_t)n);
+  const uint64_t t = uniform(blockIdx.x / (uint32_t)n);
+  constexpr uint64_t es = Elem<DT>::size;
+  if (threadIdx.x == 0) {
+    const uint64_t e = __hip_atomic_load(&a.ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t ab = ld_u32(&a.ctl->abort);
+    s_epoch = e;
+    s_abort = ab;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t epoch = uniform64(s_epoch);
+  const bool aborted = uniform(s_abort) != 0;
+  const uint64_t tag = (epoch + 1) << 8;
+  uint32_t finished = 0, counted = 0;
+  if (!aborted) {
+    uint64_t lo, hi;
+    tile_range(g, block_len(g, (uint64_t)r), t, &lo, &hi);
+    if (hi > lo) {
+      const uint64_t off = (block_lo(g, (uint64_t)r) + lo) * es;
+      fold_n<DT, 32, true, true, true>([&](int i) { return a.in[i] + off; }, n, a.out[r] + off, (hi - lo) * es);
+      wg_signal(a, a.flags + (uint64_t)r * g.tiles + t, tag + 1, 0, r);
+      ++finished;
+    }
+    if (blockIdx.x == 0) counted = ld_u32(&a.ctl->done);
+    for (int k = 1; k < n; ++k) {
+      const int j = (r + k) % n;
+      tile_range(g, block_len(g, (uint64_t)j), t, &lo, &hi);
+      if (hi <= lo) continue;
+      if (!wg_wait(a, a.flags + (uint64_t)j * g.tiles + t, tag + 1, 1, r)) break;
+      const uint64_t off = (block_lo(g, (uint64_t)j) + lo) * es;
+      simple_stream<DT, true, false>([&](int) { return (const char*)a.out[j] + off; }, 1, a.out[r] + off,
+                                      (hi - lo) * es);
+      ++finished;
+    }
+  } else if (blockIdx.x == 0) {
+    counted = ld_u32(&a.ctl->done);
+  }
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(&a.ctl->diag[5], (uint64_t)finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x == 0) advance_epoch(a, epoch, counted);
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(WG_THREADS) void colocated_twoshot_simple_kernel(KArgs a) {
+  warm_kernel_args();
+  colocated_twoshot_simple<DT>(a);
+}
+
 // Small LL128 two-shots (a.colocate): workgroup b is rank r = b % N on tile
 // t = b / N of every block.  Step 0: r puts its tile t of every other block
 // j on the wire to j (slot r*N + j).  Step 1: r gathers tile t of its own
@@ -1845,6 +1909,15 @@ static KernelFn pick_colocated_twoshot(int dtype, int proto, uint64_t tile_bytes
   }
 }
 
+static KernelFn pick_colocated_twoshot_simple(int dtype) {
+  switch (dtype) {
+    case DT_F32: return colocated_twoshot_simple_kernel<DT_F32>;
+    case DT_BF16: return colocated_twoshot_simple_kernel<DT_BF16>;
+    case DT_I32: return colocated_twoshot_simple_kernel<DT_I32>;
+    default: return nullptr;
+  }
+}
+
 // Every block and tile a whole number of words (rank buffers are 16-byte
 // aligned, blocks and tiles whole vectors, so only the buffer's end can
 // fall mid-word).
@@ -1946,8 +2019,9 @@ hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uin
   b.colocate = 0;
   if (a.g.colocated && !a.rearm_errors) {
     const uint64_t tile_bytes = a.g.tile * (uint64_t)a.g.esize;
-    KernelFn fc = a.g.kind == K_TWOSHOT ? pick_colocated_twoshot(a.g.dtype, a.g.proto, tile_bytes, word_clean(a))
-                                        : pick_colocated(a.g.dtype, a.g.proto, tile_bytes);
+    KernelFn fc = a.g.kind != K_TWOSHOT           ? pick_colocated(a.g.dtype, a.g.proto, tile_bytes)
+                  : a.g.proto == PROTO_SIMPLE ? pick_colocated_twoshot_simple(a.g.dtype)
+                                              : pick_colocated_twoshot(a.g.dtype, a.g.proto, tile_bytes, word_clean(a));
     // At most half of what is resident: the N workgroups of a tile wait on
     // each other, and another kernel may hold part of the GPU.
     uint64_t ccap = fc ? (uint64_t)resident_workgroups(fc, device) / 2 : 0;

@@ -53,6 +53,16 @@ constexpr uint64_t LL_COLOCATED_PASSES = 8;
 // 32 lines: 15 KiB of payload), at most LL128_COLOCATED_PASSES of them.
 constexpr uint64_t LL128_COLOCATED_PASS = 4 * 3840;
 constexpr uint64_t LL128_COLOCATED_PASSES = 2;
+// Simple two-shots run one workgroup per (tile, rank) -- fold tile t of the
+// rank's own block, signal, wait for the other blocks' tile t, copy them --
+// when a block (S / N) is at least SIMPLE_COLOCATED_MIN_BLOCK and its tiles,
+// spread over COLOCATED_WORKGROUPS / N, at most SIMPLE_COLOCATED_MAX_TILE.
+// Measured at N = 2, 4, 8 (us per call, ticketed -> colocated): N=8 bf16
+// 2 MiB 30.3 -> 16.6, 5 MiB 46.4 -> 26.9, 25 MiB 125.8 -> 98.5, 64 MiB
+// 268 -> 249 (256 KiB tiles), 128 MiB 422 -> 495 (512 KiB: kept ticketed);
+// blocks of 16 KiB 10.9 -> 14.1 (kept ticketed), 64 KiB 25.1 -> 14.3.
+constexpr uint64_t SIMPLE_COLOCATED_MIN_BLOCK = 64ull << 10;
+constexpr uint64_t SIMPLE_COLOCATED_MAX_TILE = 256ull << 10;
 constexpr uint64_t LL128_ALIGN = 240;       // 2 lines: a multiple of 16 bytes and of 120 bytes
 
 inline int esize_of(int dtype) { return dtype == DT_BF16 ? 2 : 4; }
@@ -134,6 +144,8 @@ struct Tuning {
   uint64_t ring_window = 0; // ring window (loops) for the windowed order
   bool ring_skew_set = false;
   uint64_t lag = 0;         // phased kinds: receiver groups behind their senders
+  uint64_t coloc_tile_bytes = 0;  // Simple two-shot: largest colocated tile (0 with _set: never)
+  bool coloc_tile_set = false;
 };
 
 // Tile size in bytes for a per-rank buffer of `rank_bytes`: aim for >= 128
@@ -277,6 +289,15 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
       colocated = true;
     }
   }
+  if (!lines && g.kind == K_TWOSHOT && !tune.tile_bytes && g.block) {
+    const uint64_t max_tile = tune.coloc_tile_set ? tune.coloc_tile_bytes : SIMPLE_COLOCATED_MAX_TILE;
+    const uint64_t block_b = g.block * es;
+    const uint64_t need = cdiv(cdiv(block_b, COLOCATED_WORKGROUPS / n), 16) * 16;
+    if (block_b >= SIMPLE_COLOCATED_MIN_BLOCK && need <= max_tile) {
+      tile_b = need;
+      colocated = true;
+    }
+  }
   // Tasks that never wait (Simple one-shot out of place, direct RS and AG)
   // skip the ticket counter when one grid covers them all.  A call that
   // would just miss that grid takes tiles large enough to fit in it: above
@@ -391,6 +412,7 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
         g.per_group = n * n;
         g.groups = g.tiles ? g.tiles + lag : 0;
         g.nflags = n * g.tiles;
+        g.colocated = colocated && g.tiles * n <= COLOCATED_WORKGROUPS ? 1 : 0;
       } else {
         g.per_group = n * (2 * n - 1);
         g.groups = g.tiles ? g.tiles + 2 * lag : 0;

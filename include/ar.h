@@ -50,7 +50,9 @@
  *     call's grid may take, 1..16, at most what fits),
  *     AR_LAG (receiver groups behind their senders), AR_RING_WINDOW and
  *     AR_RING_SKEW (ring ticket order), AR_ONESHOT_FOLD_MIB (largest N*S of
- *     a one-shot that loads every term of a pass at once).
+ *     a one-shot that loads every term of a pass at once), AR_COLOC_TILE_KB
+ *     (largest tile of a Simple two-shot run one workgroup per tile and
+ *     rank; 0: never).
  */
 #ifndef AR_H
 #define AR_H

@@ -104,6 +104,76 @@ def test_colocated_ll128_two_shot(dt, n):
     c.close()
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("n", [2, 3, 8])
+def test_colocated_simple_two_shot(dt, n):
+    # Simple two-shots of 64 KiB to 8 MiB blocks run one workgroup per (tile,
+    # rank): results equal the oracle out of place, in place and with ragged
+    # counts; a workgroup budget below the grid takes the ticketed schedule.
+    es = 2 if dt == "bf16" else 4
+    c = Comm(n, 8 << 20, 0)
+    for block_bytes, tail in ((64 << 10, 0), (1 << 20, 5), (3 << 20, 0), (8 << 20, 1)):
+        count = min(n * block_bytes, 8 << 20) // es - tail
+        host = inputs.rank_inputs(n, count, dt, _dist(dt), seed=block_bytes + tail, cfg=84)
+        want = C.allreduce(host, dt, "twoshot")
+        send = [to_dev(x, dt) for x in host]
+        recv = [empty(count, dt) for _ in range(n)]
+        _say("coloc simple two-shot", dt, n, count)
+        c.allreduce(send, recv, algo="twoshot", proto="simple")
+        torch.cuda.synchronize()
+        assert c.debug_calls(1)[0]["counter_free"] == 1, (dt, n, count)
+        for r in range(n):
+            assert_same(to_host(recv[r], dt), want[r], f"coloc simple two-shot {dt} N={n} count={count} rank {r}")
+        c.allreduce(send, None, algo="twoshot", proto="simple")
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_same(to_host(send[r], dt), want[r], f"coloc simple two-shot in place {dt} N={n} count={count} rank {r}")
+    c.set_max_workgroups(n)
+    count = n * (256 << 10) // es
+    host = inputs.rank_inputs(n, count, dt, _dist(dt), seed=2, cfg=85)
+    send = [to_dev(x, dt) for x in host]
+    recv = [empty(count, dt) for _ in range(n)]
+    c.allreduce(send, recv, algo="twoshot", proto="simple")
+    torch.cuda.synchronize()
+    assert c.debug_calls(1)[0]["counter_free"] == 0
+    want = C.allreduce(host, dt, "twoshot")
+    for r in range(n):
+        assert_same(to_host(recv[r], dt), want[r], f"budget simple two-shot {dt} N={n} rank {r}")
+    assert c.check()[0] == "AR_OK"
+    c.close()
+
+
+@pytest.mark.parametrize("n,rank,step", [(4, 2, 0), (8, 5, 0)])
+def test_colocated_simple_two_shot_withheld_signal(n, rank, step):
+    # One rank program of a colocated Simple two-shot skips its fold signal:
+    # the gathers waiting on it give up at 50 ms and name the first blocked
+    # (rank, step) of the ticketed schedule's model.
+    from oracle import sim
+
+    c = Comm(n, 1 << 20, 0)
+    count = n * (64 << 10) // 4
+    host = inputs.rank_inputs(n, count, "f32", "normal", seed=5)
+    send = [to_dev(x, "f32") for x in host]
+    recv = [empty(count, "f32") for _ in range(n)]
+    c.inject(rank, step, timeout_us=50_000)
+    _say("inject coloc two-shot", n, rank, step)
+    c.allreduce(send, recv, algo="twoshot")
+    assert c.debug_calls(1)[0]["counter_free"] == 1
+    status, r, s = c.check()
+    assert status == "AR_ERR_TIMEOUT"
+    _, first = sim.blocked("allreduce", "twoshot", n, withheld=(rank, step))
+    assert (r, s) == first
+    c.inject(-1, -1)
+    c.reset()
+    c.allreduce(send, recv, algo="twoshot")
+    torch.cuda.synchronize()
+    want = C.allreduce(host, "f32", "twoshot")
+    for q in range(n):
+        assert_same(to_host(recv[q], "f32"), want[q], f"after reset rank {q}")
+    assert c.check()[0] == "AR_OK"
+    c.close()
+
+
 def run_allreduce(n, count, dt, algo, proto, chunk=0, seed=0, in_place=False, dist=None):
     host = inputs.rank_inputs(n, count, dt, dist or _dist(dt), seed=seed, cfg=100 + n)
     send = [to_dev(x, dt) for x in host]
