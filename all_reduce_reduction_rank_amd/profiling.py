@@ -30,7 +30,9 @@ import re
 import statistics
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL = "collective_kernel"
+# Every collective kernel (ticketed or one workgroup per tile and rank) takes
+# ar::KArgs; the fused and the ceiling kernels take other argument blocks.
+KERNEL = "(ar::KArgs)"
 KERNEL_SOURCES = ("csrc/kernels.hip", "csrc/device.hpp", "csrc/schedule.hpp", "csrc/plan.hpp", "csrc/rmsnorm.hip",
                   "csrc/rmsnorm.hpp", "csrc/ceiling.hip")
 
