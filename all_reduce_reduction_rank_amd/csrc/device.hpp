@@ -284,7 +284,7 @@ struct KArgs {
   uint32_t fold;        // 1: one-shot tasks load every term of a pass at once
   uint32_t rearm_errors;  // 1: the last workgroup out also clears the abort word
                           //    and error record (workspaces no host call resets)
-  uint32_t colocate;      // 1: one-shot LL / LL128, workgroup b = (tile b/N, rank b%N)
+  uint32_t colocate;      // 1: launched as a colocated kernel, workgroup b = (tile b/N, rank b%N)
 };
 
 __device__ __forceinline__ void note_blocked(Ctl* c, int step, int rank) {

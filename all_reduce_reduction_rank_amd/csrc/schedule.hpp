@@ -95,7 +95,7 @@ struct Geometry {
   uint64_t slot_lines;  // lines reserved per staging slot
   uint64_t nslots;      // staging slots
   uint64_t nflags;      // Simple flags used
-  int32_t colocated;    // LL / LL128 one-shot: one workgroup per (tile, rank), no tickets
+  int32_t colocated;    // the plan fits one workgroup per (tile, rank), no tickets (see make_geometry)
   int32_t pad;
 };
 
