@@ -120,13 +120,26 @@ def _proto(name):
     return PROTO_AUTO if name == "auto" else PROTOS[name]
 
 
-def _dtype_name(t):
-    import torch
+_TORCH = None
+_DT_NAMES = None  # torch dtype -> "f32" / "bf16" / "i32"
 
-    names = {torch.float32: "f32", torch.bfloat16: "bf16", torch.int32: "i32"}
-    if t.dtype not in names:
+
+def _torch():
+    global _TORCH, _DT_NAMES
+    if _TORCH is None:
+        import torch
+
+        _DT_NAMES = {torch.float32: "f32", torch.bfloat16: "bf16", torch.int32: "i32"}
+        _TORCH = torch
+    return _TORCH
+
+
+def _dtype_name(t):
+    _torch()
+    name = _DT_NAMES.get(t.dtype)
+    if name is None:
         raise TypeError(f"unsupported tensor dtype {t.dtype}")
-    return names[t.dtype]
+    return name
 
 
 def _ptrs(tensors, nranks, device):
@@ -146,11 +159,48 @@ def _sizes(tensors, want, what):
             raise ValueError(f"{what}[{i}] holds {t.numel()} elements; the call needs {want}")
 
 
-def _stream_handle(stream):
-    import torch
+def _marshal(tensors, nranks, dtype, want, device):
+    """Pointer array of `nranks` rank tensors that all pass the checks keeping
+    a kernel inside them (dtype, element count, device, contiguity), in one
+    pass of cheap attribute reads; None if any fails (then `_rank_buffers`
+    names the failure).  Small calls are bound by this host work."""
+    if len(tensors) != nranks:
+        return None
+    ptrs = []
+    for t in tensors:
+        if t.dtype is not dtype or t.numel() != want or t.get_device() != device or not t.is_contiguous():
+            return None
+        ptrs.append(t.data_ptr())
+    return (ctypes.c_void_p * nranks)(*ptrs)
 
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+
+def _rank_buffers(send, recv, nranks, device, n_send, n_recv):
+    """(dtype name, send pointers, recv pointers) of a call, or the first
+    failed check as an exception: dtypes, then element counts, then device
+    and layout."""
+    dt = _dtype_name(send[0])
+    dtype = send[0].dtype
+    s = _marshal(send, nranks, dtype, n_send, device)
+    r = _marshal(recv, nranks, dtype, n_recv, device)
+    if s is not None and r is not None:
+        return dt, s, r
+    for t in list(send) + list(recv):
+        if _dtype_name(t) != dt:
+            raise TypeError("all rank buffers must share one dtype")
+    _sizes(send, n_send, "send")
+    _sizes(recv, n_recv, "recv")
+    _ptrs(send, nranks, device)
+    _ptrs(recv, nranks, device)
+    raise ValueError("rank buffers failed the device check")  # not reached: _ptrs names the failure
+
+
+def _stream_handle(stream, device=None):
+    torch = _torch()
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    if device is not None:  # the raw handle without building a Stream object
+        return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(device))
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
 class Comm:
@@ -189,15 +239,9 @@ class Comm:
         """n_send / n_recv: the elements every send / recv buffer must hold.
         The C ABI sees only pointers, so a shorter tensor would let the kernel
         read or write past it: sizes are checked here, before any launch."""
-        dt = _dtype_name(send[0])
-        for t in list(send) + list(recv):
-            if _dtype_name(t) != dt:
-                raise TypeError("all rank buffers must share one dtype")
-        _sizes(send, n_send, "send")
-        _sizes(recv, n_recv, "recv")
-        s, r = _ptrs(send, self.nranks, self.device), _ptrs(recv, self.nranks, self.device)
+        dt, s, r = _rank_buffers(send, recv, self.nranks, self.device, n_send, n_recv)
         status = getattr(_lib(), name)(self._h, s, r, count, DTYPES[dt], _algo(algo), _proto(proto),
-                                       chunk_bytes, _stream_handle(stream))
+                                       chunk_bytes, _stream_handle(stream, self.device))
         _check(status, name)
 
     def allreduce_rmsnorm(self, send, out, weight, eps=1e-6, residual=None, stream=None):
@@ -290,17 +334,11 @@ def allreduce_noalloc(send, recv=None, algo="ring", proto="simple", chunk_bytes=
 
     recv = send if recv is None else recv
     n = len(send)
-    dt = _dtype_name(send[0])
-    for t in list(send) + list(recv):
-        if _dtype_name(t) != dt:
-            raise TypeError("all rank buffers must share one dtype")
     count = send[0].numel()
-    _sizes(send, count, "send")
-    _sizes(recv, count, "recv")
     dev = torch.cuda.current_device()
-    s, r = _ptrs(send, n, dev), _ptrs(recv, n, dev)
+    dt, s, r = _rank_buffers(send, recv, n, dev, count, count)
     _check(_lib().ar_allreduce_noalloc(n, s, r, count, DTYPES[dt], _algo(algo), _proto(proto), chunk_bytes,
-                                       _stream_handle(stream)), "ar_allreduce_noalloc")
+                                       _stream_handle(stream, dev)), "ar_allreduce_noalloc")
     return recv
 
 

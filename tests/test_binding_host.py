@@ -68,3 +68,31 @@ def test_fused_rmsnorm_shapes():
         c.allreduce_rmsnorm(send, [torch.zeros(4, 64)] * 2, w, residual=[torch.zeros(256), torch.zeros(4, 64)])
     with pytest.raises(ValueError, match="send\\[1\\] has shape \\(3, 64\\)"):
         c.allreduce_rmsnorm([torch.zeros(4, 64), torch.zeros(3, 64)], [torch.zeros(4, 64)] * 2, w)
+
+
+def test_mixed_dtypes_and_counts_of_buffers_are_refused():
+    c = _comm(2)
+    with pytest.raises(TypeError, match="share one dtype"):
+        c.allreduce([_t(16), _t(16, torch.bfloat16)], [_t(16), _t(16)])
+    with pytest.raises(ValueError, match="need 2 rank buffers, got 3"):
+        c.allreduce([_t(16)] * 3, [_t(16)] * 3)
+    with pytest.raises(TypeError, match="unsupported tensor dtype"):
+        c.allreduce([_t(16, torch.float64)] * 2, [_t(16, torch.float64)] * 2)
+
+
+def test_fast_marshalling_accepts_only_buffers_every_check_passes():
+    # _marshal is the per-call fast path; it must refuse whatever the named
+    # checks refuse.  CPU tensors report device -1, which stands in for the
+    # communicator's device here.
+    from all_reduce_reduction_rank_amd.binding import _marshal
+
+    ok = [_t(32) for _ in range(4)]
+    arr = _marshal(ok, 4, torch.float32, 32, -1)
+    assert [arr[i] for i in range(4)] == [t.data_ptr() for t in ok]
+    assert _marshal(ok, 3, torch.float32, 32, -1) is None  # count of buffers
+    assert _marshal(ok, 4, torch.bfloat16, 32, -1) is None  # dtype
+    assert _marshal(ok, 4, torch.float32, 33, -1) is None  # elements
+    assert _marshal(ok, 4, torch.float32, 32, 0) is None  # device
+    strided = torch.zeros(64)[::2]
+    assert strided.numel() == 32 and not strided.is_contiguous()
+    assert _marshal(ok[:3] + [strided], 4, torch.float32, 32, -1) is None  # layout
