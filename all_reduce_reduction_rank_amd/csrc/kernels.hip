@@ -1741,6 +1741,208 @@ __device__ __forceinline__ void colocated_twoshot_ll128(const KArgs& a) {
   }
 }
 
+// Colocated LL two-shot (a.colocate, make_geometry's rule): workgroup b is
+// rank r = b % N on tile t = b / N of every block, with the LL128 two-shot's
+// steps and staging slots.  An LL line carries its flag in the same 8-byte
+// store as its payload word, so a line is whole once its flag reads new:
+// no step waits between payload and flag, and a receive is one round trip
+// per round of W words a thread, each poll reloading every line of the round.
+//   step 0: rank r's tile t of every other block j goes out as lines to
+//           slot r*N + j (owner j);
+//   step 1: owner r sums tile t of its block in rank order -- its own input
+//           and the N-1 ranks' lines of slot i*N + r -- keeps the sum and
+//           publishes it as lines to slot N*N + r;
+//   step 2: rank r copies every other owner's published tile t into its
+//           output.
+// In place is safe: only this workgroup reads or writes tile t of rank r's
+// buffer, and each of its writes follows the reads of the same bytes.
+// WORDS: every tile holds whole words (an even bf16 count, 16-byte aligned
+// buffers), so bf16 moves a word per access; otherwise two halves, so an odd
+// count's last element is exact.
+template <int DT, int W, bool WORDS>
+__device__ __forceinline__ void colocated_twoshot_ll(const KArgs& a) {
+  __shared__ uint64_t s_epoch;
+  __shared__ uint32_t s_abort;
+  const Geometry& g = a.g;
+  const int n = g.nranks;
+  const int r = (int)uniform(blockIdx.x % (uint32_t)n);
+  const uint64_t t = uniform(blockIdx.x / (uint32_t)n);
+  constexpr int es = Elem<DT>::size;
+  constexpr bool HALVES = es == 2 && !WORDS;
+  auto tile_off = [&](int j) {
+    uint64_t lo, hi;
+    tile_range(g, block_len(g, (uint64_t)j), t, &lo, &hi);
+    return (block_lo(g, (uint64_t)j) + lo) * es;
+  };
+  auto tile_bytes = [&](int j) {
+    uint64_t lo, hi;
+    tile_range(g, block_len(g, (uint64_t)j), t, &lo, &hi);
+    return (uint32_t)((hi - lo) * es);
+  };
+  const uint64_t slot_stride = uniform64(g.slot_lines * g.line_bytes);
+  const char* tile_lines = a.lines + uniform64(t * g.tile_lines * g.line_bytes);
+  auto slot = [&](uint64_t sidx, uint32_t nb) { return make_rsrc(tile_lines + sidx * slot_stride, cdiv(nb, 4) * 8); };
+  const uint64_t nn = (uint64_t)n * n;
+  // Word u of round `it` of this thread: byte offset in a tile.
+  auto woff = [&](int it, int u) { return 4 * (threadIdx.x + (uint32_t)(it * W + u) * WG_THREADS); };
+  // Bounded accesses: bytes past a tile read as 0 and are not written.
+  auto ld_w = [&](Rsrc src, uint32_t off) -> uint32_t {
+    if constexpr (HALVES)
+      return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(src, off, 0, 0) |
+             ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(src, off + 2, 0, 0) << 16);
+    else
+      return __builtin_amdgcn_raw_buffer_load_b32(src, off, 0, 0);
+  };
+  auto st_w = [&](Rsrc dst, uint32_t off, uint32_t v) {
+    if constexpr (HALVES) {
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, dst, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(v >> 16), dst, off + 2, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(v, dst, off, 0, 0);
+    }
+  };
+  const int rounds = (int)cdiv(g.tile * es, (uint64_t)W * WG_THREADS * 4);
+
+  // Step 0's first round of loads goes out with the epoch.
+  uint32_t sp[MAX_RANKS][W];
+  auto load_send = [&](int it) {
+#pragma unroll
+    for (int j = 0; j < MAX_RANKS; ++j) {
+      if (j >= n) break;
+      if (j == r) continue;
+      const Rsrc src = make_rsrc(a.in[r] + tile_off(j), tile_bytes(j));
+#pragma unroll
+      for (int u = 0; u < W; ++u) sp[j][u] = ld_w(src, woff(it, u));
+    }
+  };
+  load_send(0);
+  if (threadIdx.x == 0) {
+    const uint64_t e = __hip_atomic_load(&a.ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t ab = ld_u32(&a.ctl->abort);
+    s_epoch = e;
+    s_abort = ab;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t epoch = uniform64(s_epoch);
+  const bool aborted = uniform(s_abort) != 0;
+  const uint32_t flag = (uint32_t)(epoch % 0xffffffffull) + 1u;
+  uint32_t finished = 0, counted = 0;
+  if (!aborted) {
+    // step 0: send
+    const bool send = !withheld(a, 0, r);
+    for (int it = 0; it < rounds; ++it) {
+      if (it) load_send(it);
+      if (!send) continue;
+#pragma unroll
+      for (int j = 0; j < MAX_RANKS; ++j) {
+        if (j >= n) break;
+        if (j == r) continue;
+        const Rsrc dst = slot((uint64_t)r * n + j, tile_bytes(j));
+#pragma unroll
+        for (int u = 0; u < W; ++u) cst8(dst, 2 * woff(it, u), make_uint2(sp[j][u], flag));
+      }
+    }
+    // The peers send at about the same time: polls issued before this
+    // workgroup's own lines have landed mostly come back unwritten.
+    wait_mem();
+    if (blockIdx.x == 0) counted = ld_u32(&a.ctl->done);
+    // Every line of round `it` of the N-1 peers' slots (slot_of(i), tile
+    // bytes nb_of(i)), polled until all are written.
+    uint2 got[MAX_RANKS][W];
+    auto receive = [&](int it, auto slot_of, auto nb_of, int step) -> bool {
+      auto load = [&]() {
+#pragma unroll
+        for (int i = 0; i < MAX_RANKS; ++i) {
+          if (i >= n) break;
+          if (i == r) continue;
+          const Rsrc src = slot(slot_of(i), nb_of(i));
+#pragma unroll
+          for (int u = 0; u < W; ++u) got[i][u] = cld8(src, 2 * woff(it, u));
+        }
+      };
+      auto seen = [&]() {  // lanes past a tile read zeros and count as written
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < MAX_RANKS; ++i) {
+          if (i >= n) break;
+          if (i == r) continue;
+          const uint32_t nb = nb_of(i);
+#pragma unroll
+          for (int u = 0; u < W; ++u) ok = ok && (woff(it, u) >= nb || got[i][u].y == flag);
+        }
+        return ok;
+      };
+      load();
+      if (seen()) return true;
+      PollClock clock;
+      uint32_t level = 0;
+      while (true) {
+        poll_sleep(level);
+        load();
+        if (seen()) return true;
+        const int st = clock.tick(a);
+        if (st == POLL_ABORTED) { note_blocked(a.ctl, step, r); return false; }
+        if (st == POLL_TIMED_OUT) { raise_timeout(a.ctl, step, r); return false; }
+      }
+    };
+    // step 1: gather, sum, keep and publish block r's tile
+    bool ok = true;
+    const uint32_t nb_r = tile_bytes(r);
+    const Rsrc own_in = make_rsrc(a.in[r] + tile_off(r), nb_r);
+    const Rsrc own_out = make_rsrc(a.out[r] + tile_off(r), nb_r);
+    const Rsrc pub = slot(nn + r, nb_r);
+    const bool publish = !withheld(a, 1, r);
+    for (int it = 0; it < rounds && ok; ++it) {
+      uint32_t mine[W];
+#pragma unroll
+      for (int u = 0; u < W; ++u) mine[u] = ld_w(own_in, woff(it, u));
+      ok = receive(it, [&](int i) { return (uint64_t)i * n + r; }, [&](int) { return nb_r; }, 1);
+      if (!ok) break;
+#pragma unroll
+      for (int u = 0; u < W; ++u) {
+        Word<DT> acc;
+#pragma unroll
+        for (int i = 0; i < MAX_RANKS; ++i) {
+          if (i >= n) break;
+          const Word<DT> x = Word<DT>::widen(i == r ? mine[u] : got[i][u].x);
+          if (i == 0) acc = x; else acc.add(x);
+        }
+        const uint32_t res = n > 1 ? acc.narrow() : mine[u];
+        st_w(own_out, woff(it, u), res);
+        if (publish) cst8(pub, 2 * woff(it, u), make_uint2(res, flag));
+      }
+    }
+    if (ok) wait_mem();
+    // step 2: every other block's sum
+    for (int it = 0; it < rounds && ok; ++it) {
+      ok = receive(it, [&](int j) { return nn + j; }, [&](int j) { return tile_bytes(j); }, 2);
+      if (!ok) break;
+#pragma unroll
+      for (int j = 0; j < MAX_RANKS; ++j) {
+        if (j >= n) break;
+        if (j == r) continue;
+        const Rsrc dst = make_rsrc(a.out[r] + tile_off(j), tile_bytes(j));
+#pragma unroll
+        for (int u = 0; u < W; ++u) st_w(dst, woff(it, u), got[j][u].x);
+      }
+    }
+    finished = 3;
+  } else if (blockIdx.x == 0) {
+    counted = ld_u32(&a.ctl->done);
+  }
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(&a.ctl->diag[5], (uint64_t)finished, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x == 0) advance_epoch(a, epoch, counted);
+  }
+}
+
+template <int DT, int W, bool WORDS>
+__global__ __launch_bounds__(WG_THREADS) void colocated_twoshot_ll_kernel(KArgs a) {
+  warm_kernel_args();
+  colocated_twoshot_ll<DT, W, WORDS>(a);
+}
+
 template <int DT, int PASSES, bool WORDS>
 __global__ __launch_bounds__(WG_THREADS) void colocated_twoshot_kernel(KArgs a) {
   warm_kernel_args();
@@ -1891,9 +2093,24 @@ static KernelFn pick_colocated(int dtype, int proto, uint64_t tile_bytes) {
   }
 }
 
-// Colocated LL128 two-shots: one or two passes per tile; bf16 a word at a
-// time when `words` (4-byte aligned buffers, an even element count).
+// Colocated two-shots.  LL: rounds of 4 words a thread for tiles of one
+// 4 KiB pass, of 8 for larger ones.  LL128: one or two passes per tile.
+// bf16 a word at a time when `words` (an even element count).
 static KernelFn pick_colocated_twoshot(int dtype, int proto, uint64_t tile_bytes, bool words) {
+  if (proto == PROTO_LL) {
+    const bool one = tile_bytes <= LL_COLOCATED_TILE;
+    switch (dtype) {
+      case DT_F32:
+        return one ? colocated_twoshot_ll_kernel<DT_F32, U_LL, true> : colocated_twoshot_ll_kernel<DT_F32, 2 * U_LL, true>;
+      case DT_BF16:
+        if (words)
+          return one ? colocated_twoshot_ll_kernel<DT_BF16, U_LL, true> : colocated_twoshot_ll_kernel<DT_BF16, 2 * U_LL, true>;
+        return one ? colocated_twoshot_ll_kernel<DT_BF16, U_LL, false> : colocated_twoshot_ll_kernel<DT_BF16, 2 * U_LL, false>;
+      case DT_I32:
+        return one ? colocated_twoshot_ll_kernel<DT_I32, U_LL, true> : colocated_twoshot_ll_kernel<DT_I32, 2 * U_LL, true>;
+      default: return nullptr;
+    }
+  }
   if (proto != PROTO_LL128) return nullptr;
   constexpr int MP = (int)LL128_COLOCATED_PASSES;
   const bool one = tile_bytes <= LL128_COLOCATED_PASS;

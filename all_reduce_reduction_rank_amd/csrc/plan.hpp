@@ -268,17 +268,20 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
   // turn.  Graph time at N=8, ticketed -> colocated: LL bf16 10 KiB 9.8 ->
   // 6.0 us, 640 KiB 50.7 -> 31.9; LL128 bf16 640 KiB 35.6 -> 24.0, fp32
   // 128 KiB 15.8 -> 8.8.
-  // Small LL128 two-shots likewise run one workgroup per (tile, rank), a
-  // tile being tile t of every block.
+  // Line two-shots whose blocks exceed one pass likewise run one workgroup
+  // per (tile, rank), a tile being tile t of every block.  LL, N=8 bf16,
+  // graph time ticketed -> colocated: 80 KiB 20.7 -> 17.9 us, 640 KiB
+  // 57.5 -> 23.2, 5 MiB 90.8 -> 66.2; N=2 640 KiB 19.0 -> 10.3.
   bool colocated = false;
-  const bool coloc_kind = g.kind == K_ONESHOT || (g.kind == K_TWOSHOT && proto == PROTO_LL128);
+  const bool coloc_kind = g.kind == K_ONESHOT || g.kind == K_TWOSHOT;
   if (lines && coloc_kind && !tune.line_tile_bytes && rank_bytes) {
     // Tiles are whole passes.  Rounding LL128 tiles to 32-line units
     // instead (more, partly filled workgroups) ran no faster: t=512 two-shot
     // 62.7 -> 63.4 us, t=8 one-shot 10.5 -> 12.0.  A two-shot whose blocks
     // fit one pass stays ticketed: each workgroup would then run the three
     // steps of its one tile in turn, where the ticketed schedule overlaps
-    // them (t=1 15.9 -> 23.6 us, t=8 22.4 -> 25.2 when colocated).
+    // them (LL128 t=1 15.9 -> 23.6 us, t=8 22.4 -> 25.2 when colocated; LL
+    // t=1 13.7 -> 16.5).
     const uint64_t max_tiles = COLOCATED_WORKGROUPS / n;
     const uint64_t pass = proto == PROTO_LL ? LL_COLOCATED_TILE : LL128_COLOCATED_PASS;
     const uint64_t passes = proto == PROTO_LL ? LL_COLOCATED_PASSES : LL128_COLOCATED_PASSES;

@@ -106,6 +106,74 @@ def test_colocated_ll128_two_shot(dt, n):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16", "i32"])
 @pytest.mark.parametrize("n", [2, 3, 8])
+def test_colocated_ll_two_shot(dt, n):
+    # Two-shot LL with one workgroup per (tile, rank): blocks just over one
+    # 4 KiB pass (a second tile of 32 bytes), tiles of one pass (rounds of 4
+    # words a thread), of 3 and of 8 passes (rounds of 8 words, the last one
+    # partly past the tile), a ragged count, out of place and in place; bf16
+    # also with odd counts (element by element).  All without the ticket
+    # counter, equal to the oracle.
+    es = 2 if dt == "bf16" else 4
+    tiles = 256 // n
+    c = Comm(n, 8 << 20, 16 << 20)
+    cases = [(n * 4128 // es, 0), (n * tiles * 4096 // es, 0), (n * tiles * 3 * 4096 // es, 4),
+             (n * tiles * 8 * 4096 // es, 0), (n * tiles * 8 * 4096 // es - 8, 0)]
+    if dt == "bf16":
+        cases += [(n * tiles * 4096 // es, 1), (n * tiles * 3 * 4096 // es, 3)]
+    for base, tail in cases:
+        count = base - tail
+        host = inputs.rank_inputs(n, count, dt, _dist(dt), seed=count % 1000, cfg=86)
+        want = C.allreduce(host, dt, "twoshot")
+        send = [to_dev(x, dt) for x in host]
+        recv = [empty(count, dt) for _ in range(n)]
+        _say("coloc ll two-shot", dt, n, count)
+        c.allreduce(send, recv, algo="twoshot", proto="ll")
+        torch.cuda.synchronize()
+        assert c.debug_calls(1)[0]["counter_free"] == 1, (dt, n, count)
+        for r in range(n):
+            assert_same(to_host(recv[r], dt), want[r], f"coloc ll two-shot {dt} N={n} count={count} rank {r}")
+        c.allreduce(send, None, algo="twoshot", proto="ll")
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_same(to_host(send[r], dt), want[r], f"coloc ll two-shot in place {dt} N={n} count={count} rank {r}")
+    assert c.check()[0] == "AR_OK"
+    c.close()
+
+
+@pytest.mark.parametrize("n,rank,step", [(4, 1, 0), (8, 6, 1)])
+def test_colocated_ll_two_shot_withheld_lines(n, rank, step):
+    # One rank program of a colocated LL two-shot does not write its lines of
+    # one step (its sends, or its published sum): the receives waiting on
+    # them give up at 50 ms and name the first blocked (rank, step) of the
+    # oracle's transfer graph; after a reset the same call is exact.
+    from oracle import sim
+
+    c = Comm(n, 1 << 20, 1 << 20)
+    count = n * (64 << 10) // 4
+    host = inputs.rank_inputs(n, count, "f32", "normal", seed=6)
+    send = [to_dev(x, "f32") for x in host]
+    recv = [empty(count, "f32") for _ in range(n)]
+    c.inject(rank, step, timeout_us=50_000)
+    _say("inject coloc ll two-shot", n, rank, step)
+    c.allreduce(send, recv, algo="twoshot", proto="ll")
+    assert c.debug_calls(1)[0]["counter_free"] == 1
+    status, r, s = c.check()
+    assert status == "AR_ERR_TIMEOUT"
+    _, first = sim.blocked("allreduce", "twoshot", n, withheld=(rank, step), proto="ll")
+    assert (r, s) == first
+    c.inject(-1, -1)
+    c.reset()
+    c.allreduce(send, recv, algo="twoshot", proto="ll")
+    torch.cuda.synchronize()
+    want = C.allreduce(host, "f32", "twoshot")
+    for q in range(n):
+        assert_same(to_host(recv[q], "f32"), want[q], f"after reset rank {q}")
+    assert c.check()[0] == "AR_OK"
+    c.close()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("n", [2, 3, 8])
 def test_colocated_simple_two_shot(dt, n):
     # Simple two-shots of 64 KiB to 8 MiB blocks run one workgroup per (tile,
     # rank): results equal the oracle out of place, in place and with ragged

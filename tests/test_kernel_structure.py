@@ -43,6 +43,10 @@ def _colocated_twoshot_kernels(text):
     return list(re.finditer(r"^(_ZN2ar24colocated_twoshot_kernel\w+):(.*?)^\.Lfunc_end", text, re.S | re.M))
 
 
+def _colocated_twoshot_ll_kernels(text):
+    return list(re.finditer(r"^(_ZN2ar27colocated_twoshot_ll_kernel\w+):(.*?)^\.Lfunc_end", text, re.S | re.M))
+
+
 def _protocol(name):
     """Protocol of a kernel: collective_kernel<DT, PROTO, KIND>,
     colocated_kernel<DT, PROTO, PASSES>; colocated_twoshot_kernel<DT, PASSES,
@@ -61,6 +65,9 @@ def test_every_kernel_compiled(asm):
     # small LL128 two-shots: {1, 2 passes} x {fp32, int32, bf16 by words}
     # and bf16 by elements in one pass
     assert len(_colocated_twoshot_kernels(asm)) == 7
+    # small LL two-shots: rounds of {4, 8} words a thread x {fp32, int32,
+    # bf16 by words, bf16 by halves}
+    assert len(_colocated_twoshot_ll_kernels(asm)) == 8
 
 
 def _label_of(line):
