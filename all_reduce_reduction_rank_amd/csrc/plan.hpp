@@ -29,6 +29,12 @@ constexpr uint64_t TREE_RESIDENT_HINT = 1024;
 // grid (the default grid is 3 workgroups on each of 256 CUs, 768), so that
 // it launches without the ticket counter.
 constexpr uint64_t FIXED_GRID_TASKS = 512;
+// The L2 of one die (XCD; the dies are XCDS in schedule.hpp).
+constexpr uint64_t XCD_L2_BYTES = 4ull << 20;
+// A one-shot whose N inputs together exceed one die's L2 runs the N rank
+// programs of each tile on one die (launch_collective), so the tile's
+// inputs come into that die's L2 once and the other N-1 programs hit them.
+inline bool oneshot_by_die(uint64_t nranks, uint64_t rank_bytes) { return nranks * rank_bytes > XCD_L2_BYTES; }
 // Bytes that one step of a ring window moves over all ranks: an eighth of
 // the 256 MB last-level cache (MALL), so a step's partials are still there
 // when the next step reads them.  Measured at N=8 with 512 KiB chunks (loops
@@ -312,14 +318,17 @@ inline bool make_geometry(int op, int algo, int proto, int dtype, int nranks, ui
   // 512 KiB 26.5 -> 6.1.  A one-shot task reads N tiles, and past 16 KiB
   // tiles the longer tasks cost more than the fetches save (8 MiB: 58 -> 92
   // with 128 KiB tiles), so one-shot tiles grow to 16 KiB at most and
-  // reduce-scatter tiles to 64 KiB.
+  // reduce-scatter tiles to 64 KiB.  A one-shot placed by die (each tile's N
+  // programs on one die, oneshot_by_die) takes tiles up to 128 KiB instead:
+  // N=8 bf16 graph time, ticketed -> one grid by die: 2 MiB 28.5 -> 11.9 us,
+  // 5 MiB 44.0 -> 23.9, 8 MiB 53.8 -> 35.3.
   if (!lines && !tune.tile_bytes &&
       ((g.kind == K_ONESHOT && !in_place) || g.kind == K_RS_DIRECT || g.kind == K_AG_DIRECT)) {
     const uint64_t per_row = g.kind == K_AG_DIRECT ? n * n : n;  // tasks per tile of every block
     const uint64_t extent_b = (g.kind == K_ONESHOT ? g.total : g.block) * es;
     const uint64_t rows = umax(1, FIXED_GRID_TASKS / per_row);
     const uint64_t need = cdiv(cdiv(extent_b, rows), 16) * 16;
-    const uint64_t bound = g.kind == K_ONESHOT     ? 16384
+    const uint64_t bound = g.kind == K_ONESHOT     ? (oneshot_by_die(n, rank_bytes) ? 131072 : 16384)
                            : g.kind == K_RS_DIRECT ? 65536
                                                    : simple_tile_cap(rank_bytes, g.kind, in_place != 0);
     if (need > tile_b && need <= bound) tile_b = need;

@@ -120,6 +120,20 @@ AR_HD uint64_t block_len(const Geometry& g, uint64_t j) {
   return umin((j + 1) * g.block, g.total) - block_lo(g, j);
 }
 
+// The GPU's dies (XCDs): workgroups are handed to them in turn, so
+// workgroup b runs on die b % XCDS.
+constexpr uint64_t XCDS = 8;
+
+// Ticket of workgroup b in a grid that runs each group of G consecutive
+// tickets on one die: group m goes to die m % XCDS, as workgroups
+// XCDS (G (m / XCDS) + i) + m % XCDS, i < G.  Over a grid of
+// XCDS G ceil(groups / XCDS) workgroups every ticket appears exactly once
+// (the workgroups whose ticket lies past the last one run nothing).
+AR_HD uint64_t die_ticket(uint32_t b, uint32_t G) {
+  const uint32_t q = b / (uint32_t)XCDS;
+  return ((uint64_t)(b % (uint32_t)XCDS) + XCDS * (uint64_t)(q / G)) * G + q % G;
+}
+
 // Tile k of an extent of `len` elements cut in tiles of g.tile: [lo, hi).
 AR_HD void tile_range(const Geometry& g, uint64_t len, uint64_t k, uint64_t* lo, uint64_t* hi) {
   *lo = umin(k * g.tile, len);

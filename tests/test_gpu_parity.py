@@ -105,6 +105,33 @@ def test_colocated_ll128_two_shot(dt, n):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("n", [3, 5, 8])
+def test_one_shot_placed_by_die(dt, n):
+    # Simple one-shots whose N inputs exceed one die's 4 MiB L2 run each
+    # tile's N rank programs on one die: a grid of 8 N ceil(tiles / 8)
+    # workgroups, some of them idle.  Tile counts that are and are not a
+    # multiple of 8, ragged counts: every output equals the oracle.
+    es = 2 if dt == "bf16" else 4
+    c = Comm(n, 8 << 20, 0)
+    for rank_bytes, tail in (((4 << 20) // n + (1 << 16), 0), (3 << 20, 5), (8 << 20, 1), ((5 << 20) + 4096, 0)):
+        count = rank_bytes // es - tail
+        assert n * count * es > 4 << 20
+        host = inputs.rank_inputs(n, count, dt, _dist(dt), seed=rank_bytes % 997 + tail, cfg=87)
+        want = C.allreduce(host, dt, "oneshot")
+        send = [to_dev(x, dt) for x in host]
+        recv = [empty(count, dt) for _ in range(n)]
+        _say("one-shot by die", dt, n, count)
+        c.allreduce(send, recv, algo="oneshot", proto="simple")
+        torch.cuda.synchronize()
+        rec = c.debug_calls(1)[0]
+        assert rec["counter_free"] == 1 and rec["grid"] % (8 * n) == 0, rec
+        for r in range(n):
+            assert_same(to_host(recv[r], dt), want[r], f"one-shot by die {dt} N={n} count={count} rank {r}")
+    assert c.check()[0] == "AR_OK"
+    c.close()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "i32"])
 @pytest.mark.parametrize("n", [2, 3, 8])
 def test_colocated_ll_two_shot(dt, n):
     # Two-shot LL with one workgroup per (tile, rank): blocks just over one

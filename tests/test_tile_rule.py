@@ -1,7 +1,9 @@
 """Tile choice of the schedules that never wait (host only): compiles
 tests/tile_rule_check.cpp against the library's planning header with g++ and
 runs it.  Such calls launch without the ticket counter when one grid covers
-their tasks, and the planner grows their tiles toward that within a bound."""
+their tasks, and the planner grows their tiles toward that within a bound.
+It also checks the placement of a one-shot's tile programs on one die
+(die_ticket): every ticket exactly once, each tile's programs on one die."""
 
 import os
 import subprocess
@@ -19,3 +21,4 @@ def test_never_waiting_calls_fit_one_grid_when_a_bounded_tile_allows(tmp_path):
     assert " 0 bad" in run.stdout
     grown = int(run.stdout.split(" grown")[0].split(",")[-1])
     assert grown > 0  # the rule is exercised
+    assert " 560 placements" in run.stdout  # die_ticket checked for G = 1..8, 1..70 groups

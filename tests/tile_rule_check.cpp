@@ -8,6 +8,7 @@
 // size-based choice; tiles stay whole 16-byte vectors.
 #include <cstdio>
 #include <initializer_list>
+#include <vector>
 
 #include "../all_reduce_reduction_rank_amd/csrc/plan.hpp"
 
@@ -32,7 +33,10 @@ int main() {
             const uint64_t rank_bytes = g.total * es;
             const uint64_t tile_b = g.tile * es;
             const uint64_t base = pick_tile_bytes(PROTO_SIMPLE, rank_bytes, g.kind, false);
-            const uint64_t bound = g.kind == K_ONESHOT ? 16384 : g.kind == K_RS_DIRECT ? 65536
+            // one-shot: 128 KiB tiles when the N inputs exceed one die's 4 MiB L2
+            // (the tile's N programs then run on one die), else 16 KiB
+            const uint64_t oneshot_bound = (uint64_t)n * rank_bytes > (4ull << 20) ? 131072 : 16384;
+            const uint64_t bound = g.kind == K_ONESHOT ? oneshot_bound : g.kind == K_RS_DIRECT ? 65536
                                                        : simple_tile_cap(rank_bytes, g.kind, false);
             const uint64_t per_row = g.kind == K_AG_DIRECT ? (uint64_t)n * n : (uint64_t)n;
             const uint64_t extent_b = (g.kind == K_ONESHOT ? g.total : g.block) * es;
@@ -50,6 +54,28 @@ int main() {
             }
             if (tile_b > base) ++grown;
           }
-  std::printf("%d shapes, %d grown, %d bad\n", checked, grown, bad);
+  // die_ticket: over a grid of XCDS * G * ceil(groups / XCDS) workgroups,
+  // every ticket of `groups` groups of G appears exactly once, all G tickets
+  // of a group on one die (workgroup b on die b % XCDS), and the workgroups
+  // left over get tickets past the last.
+  int placed = 0;
+  for (uint32_t G = 1; G <= (uint32_t)MAX_RANKS; ++G)
+    for (uint32_t groups = 1; groups <= 70; ++groups) {
+      const uint32_t grid = (uint32_t)(XCDS * G * cdiv(groups, XCDS));
+      const uint32_t ntasks = groups * G;
+      std::vector<int> seen(ntasks, 0), die(groups, -1);
+      for (uint32_t b = 0; b < grid; ++b) {
+        const uint64_t t = die_ticket(b, G);
+        if (t >= ntasks) continue;
+        ++seen[t];
+        const int d = (int)(b % XCDS), m = (int)(t / G);
+        if (die[m] < 0) die[m] = d;
+        if (die[m] != d) { std::printf("FAIL die_ticket G %u groups %u: group %d on two dies\n", G, groups, m); ++bad; }
+      }
+      for (uint32_t t = 0; t < ntasks; ++t)
+        if (seen[t] != 1) { std::printf("FAIL die_ticket G %u groups %u: ticket %u seen %d times\n", G, groups, t, seen[t]); ++bad; }
+      ++placed;
+    }
+  std::printf("%d shapes, %d grown, %d placements, %d bad\n", checked, grown, placed, bad);
   return bad ? 1 : 0;
 }
