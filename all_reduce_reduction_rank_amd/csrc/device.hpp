@@ -285,7 +285,7 @@ struct KArgs {
   uint32_t rearm_errors;  // 1: the last workgroup out also clears the abort word
                           //    and error record (workspaces no host call resets)
   uint32_t colocate;      // 1: launched as a colocated kernel, workgroup b = (tile b/N, rank b%N)
-  uint32_t by_die;        // G > 0 (fixed, batch 1): the G tickets of each tile run on one die
+  uint32_t by_die;        // G > 0 (fixed, batch 1): each run of G tickets sharing a tile runs on one die
 };
 
 __device__ __forceinline__ void note_blocked(Ctl* c, int step, int rank) {

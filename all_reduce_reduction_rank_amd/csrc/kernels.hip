@@ -2235,10 +2235,16 @@ hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uin
   // tile re-read the same N input tiles, so they run on one die and share
   // its L2 (N=8 bf16 640 KiB per rank: 10.8 -> 6.9 us in a graph; 1 MiB
   // 19.9 -> 8.2; at most a few percent either way when the inputs fit).
+  // The N receivers of a direct all-gather's shard tile likewise.  Both
+  // number their tickets so that the N sharing a tile are consecutive.
   b.by_die = 0;
-  if (b.fixed && b.batch == 1 && a.g.kind == K_ONESHOT && a.g.proto == PROTO_SIMPLE && !a.g.in_place &&
-      oneshot_by_die(a.g.nranks, a.g.total * (uint64_t)a.g.esize)) {
-    const uint64_t G = (uint64_t)a.g.nranks;  // tickets tile * N + rank
+  const uint64_t rank_bytes = a.g.total * (uint64_t)a.g.esize;
+  const bool shared_tiles =
+      a.g.proto == PROTO_SIMPLE &&
+      ((a.g.kind == K_ONESHOT && !a.g.in_place && oneshot_by_die(a.g.nranks, rank_bytes)) ||
+       (a.g.kind == K_AG_DIRECT && allgather_by_die(a.g.nranks, rank_bytes)));
+  if (b.fixed && b.batch == 1 && shared_tiles) {
+    const uint64_t G = (uint64_t)a.g.nranks;
     grid = XCDS * G * cdiv(cdiv(a.g.ntasks, G), XCDS);
     b.by_die = (uint32_t)G;
   }

@@ -35,6 +35,12 @@ constexpr uint64_t XCD_L2_BYTES = 4ull << 20;
 // programs of each tile on one die (launch_collective), so the tile's
 // inputs come into that die's L2 once and the other N-1 programs hit them.
 inline bool oneshot_by_die(uint64_t nranks, uint64_t rank_bytes) { return nranks * rank_bytes > XCD_L2_BYTES; }
+// Likewise the N receivers of each shard tile of a direct all-gather, once
+// the N x S bytes they write reach 32 MiB (S = the full per-rank buffer).
+// N=8 bf16 graph time, 5 MiB per rank 14.2 -> 9.7 us, 8 MiB 21.4 -> 14.8;
+// N=4 16 MiB 21.3 -> 14.8; N=2 32 MiB 21.6 -> 17.2.  Below that the
+// placement cost up to 10 % (N=4 5 MiB 5.8 -> 6.4).
+inline bool allgather_by_die(uint64_t nranks, uint64_t rank_bytes) { return nranks * rank_bytes >= (32ull << 20); }
 // Bytes that one step of a ring window moves over all ranks: an eighth of
 // the 256 MB last-level cache (MALL), so a step's partials are still there
 // when the next step reads them.  Measured at N=8 with 512 KiB chunks (loops

@@ -131,6 +131,34 @@ def test_one_shot_placed_by_die(dt, n):
     c.close()
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_all_gather_placed_by_die(dt, n):
+    # Direct all-gathers writing N x S >= 32 MiB run each shard tile's N
+    # receivers on one die (a grid of 8 N ceil(groups / 8) workgroups):
+    # whole and ragged shards, every output equal to the oracle.
+    es = 2 if dt == "bf16" else 4
+    c = Comm(n, 32 << 20, 0)
+    for full_bytes, tail in (((32 << 20) // n, 0), ((32 << 20) // n + 4096, 3)):
+        count = (full_bytes // n) // es - tail  # per-rank send elements
+        assert n * n * count * es >= 32 << 20 or tail
+        host = inputs.rank_inputs(n, count, dt, _dist(dt), seed=full_bytes % 991 + tail, cfg=88)
+        want = C.allgather(host, dt, "oneshot")
+        send = [to_dev(x, dt) for x in host]
+        recv = [empty(n * count, dt) for _ in range(n)]
+        _say("all-gather by die", dt, n, count)
+        c.allgather(send, recv, algo="oneshot", proto="simple")
+        torch.cuda.synchronize()
+        rec = c.debug_calls(1)[0]
+        assert rec["counter_free"] == 1, rec
+        if n * n * count * es >= 32 << 20:
+            assert rec["grid"] % (8 * n) == 0, rec
+        for r in range(n):
+            assert_same(to_host(recv[r], dt), want[r], f"all-gather by die {dt} N={n} count={count} rank {r}")
+    assert c.check()[0] == "AR_OK"
+    c.close()
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16", "i32"])
 @pytest.mark.parametrize("n", [2, 3, 8])
 def test_colocated_ll_two_shot(dt, n):
