@@ -252,7 +252,8 @@ __device__ __forceinline__ void cst_partial(Rsrc r, uint32_t off, const uint4& x
 // every workgroup, the abort word is polled, the epoch is read at start.
 struct Ctl {
   uint32_t ticket;    // next task ticket of the running call
-  uint32_t pad0[31];
+  uint32_t die_next[8];  // by-die calls: next ticket index of each die's share
+  uint32_t pad0[23];
   uint32_t done;      // workgroups of the running call that have finished
   uint32_t pad1[31];
   uint64_t epoch;     // calls completed on this communicator
@@ -285,7 +286,8 @@ struct KArgs {
   uint32_t rearm_errors;  // 1: the last workgroup out also clears the abort word
                           //    and error record (workspaces no host call resets)
   uint32_t colocate;      // 1: launched as a colocated kernel, workgroup b = (tile b/N, rank b%N)
-  uint32_t by_die;        // G > 0 (fixed, batch 1): each run of G tickets sharing a tile runs on one die
+  uint32_t by_die;        // G > 0: each run of G tickets sharing a tile runs on one die (die_ticket;
+                          //        ticketed calls fetch from their die's counter, die_next)
 };
 
 __device__ __forceinline__ void note_blocked(Ctl* c, int step, int rank) {

@@ -132,6 +132,35 @@ def test_one_shot_placed_by_die(dt, n):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [3, 8])
+def test_one_shot_ticketed_by_die(dt, n):
+    # One-shots too large for one grid draw their tickets from one counter
+    # per die (each die's share: the tiles whose N programs run there).
+    # Default grid, a budget of 12 workgroups (a grid of 8: one per die) and
+    # of 5 (fewer than the dies: one shared counter); a ragged count.  Every
+    # output equals the oracle, and repeated calls re-arm the counters.
+    es = 2 if dt == "bf16" else 4
+    c = Comm(n, 48 << 20, 0)
+    count = (48 << 20) // es - 7  # 128 KiB tiles: 384 per buffer, beyond one grid
+    host = inputs.rank_inputs(n, count, dt, _dist(dt), seed=n, cfg=89)
+    want = C.allreduce(host, dt, "oneshot")
+    send = [to_dev(x, dt) for x in host]
+    for budget in (0, 12, 5, 0):
+        c.set_max_workgroups(budget)
+        recv = [empty(count, dt) for _ in range(n)]
+        _say("one-shot ticketed by die", dt, n, count, budget)
+        c.allreduce(send, recv, algo="oneshot", proto="simple")
+        torch.cuda.synchronize()
+        rec = c.debug_calls(1)[0]
+        assert rec["counter_free"] == 0, rec
+        assert rec["grid"] % 8 == 0 or budget == 5, rec
+        for r in range(n):
+            assert_same(to_host(recv[r], dt), want[r], f"one-shot by die {dt} N={n} budget {budget} rank {r}")
+    assert c.check()[0] == "AR_OK"
+    c.close()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("n", [2, 4, 8])
 def test_all_gather_placed_by_die(dt, n):
     # Direct all-gathers writing N x S >= 32 MiB run each shard tile's N
