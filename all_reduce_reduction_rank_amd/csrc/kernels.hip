@@ -2307,14 +2307,18 @@ hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uin
   // rank 43.7 -> 38.9, 16 MiB 112.8 -> 105.3, 32 MiB 187.5 -> 221.2; fp32
   // 4 MiB 39.4 -> 38.2, 8 MiB 59.2 -> 61.3, 32 MiB 169.5 -> 227.6.  bf16
   // gains further (twice the widen/add/round work per byte to hide).  So:
-  // N inputs of at most 128 MiB (bf16) or 32 MiB (4-byte types).
+  // N inputs of at most 128 MiB (bf16) or 32 MiB (4-byte types) -- those
+  // figures predate the placement by die.  Placed by die (the N programs of
+  // a tile share one L2), the fold wins at every size: N=8 fp32 25 MiB
+  // 123.9 -> 100.4 us, 256 MiB 1450 -> 1327; bf16 256 MiB 1646 -> 1353.
   static const uint64_t fold_env = [] {
     const char* e = getenv("AR_ONESHOT_FOLD_MIB");
     return e ? (strtoull(e, nullptr, 10) << 20) : ~0ull;
   }();
   const uint64_t fold_max = fold_env != ~0ull ? fold_env : (a.g.esize == 2 ? 128ull << 20 : 32ull << 20);
+  const bool fold_by_die = fold_env == ~0ull && b.by_die != 0;
   b.fold = (a.g.kind == K_ONESHOT && !a.g.in_place &&
-            (uint64_t)a.g.nranks * a.g.total * (uint64_t)a.g.esize <= fold_max) ? 1u : 0u;
+            (fold_by_die || (uint64_t)a.g.nranks * a.g.total * (uint64_t)a.g.esize <= fold_max)) ? 1u : 0u;
   hipLaunchKernelGGL(f, dim3((unsigned)grid), dim3(WG_THREADS), 0, stream, b);
   if (info) {
     info->grid = (uint32_t)grid;
