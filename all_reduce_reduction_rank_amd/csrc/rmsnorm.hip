@@ -19,6 +19,7 @@
 #include <stdint.h>
 
 #include "device.hpp"
+#include "plan.hpp"
 #include "rmsnorm.hpp"
 
 namespace ar {
@@ -76,7 +77,10 @@ __global__ __launch_bounds__(T) void rmsnorm_kernel(RmsArgs a) {
   const uint64_t nvec = a.hidden / E;
   const uint64_t items = a.rows * (uint64_t)a.nranks;
   const int n = a.nranks;
-  for (uint64_t item = blockIdx.x; item < items; item += gridDim.x) {
+  // Items (row, rank) = row * N + rank, gridDim.x at a time; by die, the
+  // N items of a row (which read the same N input rows) run on one die.
+  const uint64_t first = a.by_die ? die_ticket(blockIdx.x, a.by_die) : blockIdx.x;
+  for (uint64_t item = first; item < items; item += gridDim.x) {
     const uint64_t row = item / (uint64_t)n;
     const int r = (int)(item % (uint64_t)n);
     const uint64_t base = row * a.hidden * es;
@@ -144,13 +148,23 @@ hipError_t launch_rmsnorm(const RmsArgs& a, int dtype, int device, hipStream_t s
   if (max_workgroups) grid = umin(grid, (uint64_t)max_workgroups);
   if (grid < 1) grid = 1;
   const bool one_row = items <= grid;
+  // Like the one-shot: once the N inputs exceed one die's L2, the N items
+  // of a row run on one die, with a grid of whole 8 N blocks so that each
+  // stride of gridDim.x items is one permutation of them.
+  RmsArgs b = a;
+  b.by_die = 0;
+  const uint64_t n = (uint64_t)a.nranks, es = dtype == DT_BF16 ? 2 : 4;
+  if (!one_row && oneshot_by_die(n, a.rows * a.hidden * es) && grid >= XCDS * n) {
+    grid = grid / (XCDS * n) * (XCDS * n);
+    b.by_die = (uint32_t)n;
+  }
   const dim3 g((unsigned)grid);
   if (dtype == DT_BF16) {
-    if (one_row) hipLaunchKernelGGL((rmsnorm_kernel<DT_BF16, true, 1024>), g, dim3(1024), 0, stream, a);
-    else hipLaunchKernelGGL((rmsnorm_kernel<DT_BF16, false, WG_THREADS>), g, dim3(WG_THREADS), 0, stream, a);
+    if (one_row) hipLaunchKernelGGL((rmsnorm_kernel<DT_BF16, true, 1024>), g, dim3(1024), 0, stream, b);
+    else hipLaunchKernelGGL((rmsnorm_kernel<DT_BF16, false, WG_THREADS>), g, dim3(WG_THREADS), 0, stream, b);
   } else {
-    if (one_row) hipLaunchKernelGGL((rmsnorm_kernel<DT_F32, true, 1024>), g, dim3(1024), 0, stream, a);
-    else hipLaunchKernelGGL((rmsnorm_kernel<DT_F32, false, WG_THREADS>), g, dim3(WG_THREADS), 0, stream, a);
+    if (one_row) hipLaunchKernelGGL((rmsnorm_kernel<DT_F32, true, 1024>), g, dim3(1024), 0, stream, b);
+    else hipLaunchKernelGGL((rmsnorm_kernel<DT_F32, false, WG_THREADS>), g, dim3(WG_THREADS), 0, stream, b);
   }
   return hipGetLastError();
 }

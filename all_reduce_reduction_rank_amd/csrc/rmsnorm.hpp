@@ -19,6 +19,7 @@ struct RmsArgs {
   uint64_t rows, hidden;  // hidden: a multiple of one 16-byte vector
   int32_t nranks;
   float eps;
+  uint32_t by_die;  // N > 0: the N items of each row run on one die (die_ticket)
 };
 
 hipError_t launch_rmsnorm(const RmsArgs& a, int dtype, int device, hipStream_t stream, uint32_t max_workgroups);

@@ -67,6 +67,17 @@ def run_fused(n, rows, hidden, dt, with_residual, eps=1e-6, seed=0, comm=None, z
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [3, 8])
+def test_fused_prefill_rows_placed_by_die(n, dt):
+    # More (row, rank) items than the grid and N inputs beyond one die's
+    # L2: each row's N items run on one die, the grid cut to whole 8 N
+    # blocks of workgroups.  The TP prefill shape [512, 5120] and a
+    # ragged row count.
+    for rows, hidden in ((512, 5120), (301, 2048)):
+        run_fused(n, rows, hidden, dt, with_residual=True, seed=rows + n)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("n", [1, 2, 4, 8])
 def test_fused_matches_oracle(n, dt):
     # (160, 1024): at N=8, 1280 (row, rank) items, more than one per
