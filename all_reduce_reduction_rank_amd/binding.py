@@ -249,6 +249,13 @@ class Comm:
 
         send / out / residual: N contiguous [rows, hidden] device tensors
         (residual updated in place, or None); weight: [hidden]."""
+        fast = self._rmsnorm_buffers(send, out, weight, residual)
+        if fast is not None:  # every check passed in one cheap pass
+            dt, rows, hidden, s, o, res = fast
+            status = _lib().ar_allreduce_rmsnorm(self._h, s, o, res, ctypes.c_void_p(weight.data_ptr()), rows,
+                                                 hidden, float(eps), DTYPES[dt], _stream_handle(stream, self.device))
+            _check(status, "ar_allreduce_rmsnorm")
+            return out
         dt = _dtype_name(send[0])
         for t in list(send) + list(out) + list(residual or []) + [weight]:
             if _dtype_name(t) != dt:
@@ -268,6 +275,32 @@ class Comm:
                                              float(eps), DTYPES[dt], _stream_handle(stream))
         _check(status, "ar_allreduce_rmsnorm")
         return out
+
+    def _rmsnorm_buffers(self, send, out, weight, residual):
+        """(dtype name, rows, hidden, pointer arrays) of a fused call whose
+        buffers all pass its checks (one dtype, [rows, hidden] contiguous
+        on the communicator's device, weight [hidden]), else None."""
+        _torch()
+        dt = _DT_NAMES.get(send[0].dtype)
+        if dt is None or send[0].dim() != 2:
+            return None
+        dtype, shape = send[0].dtype, send[0].shape
+        rows, hidden = shape
+        n, dev = self.nranks, self.device
+        ptrs = []
+        for ts in (send, out) + ((residual,) if residual is not None else ()):
+            if len(ts) != n:
+                return None
+            p = []
+            for t in ts:
+                if t.dtype is not dtype or t.shape != shape or t.get_device() != dev or not t.is_contiguous():
+                    return None
+                p.append(t.data_ptr())
+            ptrs.append((ctypes.c_void_p * n)(*p))
+        if (weight.dtype is not dtype or weight.numel() != hidden or weight.get_device() != dev
+                or not weight.is_contiguous()):
+            return None
+        return dt, rows, hidden, ptrs[0], ptrs[1], ptrs[2] if residual is not None else None
 
     def allreduce(self, send, recv=None, algo="ring", proto="simple", chunk_bytes=0, stream=None):
         """recv[r] = sum of send[0..N-1]; recv=None runs in place."""

@@ -96,3 +96,25 @@ def test_fast_marshalling_accepts_only_buffers_every_check_passes():
     strided = torch.zeros(64)[::2]
     assert strided.numel() == 32 and not strided.is_contiguous()
     assert _marshal(ok[:3] + [strided], 4, torch.float32, 32, -1) is None  # layout
+
+
+def test_fused_fast_path_accepts_only_buffers_every_check_passes():
+    # The fused call's one-pass check (_rmsnorm_buffers) must refuse what
+    # the named checks refuse; CPU tensors (device -1) stand in for device ones.
+    c = _comm(2)
+    c.device = -1
+    send = [torch.zeros(4, 64) for _ in range(2)]
+    out = [torch.zeros(4, 64) for _ in range(2)]
+    w = torch.zeros(64)
+    got = c._rmsnorm_buffers(send, out, w, None)
+    assert got is not None and got[:3] == ("f32", 4, 64) and got[5] is None
+    assert [got[3][i] for i in range(2)] == [t.data_ptr() for t in send]
+    assert c._rmsnorm_buffers(send, [torch.zeros(4, 64), torch.zeros(64, 4)], w, None) is None  # shape
+    assert c._rmsnorm_buffers(send, out, torch.zeros(32), None) is None  # weight length
+    assert c._rmsnorm_buffers(send, out, w, [torch.zeros(4, 64)]) is None  # residual count
+    assert c._rmsnorm_buffers(send, out, w.to(torch.bfloat16), None) is None  # weight dtype
+    strided = torch.zeros(64, 4).T
+    assert strided.shape == (4, 64) and not strided.is_contiguous()
+    assert c._rmsnorm_buffers(send, [strided, out[1]], w, None) is None  # layout
+    c.device = 0
+    assert c._rmsnorm_buffers(send, out, w, None) is None  # not on the communicator's device
