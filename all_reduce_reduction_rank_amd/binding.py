@@ -49,7 +49,7 @@ class CallRecord(ctypes.Structure):
     _fields_ = [("seq", ctypes.c_uint64), ("op", ctypes.c_int32), ("algo", ctypes.c_int32),
                 ("proto", ctypes.c_int32), ("dtype", ctypes.c_int32), ("nranks", ctypes.c_int32),
                 ("in_place", ctypes.c_int32), ("grid", ctypes.c_uint32), ("batch", ctypes.c_uint32),
-                ("counter_free", ctypes.c_uint32), ("pad", ctypes.c_uint32), ("count", ctypes.c_uint64),
+                ("counter_free", ctypes.c_uint32), ("by_die", ctypes.c_uint32), ("count", ctypes.c_uint64),
                 ("ntasks", ctypes.c_uint64), ("tile_bytes", ctypes.c_uint64)]
 
 
@@ -349,7 +349,7 @@ class Comm:
                  {v: k for k, v in DTYPES.items()})
         out = []
         for r in recs[:n.value]:
-            d = {f: getattr(r, f) for f, _ in CallRecord._fields_ if f != "pad"}
+            d = {f: getattr(r, f) for f, _ in CallRecord._fields_}
             d["op"], d["algo"], d["proto"], d["dtype"] = (names[0][r.op], names[1][r.algo], names[2][r.proto],
                                                           names[3][r.dtype])
             out.append(d)

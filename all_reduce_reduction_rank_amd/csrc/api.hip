@@ -359,6 +359,7 @@ static ar_status run(ar_comm_t c, int op, const void* const* send, void* const* 
   rec.grid = info.grid;
   rec.batch = info.batch;
   rec.counter_free = info.counter_free;
+  rec.by_die = info.by_die;
   rec.count = count;
   rec.ntasks = g.ntasks;
   rec.tile_bytes = g.tile * (uint64_t)g.esize;

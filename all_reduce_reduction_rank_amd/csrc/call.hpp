@@ -24,7 +24,7 @@ ar_status plan_call(int op, int n, const void* const* send, void* const* recv, u
 
 // How a call was launched (for the call log and AR_DEBUG).
 struct LaunchInfo {
-  uint32_t grid = 0, batch = 0, counter_free = 0;
+  uint32_t grid = 0, batch = 0, counter_free = 0, by_die = 0;
 };
 
 hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uint32_t max_workgroups,

@@ -48,11 +48,11 @@ inline const char* dtype_name(int d) { return d == 0 ? "f32" : d == 1 ? "bf16" :
 // tile 32768 B, 458752 tasks, grid 768 x batch 2".
 inline int format_record(char* buf, size_t len, const ar_call_record& r) {
   return snprintf(buf, len,
-                  "call %llu: %s %s/%s %s N=%d count=%llu %s, tile %llu B, %llu tasks, grid %u x batch %u%s",
+                  "call %llu: %s %s/%s %s N=%d count=%llu %s, tile %llu B, %llu tasks, grid %u x batch %u%s%s",
                   (unsigned long long)r.seq, op_name(r.op), algo_name(r.algo), proto_name(r.proto),
                   dtype_name(r.dtype), r.nranks, (unsigned long long)r.count, r.in_place ? "in place" : "out of place",
                   (unsigned long long)r.tile_bytes, (unsigned long long)r.ntasks, r.grid, r.batch,
-                  r.counter_free ? ", no ticket counter" : "");
+                  r.counter_free ? ", no ticket counter" : "", r.by_die ? ", by die" : "");
 }
 
 }  // namespace ar

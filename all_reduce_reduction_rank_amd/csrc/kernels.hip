@@ -2324,6 +2324,7 @@ hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uin
     info->grid = (uint32_t)grid;
     info->batch = b.batch;
     info->counter_free = b.fixed | b.colocate;
+    info->by_die = b.by_die;
   }
   return hipGetLastError();
 }

@@ -138,6 +138,7 @@ extern "C" ar_status ar_allreduce_noalloc(int nranks, const void* const* send, v
     r.grid = info.grid;
     r.batch = info.batch;
     r.counter_free = info.counter_free;
+    r.by_die = info.by_die;
     r.count = count;
     r.ntasks = g.ntasks;
     r.tile_bytes = g.tile * (uint64_t)g.esize;

@@ -307,7 +307,7 @@ typedef struct {
   uint32_t grid;         /* workgroups launched */
   uint32_t batch;        /* tickets a workgroup takes per fetch */
   uint32_t counter_free; /* 1: the call ran without the ticket counter */
-  uint32_t pad;
+  uint32_t by_die;       /* N > 0: the N rank programs reading a tile ran on one die (XCD) */
   uint64_t count;        /* the call's count argument */
   uint64_t ntasks;       /* tasks of the call's kernel */
   uint64_t tile_bytes;   /* payload bytes per task tile */

@@ -124,7 +124,7 @@ def test_one_shot_placed_by_die(dt, n):
         c.allreduce(send, recv, algo="oneshot", proto="simple")
         torch.cuda.synchronize()
         rec = c.debug_calls(1)[0]
-        assert rec["counter_free"] == 1 and rec["grid"] % (8 * n) == 0, rec
+        assert rec["counter_free"] == 1 and rec["by_die"] == n and rec["grid"] % (8 * n) == 0, rec
         for r in range(n):
             assert_same(to_host(recv[r], dt), want[r], f"one-shot by die {dt} N={n} count={count} rank {r}")
     assert c.check()[0] == "AR_OK"
@@ -153,7 +153,7 @@ def test_one_shot_ticketed_by_die(dt, n):
         torch.cuda.synchronize()
         rec = c.debug_calls(1)[0]
         assert rec["counter_free"] == 0, rec
-        assert rec["grid"] % 8 == 0 or budget == 5, rec
+        assert (rec["by_die"] == n and rec["grid"] % 8 == 0) or (budget == 5 and rec["grid"] < 8), rec
         for r in range(n):
             assert_same(to_host(recv[r], dt), want[r], f"one-shot by die {dt} N={n} budget {budget} rank {r}")
     assert c.check()[0] == "AR_OK"
@@ -181,7 +181,7 @@ def test_all_gather_placed_by_die(dt, n):
         rec = c.debug_calls(1)[0]
         assert rec["counter_free"] == 1, rec
         if n * n * count * es >= 32 << 20:
-            assert rec["grid"] % (8 * n) == 0, rec
+            assert rec["by_die"] == n and rec["grid"] % (8 * n) == 0, rec
         for r in range(n):
             assert_same(to_host(recv[r], dt), want[r], f"all-gather by die {dt} N={n} count={count} rank {r}")
     assert c.check()[0] == "AR_OK"
