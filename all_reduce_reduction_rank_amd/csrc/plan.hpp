@@ -198,7 +198,14 @@ inline uint64_t simple_tile_cap(uint64_t rank_bytes, int kind, bool in_place) {
 
 inline uint64_t pick_tile_bytes(int proto, uint64_t rank_bytes, int kind, bool in_place, int nranks = 8) {
   const uint64_t want = floor_pow2(rank_bytes / 128 + 1);
-  if (proto == PROTO_SIMPLE) return clampu(want, 4096, simple_tile_cap(rank_bytes, kind, in_place));
+  if (proto == PROTO_SIMPLE) {
+    uint64_t cap = simple_tile_cap(rank_bytes, kind, in_place);
+    // A one-shot placed by die keeps about 12 tiles of N inputs in flight
+    // on each die: 64 KiB tiles beat 128 KiB there (N=8 fp32 256 MiB 1327
+    // -> 1257 us, 25 MiB 100.1 -> 96.5; 32 KiB: 1274, 116.2).
+    if (kind == K_ONESHOT && !in_place && oneshot_by_die((uint64_t)nranks, rank_bytes)) cap = umin(cap, 65536);
+    return clampu(want, 4096, cap);
+  }
   if (proto == PROTO_LL) return clampu(want, 4096, kind == K_TWOSHOT && nranks <= 4 ? 16384 : 32768);
   const uint64_t passes =
       kind == K_ONESHOT ? (nranks <= 4 ? 4 : 16) : (kind == K_RS_DIRECT ? 4 : 8);

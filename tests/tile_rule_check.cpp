@@ -32,7 +32,7 @@ int main() {
             ++checked;
             const uint64_t rank_bytes = g.total * es;
             const uint64_t tile_b = g.tile * es;
-            const uint64_t base = pick_tile_bytes(PROTO_SIMPLE, rank_bytes, g.kind, false);
+            const uint64_t base = pick_tile_bytes(PROTO_SIMPLE, rank_bytes, g.kind, false, n);
             // one-shot: 128 KiB tiles when the N inputs exceed one die's 4 MiB L2
             // (the tile's N programs then run on one die), else 16 KiB
             const uint64_t oneshot_bound = (uint64_t)n * rank_bytes > (4ull << 20) ? 131072 : 16384;
