@@ -1593,8 +1593,11 @@ __device__ __forceinline__ void colocated_twoshot_ll128(const KArgs& a) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint64_t epoch = uniform64(s_epoch);
   const bool aborted = uniform(s_abort) != 0;
-  const uint64_t flag = epoch + 1;
-  const uint2 flag2 = make_uint2((uint32_t)flag, (uint32_t)(flag >> 32));
+  // The flag word: low half (calls mod (2^32 - 1)) + 1, never 0, so that a
+  // line still holding its payload-first zero flag word never passes; high
+  // half calls div (2^32 - 1).  One value per call; the receives compare the
+  // low half (as LL's 4-byte flags, it repeats after 2^32 - 1 calls).
+  const uint2 flag2 = make_uint2((uint32_t)(epoch % 0xffffffffull) + 1u, (uint32_t)(epoch / 0xffffffffull));
   uint32_t finished = 0, counted = 0;
   const int passes = (int)cdiv(g.tile * es, LL128_COLOCATED_PASS);  // at most PASSES (launch_collective)
   if (!aborted) {
@@ -1623,30 +1626,37 @@ __device__ __forceinline__ void colocated_twoshot_ll128(const KArgs& a) {
     wait_mem();
     if (blockIdx.x == 0) counted = ld_u32(&a.ctl->done);
     // A wait over the flag words of `slots` (slot index per peer, lines of
-    // the tile of that peer's block), every peer and line at once.
-    uint2 fl[MAX_RANKS][U_C128];
-    auto wait_flags = [&](int p, auto slot_of, auto nb_of, int step) -> bool {
+    // the tile of that peer's block), every peer, line and pass at once: a
+    // sender raises the flags of all its passes together, after all their
+    // payload, so one round trip covers the step.  Only the low half of each
+    // flag word is read (flag2.x, never 0).
+    uint32_t fl[PASSES][MAX_RANKS][U_C128];
+    auto wait_flags = [&](auto slot_of, auto nb_of, int step) -> bool {
       auto load = [&]() {
 #pragma unroll
-        for (int i = 0; i < MAX_RANKS; ++i) {
-          if (i >= n) break;
-          if (i == r) continue;
-          const Rsrc src = slot(slot_of(i), nb_of(i));
+        for (int p = 0; p < PASSES; ++p)
 #pragma unroll
-          for (int u = 0; u < U_C128; ++u) fl[i][u] = cld8(src, line_of(p, u) * LL128_LINE + LL128_DATA);
-        }
+          for (int i = 0; i < MAX_RANKS; ++i) {
+            if (i >= n) break;
+            if (i == r) continue;
+            const Rsrc src = slot(slot_of(i), nb_of(i));  // lines past the tile read as 0, no access
+#pragma unroll
+            for (int u = 0; u < U_C128; ++u)
+              fl[p][i][u] = __builtin_amdgcn_raw_buffer_load_b32(src, line_of(p, u) * LL128_LINE + LL128_DATA, 0, CPOL_SC1);
+          }
       };
       auto seen = [&]() {
         bool ok = true;
 #pragma unroll
-        for (int i = 0; i < MAX_RANKS; ++i) {
-          if (i >= n) break;
-          if (i == r) continue;
-          const uint32_t nl = (uint32_t)cdiv(nb_of(i), LL128_DATA);
+        for (int p = 0; p < PASSES; ++p)
 #pragma unroll
-          for (int u = 0; u < U_C128; ++u)
-            ok = ok && (line_of(p, u) >= nl || (fl[i][u].x == flag2.x && fl[i][u].y == flag2.y));
-        }
+          for (int i = 0; i < MAX_RANKS; ++i) {
+            if (i >= n) break;
+            if (i == r) continue;
+            const uint32_t nl = (uint32_t)cdiv(nb_of(i), LL128_DATA);
+#pragma unroll
+            for (int u = 0; u < U_C128; ++u) ok = ok && (line_of(p, u) >= nl || fl[p][i][u] == flag2.x);
+          }
         return ok;
       };
       load();
@@ -1668,14 +1678,13 @@ __device__ __forceinline__ void colocated_twoshot_ll128(const KArgs& a) {
     const Rsrc own_in = make_rsrc(a.in[r] + tile_off(r), nb_r);
     const Rsrc own_out = make_rsrc(a.out[r] + tile_off(r), nb_r);
     const Rsrc pub = slot(nn + r, nb_r);
+    ok = wait_flags([&](int i) { return (uint64_t)i * n + r; }, [&](int) { return nb_r; }, 1);
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       if (p >= passes || !ok) break;
       uint4 mine[U_C128];
 #pragma unroll
       for (int u = 0; u < U_C128; ++u) mine[u] = load_piece_bounded<DT, WORDS>(own_in, line_of(p, u) * LL128_DATA + 16 * q, full);
-      ok = wait_flags(p, [&](int i) { return (uint64_t)i * n + r; }, [&](int) { return nb_r; }, 1);
-      if (!ok) break;
       uint4 pv[MAX_RANKS][U_C128];
 #pragma unroll
       for (int i = 0; i < MAX_RANKS; ++i) {
@@ -1711,11 +1720,10 @@ __device__ __forceinline__ void colocated_twoshot_ll128(const KArgs& a) {
       wait_mem();
     }
     // step 2: every other block's sum
+    if (ok) ok = wait_flags([&](int j) { return nn + j; }, [&](int j) { return tile_bytes(j); }, 2);
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       if (p >= passes || !ok) break;
-      ok = wait_flags(p, [&](int j) { return nn + j; }, [&](int j) { return tile_bytes(j); }, 2);
-      if (!ok) break;
       uint4 pv[MAX_RANKS][U_C128];
 #pragma unroll
       for (int j = 0; j < MAX_RANKS; ++j) {

@@ -224,12 +224,13 @@ def test_colocated_ll_two_shot(dt, n):
     c.close()
 
 
-@pytest.mark.parametrize("n,rank,step", [(4, 1, 0), (8, 6, 1)])
-def test_colocated_ll_two_shot_withheld_lines(n, rank, step):
-    # One rank program of a colocated LL two-shot does not write its lines of
-    # one step (its sends, or its published sum): the receives waiting on
-    # them give up at 50 ms and name the first blocked (rank, step) of the
-    # oracle's transfer graph; after a reset the same call is exact.
+@pytest.mark.parametrize("proto,n,rank,step", [("ll", 4, 1, 0), ("ll", 8, 6, 1), ("ll128", 4, 2, 0), ("ll128", 8, 3, 1)])
+def test_colocated_ll_two_shot_withheld_lines(proto, n, rank, step):
+    # One rank program of a colocated LL / LL128 two-shot does not finish its
+    # lines of one step (its sends, or its published sum; LL128: payload
+    # without the flag words): the receives waiting on them give up at 50 ms
+    # and name the first blocked (rank, step) of the oracle's transfer
+    # graph; after a reset the same call is exact.
     from oracle import sim
 
     c = Comm(n, 1 << 20, 1 << 20)
@@ -238,16 +239,16 @@ def test_colocated_ll_two_shot_withheld_lines(n, rank, step):
     send = [to_dev(x, "f32") for x in host]
     recv = [empty(count, "f32") for _ in range(n)]
     c.inject(rank, step, timeout_us=50_000)
-    _say("inject coloc ll two-shot", n, rank, step)
-    c.allreduce(send, recv, algo="twoshot", proto="ll")
+    _say("inject coloc two-shot", proto, n, rank, step)
+    c.allreduce(send, recv, algo="twoshot", proto=proto)
     assert c.debug_calls(1)[0]["counter_free"] == 1
     status, r, s = c.check()
     assert status == "AR_ERR_TIMEOUT"
-    _, first = sim.blocked("allreduce", "twoshot", n, withheld=(rank, step), proto="ll")
+    _, first = sim.blocked("allreduce", "twoshot", n, withheld=(rank, step), proto=proto)
     assert (r, s) == first
     c.inject(-1, -1)
     c.reset()
-    c.allreduce(send, recv, algo="twoshot", proto="ll")
+    c.allreduce(send, recv, algo="twoshot", proto=proto)
     torch.cuda.synchronize()
     want = C.allreduce(host, "f32", "twoshot")
     for q in range(n):

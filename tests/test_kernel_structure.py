@@ -196,7 +196,11 @@ def _payload_over_flag(body):
                 checked += 1
                 if "flag" in pending:
                     bad.append(line.strip())
-            pending.append("flag" if m.group(1) == "dwordx2" and sc1 else "data")
+            # flags: 8-byte device-scope loads, and the 4-byte ones of the
+            # LL128 two-shot's low-half flag polls (buffer loads; control
+            # words such as the abort word load through global_load)
+            is_flag = sc1 and (m.group(1) == "dwordx2" or (m.group(1) == "dword" and line.lstrip().startswith("buffer_")))
+            pending.append("flag" if is_flag else "data")
         elif re.match(r"^\s+(?:global|buffer)_(?:store|atomic)", line):
             pending.append("data")  # stores and atomics count in vmcnt too
     return checked, bad
@@ -214,6 +218,11 @@ def test_the_order_check_sees_a_payload_load_over_a_flag():
     assert _payload_over_flag("\n".join([flag, ".LBB0_1:", "\ts_cbranch_scc1 .LBB0_2", payload]))[1]
     assert not _payload_over_flag("\n".join([flag, plain]))[1]
     assert _payload_over_flag("\n".join([flag, payload, plain])) == (1, [payload.strip()])
+    low = "\tbuffer_load_dword v4, v1, s[16:19], 0 offen offset:120 sc1"
+    ctl = "\tglobal_load_dword v5, v1, s[8:9] sc1"
+    assert _payload_over_flag("\n".join([low, payload]))[1]
+    assert not _payload_over_flag("\n".join([low, "\ts_waitcnt vmcnt(0)", payload]))[1]
+    assert not _payload_over_flag("\n".join([ctl, payload]))[1]
 
 
 def test_payload_loads_wait_for_their_flags(asm):
