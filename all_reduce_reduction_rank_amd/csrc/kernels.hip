@@ -2275,9 +2275,10 @@ hipError_t launch_collective(const KArgs& a, int device, hipStream_t stream, uin
       a.g.proto == PROTO_SIMPLE &&
       ((a.g.kind == K_ONESHOT && !a.g.in_place && oneshot_by_die(a.g.nranks, rank_bytes)) ||
        (a.g.kind == K_AG_DIRECT && allgather_by_die(a.g.nranks, rank_bytes)));
-  if (b.fixed && b.batch == 1 && shared_tiles) {
-    const uint64_t G = (uint64_t)a.g.nranks;
-    grid = XCDS * G * cdiv(cdiv(a.g.ntasks, G), XCDS);
+  const uint64_t G = (uint64_t)a.g.nranks;
+  const uint64_t die_grid = XCDS * G * cdiv(cdiv(a.g.ntasks, G), XCDS);
+  if (b.fixed && b.batch == 1 && shared_tiles && die_grid <= cap) {  // within a workgroup budget too
+    grid = die_grid;
     b.by_die = (uint32_t)G;
   } else if (!b.fixed && shared_tiles && a.g.kind == K_ONESHOT && grid >= XCDS) {
     // Ticketed one-shots: a counter per die (a grid of whole dies, so each

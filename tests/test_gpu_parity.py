@@ -127,6 +127,22 @@ def test_one_shot_placed_by_die(dt, n):
         assert rec["counter_free"] == 1 and rec["by_die"] == n and rec["grid"] % (8 * n) == 0, rec
         for r in range(n):
             assert_same(to_host(recv[r], dt), want[r], f"one-shot by die {dt} N={n} count={count} rank {r}")
+    if n == 3:
+        # 510 tasks in one grid, whose placement by die would need 528
+        # workgroups: under a budget of 520 the call keeps its 510.
+        count = (3 << 20) // es
+        host = inputs.rank_inputs(n, count, dt, _dist(dt), seed=11, cfg=87)
+        send = [to_dev(x, dt) for x in host]
+        recv = [empty(count, dt) for _ in range(n)]
+        c.set_max_workgroups(520)
+        c.allreduce(send, recv, algo="oneshot", proto="simple")
+        torch.cuda.synchronize()
+        rec = c.debug_calls(1)[0]
+        assert rec["counter_free"] == 1 and rec["by_die"] == 0 and rec["grid"] <= 520, rec
+        want = C.allreduce(host, dt, "oneshot")
+        for r in range(n):
+            assert_same(to_host(recv[r], dt), want[r], f"one-shot budget {dt} rank {r}")
+        c.set_max_workgroups(0)
     assert c.check()[0] == "AR_OK"
     c.close()
 
